@@ -1,0 +1,219 @@
+"""ctypes binding of libigconv (include/ig_conv.h).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the library, and raises ``IgError`` on a nonzero
+status. Tensors must already live on the GPU with the documented dtype and
+layout; nothing here computes, converts or falls back to the CPU. If the
+library is missing, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libigconv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libigconv.so is not built (%s); run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python implicit_gemm_conv_nhwc_amd/build.py`" % LIB_PATH)
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+_vp = ctypes.c_void_p
+_size_t = ctypes.c_size_t
+
+IG_MAX_RES = 4
+IG_MAX_UP = 8
+
+STATUS = {0: "IG_OK", -1: "IG_EINVAL", -2: "IG_EUNSUPPORTED", -3: "IG_EWORKSPACE", -4: "IG_EHIP"}
+
+
+class IgError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s: %s" % (STATUS.get(code, code), msg))
+        self.code = code
+
+
+def _sig(name, argtypes, restype=_c_int):
+    f = getattr(lib, name)
+    f.argtypes = argtypes
+    f.restype = restype
+    return f
+
+
+lib.ig_last_error.restype = ctypes.c_char_p
+lib.ig_last_error.argtypes = []
+lib.ig_version.restype = _c_int
+
+_pack = _sig("ig_pack_conv_weights", [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp])
+_conv3 = _sig("conv3x3_nhwc", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_float, _vp, _vp])
+_conv3u = _sig("conv3x3_up2_nhwc", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_float, _vp, _vp])
+_convx = _sig("ig_conv_nhwc_ex", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_float,
+                                  _c_int, _vp, _vp])
+_gemm = _sig("gemm1x1", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _c_float, _vp, _c_int,
+                         _c_int, _vp])
+_gemm_acc = _sig("gemm1x1_acc", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _c_float, _vp,
+                                 _c_int, _vp])
+_rms = _sig("rmsnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_float, _vp, _vp])
+_cast = _sig("guard_cast", [_vp, _c_int, _c_int, _vp, _c_int, _vp, _vp])
+_comb = _sig("ig_combine", [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp])
+_smax = _sig("ig_softmax_rows_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp])
+_lat = _sig("ig_latent_to_nhwc_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp])
+_out = _sig("ig_nhwc_to_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
+_zero = _sig("ig_zero_rows_f16", [_vp, _c_int, _c_int, _c_int, _vp])
+_dupup = _sig("ig_dupup_add", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                               _vp])
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc):
+    if rc != 0:
+        raise IgError(rc, lib.ig_last_error().decode())
+    return rc
+
+
+def last_error():
+    return lib.ig_last_error().decode()
+
+
+def version():
+    v = lib.ig_version()
+    return (v >> 16, v & 0xFFFF)
+
+
+# ---------------------------------------------------------------------------
+# entry points (names as in include/ig_conv.h)
+# ---------------------------------------------------------------------------
+
+
+def pack_conv_weights(w, cout, cin, k, cout_p, cin_p, plane, stream=None):
+    """OIHW f16 w -> plane [cout_p][k*k][cin_p] (zero padded)."""
+    return _check(_pack(_ptr(w), cout, cin, k, cout_p, cin_p, _ptr(plane), _stream(stream)))
+
+
+def conv3x3_nhwc(x, H, W, cin_p, w, cout_p, bias, oscale, y, stream=None):
+    return _check(_conv3(_ptr(x), H, W, cin_p, _ptr(w), cout_p, _ptr(bias), float(oscale), _ptr(y),
+                         _stream(stream)))
+
+
+def conv3x3_up2_nhwc(x, H, W, cin_p, w, cout_p, bias, oscale, y, stream=None):
+    return _check(_conv3u(_ptr(x), H, W, cin_p, _ptr(w), cout_p, _ptr(bias), float(oscale), _ptr(y),
+                          _stream(stream)))
+
+
+def conv_nhwc_ex(x, H, W, cin_p, mode, w, cout_p, bias, oscale, accumulate, y, stream=None):
+    return _check(_convx(_ptr(x), H, W, cin_p, mode, _ptr(w), cout_p, _ptr(bias), float(oscale),
+                         int(accumulate), _ptr(y), _stream(stream)))
+
+
+def gemm1x1(a, M, K, lda, b, N, ldb, bias, oscale, c, ldc, c_is_f16, stream=None):
+    return _check(_gemm(_ptr(a), M, K, lda, _ptr(b), N, ldb, _ptr(bias), float(oscale), _ptr(c), ldc,
+                        int(c_is_f16), _stream(stream)))
+
+
+def gemm1x1_acc(a, M, K, lda, b, N, ldb, bias, oscale, c, ldc, stream=None):
+    return _check(_gemm_acc(_ptr(a), M, K, lda, _ptr(b), N, ldb, _ptr(bias), float(oscale), _ptr(c),
+                            ldc, _stream(stream)))
+
+
+def rmsnorm_silu_f16(x, M, cp, c_real, bias, gamma, silu, eps, y, stream=None):
+    return _check(_rms(_ptr(x), M, cp, c_real, _ptr(bias), _ptr(gamma), int(silu), float(eps), _ptr(y),
+                       _stream(stream)))
+
+
+def guard_cast(x, M, C, bias, guard_log2, y, stream=None):
+    return _check(_cast(_ptr(x), M, C, _ptr(bias), int(guard_log2), _ptr(y), _stream(stream)))
+
+
+def combine(x, h, hb, s, sb, M, C, mode, stream=None):
+    return _check(_comb(_ptr(x), _ptr(h), _ptr(hb), _ptr(s), _ptr(sb), M, C, mode, _stream(stream)))
+
+
+def softmax_rows_f16(S, rows, lds, valid, ncols, P, ldp, stream=None):
+    return _check(_smax(_ptr(S), rows, lds, valid, ncols, _ptr(P), ldp, _stream(stream)))
+
+
+def latent_to_nhwc_f16(z, zc, M, cp, y, stream=None):
+    return _check(_lat(_ptr(z), zc, M, cp, _ptr(y), _stream(stream)))
+
+
+def nhwc_to_nchw(y, M, ld, nch, bias, out, stream=None):
+    return _check(_out(_ptr(y), M, ld, nch, _ptr(bias), _ptr(out), _stream(stream)))
+
+
+def zero_rows_f16(y, r0, r1, ld, stream=None):
+    return _check(_zero(_ptr(y), r0, r1, ld, _stream(stream)))
+
+
+def dupup_add(src, H, W, cin_p, x, cout, cout_p, factor, repeats, ft, stream=None):
+    return _check(_dupup(_ptr(src), H, W, cin_p, _ptr(x), cout, cout_p, factor, repeats, ft,
+                         _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# the decoder descriptor (mirrors the structs of include/ig_conv.h)
+# ---------------------------------------------------------------------------
+
+
+class ConvW(ctypes.Structure):
+    _fields_ = [("w", _vp), ("b", _vp), ("cin", _c_int), ("cout", _c_int), ("cin_p", _c_int),
+                ("cout_p", _c_int), ("k", _c_int)]
+
+
+class ResnetW(ctypes.Structure):
+    _fields_ = [("g1", _vp), ("c1", ConvW), ("g2", _vp), ("c2", ConvW), ("has_sc", _c_int),
+                ("sc", ConvW)]
+
+
+class AttnW(ctypes.Structure):
+    _fields_ = [("gamma", _vp), ("q", ConvW), ("k", ConvW), ("v", ConvW), ("proj", ConvW)]
+
+
+class UpW(ctypes.Structure):
+    _fields_ = [("n_res", _c_int), ("res", ResnetW * IG_MAX_RES), ("has_up", _c_int), ("up", ConvW)]
+
+
+class DecoderDesc(ctypes.Structure):
+    _fields_ = [("zc", _c_int), ("conv_in", ConvW), ("mid", ResnetW * 2), ("attn", AttnW),
+                ("n_up", _c_int), ("ups", UpW * IG_MAX_UP), ("norm_out_gamma", _vp),
+                ("norm_out_c", _c_int), ("conv_out", ConvW)]
+
+
+_ws_bytes = _sig("ig_decoder_workspace_bytes", [ctypes.POINTER(DecoderDesc), _c_int, _c_int, _c_int],
+                 _size_t)
+_dec = _sig("decoder_forward", [ctypes.POINTER(DecoderDesc), _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                                _size_t, _vp, _vp])
+
+
+def decoder_workspace_bytes(desc, h0, w0, q_chunk=0):
+    n = _ws_bytes(ctypes.byref(desc), h0, w0, q_chunk)
+    if n == 0:
+        raise IgError(-1, last_error())
+    return n
+
+
+def decoder_forward(desc, latent, h0, w0, guard_log2, q_chunk, ws, ws_bytes, out, stream=None):
+    return _check(_dec(ctypes.byref(desc), _ptr(latent), h0, w0, int(guard_log2), int(q_chunk),
+                       _ptr(ws), ws_bytes, _ptr(out), _stream(stream)))

@@ -1,0 +1,64 @@
+// Internal declarations of libigconv: error reporting and the kernel
+// launchers the C entry points and decoder_forward share. Launchers assume
+// their arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ig_conv.h"
+
+namespace ig {
+
+// Record the reason for a failure on this thread and return `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the thread's last error.
+void clear_error();
+// IG_EHIP with the HIP error's text when the last launch failed, else IG_OK.
+int check_launch(const char *what);
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------------
+// implicit GEMM (MFMA f16 -> f32)
+// ---------------------------------------------------------------------
+enum GemmMode { kGemm = 0, kConv3x3 = 1, kConv3x3Up2 = 2 };
+
+struct IgemmArgs {
+    const _Float16 *a;  // kGemm: A [M][lda]; convs: NHWC image [H*W][cin_p]
+    const _Float16 *b;  // B [N][ldb] (conv plane: ldb = taps * cin_p)
+    const float *bias;  // [N] or null
+    void *c;            // [M][ldc], f32 or f16
+    int M, N, K;
+    int lda, ldb, ldc;
+    int H, W;           // input image (convs); the up2 output is 2H x 2W
+    int cin_p;
+    float oscale;
+    int accumulate;     // f32 output only: c += result
+    int out_f16;
+};
+
+// Launch the MFMA implicit GEMM for `mode`; picks the tile shape.
+void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------------
+// memory-bound kernels
+// ---------------------------------------------------------------------
+void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias,
+                    const float *gamma, int silu, float eps, _Float16 *y, hipStream_t s);
+void launch_guard_cast(const float *x, int M, int C, const float *bias, int guard_log2,
+                       _Float16 *y, hipStream_t s);
+void launch_combine(float *x, const float *h, const float *hb, const float *sv, const float *sb,
+                    int M, int C, int mode, hipStream_t s);
+void launch_softmax(const float *S, int rows, int lds, int valid, int ncols, _Float16 *P, int ldp,
+                    hipStream_t s);
+void launch_latent_ingest(const float *z, int zc, int M, int cp, _Float16 *y, hipStream_t s);
+void launch_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, float *out,
+                         hipStream_t s);
+void launch_pack_weights(const _Float16 *w, int cout, int cin, int k, int cout_p, int cin_p,
+                         _Float16 *plane, hipStream_t s);
+void launch_zero_rows_f16(_Float16 *y, int r0, int r1, int ld, hipStream_t s);
+void launch_dupup(const float *src, int H, int W, int cin_p, float *x, int cout, int cout_p,
+                  int factor, int repeats, int ft, hipStream_t s);
+
+}  // namespace ig

@@ -1,0 +1,261 @@
+// MFMA implicit GEMM for gfx950: the decoder's 3x3 convolutions (plain and
+// with the nearest-2x upsample folded into the gather), its 1x1 convs and
+// the attention's products, all as C[M][N] = oscale * A.B^T (+ bias).
+//
+// Page "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs": module doc (every
+// 3x3 conv an implicit GEMM with the nearest-2x upsample folded into the
+// A-tile gather, 1x1 convs as plain GEMMs, f16 inputs, f32 accumulation),
+// `mmc` (B is the weight "plane" [N][K], A the activations) and `qconv`
+// (the plane's K order is (tap, channel)).
+//
+// Design for CDNA4 (not the pages' 128x64 cooperative-matrix tiling):
+//  * one workgroup = 4 wave64s in a 2x2 grid, tile BM x BN (256|128 x
+//    128|64); each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles,
+//    v_mfma_f32_32x32x16_f16 with the f32 accumulators kept in registers;
+//  * K advances 32 channels per step. For a conv a step is (channel chunk,
+//    tap), taps innermost, so the nine shifted gathers of one 64-byte
+//    channel chunk follow each other and hit the same cache lines;
+//  * the gather is implicit: each thread owns fixed output pixels and
+//    computes the source pixel of every tap on the fly (zero outside the
+//    image; for up2 in upsampled coordinates, then halved), so no im2col
+//    matrix ever exists;
+//  * global -> registers -> LDS, double-buffered, the next step's loads in
+//    flight during the current step's MFMAs; one barrier per step. LDS rows
+//    are 64 B of data + 16 B of padding so the 16-byte fragment reads of
+//    consecutive rows fall in different banks;
+//  * the tile order is XCD-aware: workgroups are dealt round robin to the 8
+//    XCDs, so block b is remapped to run tile (b % 8) * (grid / 8) + b / 8,
+//    keeping neighbouring image rows (the 3x3 halos) in one XCD's L2;
+//  * the epilogue applies oscale, the bias and optionally the residual add
+//    (y += ...) and writes f32 or f16 with rows >= M masked.
+#include "ig_internal.h"
+
+namespace ig {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 32;           // K elements per pipeline step
+constexpr int LDS_ROW = BK + 8;  // halves per LDS row (64 B data + 16 B pad)
+constexpr int NT = 256;          // threads per workgroup
+
+// Per-thread gather state for A: output pixel coordinates (convs) or the
+// row pointer (GEMM) of each row this thread loads.
+template <int MODE, int A_PER>
+struct AGather {
+    int oy[A_PER], ox[A_PER];
+    const _Float16 *row[A_PER];
+};
+
+template <int MODE, int A_PER, int B_PER>
+__device__ __forceinline__ void load_step(const IgemmArgs &p, const AGather<MODE, A_PER> &g,
+                                          const _Float16 *const (&b_row)[B_PER], int q, int ks,
+                                          int Hout, int Wout, uint4 (&ra)[A_PER], uint4 (&rb)[B_PER])
+{
+    int kb;
+    if (MODE == kGemm) {
+        kb = ks * BK;
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (g.row[j]) v = *reinterpret_cast<const uint4 *>(g.row[j] + kb);
+            ra[j] = v;
+        }
+    } else {
+        const int c = ks / 9;
+        const int tap = ks - 9 * c;
+        const int dy = tap / 3, dx = tap - 3 * dy;
+        kb = tap * p.cin_p + c * BK;
+        const _Float16 *abase = p.a + c * BK + q * 8;
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j) {
+            const int uy = g.oy[j] + dy - 1, ux = g.ox[j] + dx - 1;
+            const bool ok = (uy >= 0) & (uy < Hout) & (ux >= 0) & (ux < Wout);
+            const int sy = (MODE == kConv3x3Up2) ? (uy >> 1) : uy;
+            const int sx = (MODE == kConv3x3Up2) ? (ux >> 1) : ux;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (ok) v = *reinterpret_cast<const uint4 *>(abase + (int64_t)(sy * p.W + sx) * p.cin_p);
+            ra[j] = v;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j) rb[j] = *reinterpret_cast<const uint4 *>(b_row[j] + kb);
+}
+
+template <int BM, int BN, int A_PER, int B_PER>
+__device__ __forceinline__ void store_step(_Float16 (*sA)[LDS_ROW], _Float16 (*sB)[LDS_ROW], int rbase,
+                                           int q, const uint4 (&ra)[A_PER], const uint4 (&rb)[B_PER])
+{
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) *reinterpret_cast<uint4 *>(&sA[rbase + 64 * j][q * 8]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j) *reinterpret_cast<uint4 *>(&sB[rbase + 64 * j][q * 8]) = rb[j];
+}
+
+template <int FM, int FN, int WTM, int WTN>
+__device__ __forceinline__ void mma_step(const _Float16 (*sA)[LDS_ROW], const _Float16 (*sB)[LDS_ROW],
+                                         int wm, int wn, int frow, int fk, f32x16 (&acc)[FM][FN])
+{
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+        half8 af[FM], bf[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[i] = *reinterpret_cast<const half8 *>(&sA[wm * WTM + i * 32 + frow][kk * 16 + fk]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bf[j] = *reinterpret_cast<const half8 *>(&sB[wn * WTN + j * 32 + frow][kk * 16 + fk]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int MODE, int BM, int BN, bool OUT_F16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_igemm(IgemmArgs p)
+{
+    constexpr int WTM = BM / 2, WTN = BN / 2;        // wave tile
+    constexpr int FM = WTM / 32, FN = WTN / 32;      // 32x32 MFMA tiles per wave
+    constexpr int A_PER = BM / 64, B_PER = BN / 64;  // 16-byte loads per thread per step
+
+    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM][LDS_ROW];
+    __shared__ __attribute__((aligned(16))) _Float16 sB[2][BN][LDS_ROW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // XCD-aware tile order
+    const int nblk = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int n_tiles = p.N / BN;
+    const int mt = bid / n_tiles, ntile = bid - mt * n_tiles;
+    const int m0 = mt * BM, n0 = ntile * BN;
+
+    const int q = tid & 3;       // which 16-byte chunk of the 64-byte K slice
+    const int rbase = tid >> 2;  // 0..63: row within each group of 64
+
+    const int Wout = (MODE == kConv3x3Up2) ? 2 * p.W : p.W;
+    const int Hout = (MODE == kConv3x3Up2) ? 2 * p.H : p.H;
+
+    AGather<MODE, A_PER> g;
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) {
+        const int m = m0 + rbase + 64 * j;
+        if (MODE == kGemm) {
+            g.row[j] = (m < p.M) ? p.a + (int64_t)m * p.lda + q * 8 : nullptr;
+            g.oy[j] = 0;
+            g.ox[j] = 0;
+        } else {
+            g.row[j] = nullptr;
+            const bool in = m < p.M;
+            const int oy = m / Wout;
+            g.oy[j] = in ? oy : -(1 << 28);  // an out-of-range row fails every bounds test
+            g.ox[j] = m - oy * Wout;
+        }
+    }
+    const _Float16 *b_row[B_PER];
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j) b_row[j] = p.b + (int64_t)(n0 + rbase + 64 * j) * p.ldb + q * 8;
+
+    const int nks = (MODE == kGemm) ? (p.K / BK) : 9 * (p.cin_p / BK);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int frow = lane & 31;      // fragment row (A) / column (B)
+    const int fk = (lane >> 5) * 8;  // this lane's 8 K elements within 16
+
+    uint4 ra[A_PER], rb[B_PER];
+    load_step<MODE, A_PER, B_PER>(p, g, b_row, q, 0, Hout, Wout, ra, rb);
+    store_step<BM, BN, A_PER, B_PER>(sA[0], sB[0], rbase, q, ra, rb);
+    __syncthreads();
+
+    int cur = 0;
+    for (int ks = 0; ks < nks - 1; ++ks) {
+        load_step<MODE, A_PER, B_PER>(p, g, b_row, q, ks + 1, Hout, Wout, ra, rb);
+        mma_step<FM, FN, WTM, WTN>(sA[cur], sB[cur], wm, wn, frow, fk, acc);
+        store_step<BM, BN, A_PER, B_PER>(sA[cur ^ 1], sB[cur ^ 1], rbase, q, ra, rb);
+        __syncthreads();
+        cur ^= 1;
+    }
+    mma_step<FM, FN, WTM, WTN>(sA[cur], sB[cur], wm, wn, frow, fk, acc);
+
+    // epilogue: lane holds column (lane & 31) of each 32x32 tile, rows
+    // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r
+    const float osc = p.oscale;
+    const bool accum = p.accumulate != 0;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + frow;
+        const float bv = p.bias ? p.bias[col] : 0.f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row < p.M) {
+                    float v = osc * acc[i][j][r] + bv;
+                    const int64_t off = (int64_t)row * p.ldc + col;
+                    if (OUT_F16) {
+                        reinterpret_cast<_Float16 *>(p.c)[off] = (_Float16)v;
+                    } else {
+                        float *cp = reinterpret_cast<float *>(p.c) + off;
+                        if (accum) v += *cp;
+                        *cp = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int MODE, int BM, int BN, bool F16>
+void launch_t(const IgemmArgs &a, hipStream_t s)
+{
+    const int mt = (a.M + BM - 1) / BM;
+    const int grid = mt * (a.N / BN);
+    hipLaunchKernelGGL((k_igemm<MODE, BM, BN, F16>), dim3(grid), dim3(NT), 0, s, a);
+}
+
+template <int MODE, bool F16>
+void launch_mode(const IgemmArgs &a, hipStream_t s)
+{
+    const bool bn128 = (a.N % 128) == 0;
+    const int bn = bn128 ? 128 : 64;
+    // prefer the 256-row tile when it still gives two workgroups per CU
+    const long tiles256 = (long)((a.M + 255) / 256) * (a.N / bn);
+    const bool bm256 = tiles256 >= 512;
+    if (bm256 && bn128) launch_t<MODE, 256, 128, F16>(a, s);
+    else if (bm256) launch_t<MODE, 256, 64, F16>(a, s);
+    else if (bn128) launch_t<MODE, 128, 128, F16>(a, s);
+    else launch_t<MODE, 128, 64, F16>(a, s);
+}
+
+}  // namespace
+
+void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s)
+{
+    if (a.M <= 0) return;
+    switch (mode) {
+    case kGemm:
+        if (a.out_f16) launch_mode<kGemm, true>(a, s);
+        else launch_mode<kGemm, false>(a, s);
+        break;
+    case kConv3x3: launch_mode<kConv3x3, false>(a, s); break;
+    case kConv3x3Up2: launch_mode<kConv3x3Up2, false>(a, s); break;
+    default: break;
+    }
+}
+
+}  // namespace ig

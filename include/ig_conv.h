@@ -1,0 +1,258 @@
+/*
+ * ig_conv.h -- C ABI of libigconv, the MI355X (gfx950) implementation of
+ * the resident image-VAE decoder's NHWC implicit-GEMM convolution path.
+ *
+ * Source pages (cited by title and item):
+ *   [QI]  "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs" -- the resident
+ *         decoder: module doc, RMSN_SRC, CAST_SRC, OUT_SRC, `guard`,
+ *         `cpad`, `qconv`, `Rec::conv`/`conv_s`/`rmsn`/`combine`/`cast`/
+ *         `resnet`, `attention`, `run_blocks`, `output_rows`, `decode`.
+ *   [VAE] "cortiq-engine 0.7.6, src/vae.rs" -- the CPU NCHW decoder:
+ *         `Conv2d::apply`, `upsample2x`, `AttnBlock::apply`,
+ *         `VaeDecoder::decode`.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer the caller allocated and
+ *     owns; the library keeps none of them after the call returns.
+ *     f16 data is IEEE binary16, passed as uint16_t bit patterns.
+ *     Every f16/f32 buffer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls are
+ *     asynchronous on it; results are ready when the stream is.
+ *   - Activations are NHWC: pixel-major rows, channels contiguous,
+ *     rows [M][cp] with cp the padded channel count. Padded channels hold
+ *     zeros; weights and norm scales are zero there, so outputs in the pad
+ *     stay zero ([QI] module doc and `cpad`: channels padded to multiples
+ *     of 64).
+ *   - Return value: IG_OK (0) or a negative status. Shapes and pointers are
+ *     checked BEFORE anything is enqueued: on IG_EINVAL / IG_EUNSUPPORTED /
+ *     IG_EWORKSPACE nothing was enqueued and no output was touched (the
+ *     pages' "declined, output untouched" contract of [QI] `decode` and
+ *     `decline`). IG_EHIP means a launch failed after validation.
+ *     ig_last_error() returns the reason as text (per thread).
+ *   - M = 0 (no pixels / rows) is valid and enqueues nothing.
+ */
+#ifndef IG_CONV_H
+#define IG_CONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IG_OK 0
+#define IG_EINVAL (-1)       /* bad argument: null or misaligned pointer, bad size */
+#define IG_EUNSUPPORTED (-2) /* a shape outside the kernels' contract */
+#define IG_EWORKSPACE (-3)   /* workspace missing or too small */
+#define IG_EHIP (-4)         /* a HIP launch or runtime call failed */
+
+#define IG_MAX_RES 4 /* resnet units per up stage */
+#define IG_MAX_UP 8  /* up stages */
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *ig_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int ig_version(void);
+
+/* ---------------------------------------------------------------------
+ * Weight packing ([QI] `qconv`): an OIHW f16 conv weight w[cout][cin][k][k]
+ * becomes the plane[cout_p][k*k][cin_p] the convolutions read: row o holds
+ * (tap, channel) pairs, tap = ky*k + kx, plane[o][tap][ci] =
+ * w[o][ci][ky][kx], zero for o >= cout or ci >= cin.
+ * k must be 1 or 3; cout_p >= cout, cin_p >= cin, both multiples of 64.
+ * --------------------------------------------------------------------- */
+int ig_pack_conv_weights(const uint16_t *w, int cout, int cin, int k, int cout_p, int cin_p,
+                         uint16_t *plane, void *stream);
+
+/* ---------------------------------------------------------------------
+ * 3x3 convolution, stride 1, zero padding 1, as an implicit GEMM
+ * ([QI] module doc: every 3x3 conv an implicit GEMM, f16 inputs, f32
+ * accumulation; `Rec::conv_s`; [VAE] `Conv2d::apply` for the definition):
+ *   y[p][o] = oscale * sum_{tap,ci} plane[o][tap][ci] * x[src(p,tap)][ci]
+ *             (+ bias[o] if bias != NULL)
+ * where src(p,tap) is pixel (r+ky-1, c+kx-1) of the H x W image, zero
+ * outside it. GEMM shape M = H*W, N = cout_p, K = 9*cin_p.
+ *   x:     f16 NHWC [H*W][cin_p]        (cin_p: multiple of 64)
+ *   w:     f16 plane [cout_p][9][cin_p] (cout_p: multiple of 64)
+ *   bias:  f32 [cout_p] or NULL
+ *   y:     f32 NHWC [H*W][cout_p]
+ * --------------------------------------------------------------------- */
+int conv3x3_nhwc(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout_p,
+                 const float *bias, float oscale, float *y, void *stream);
+
+/* ---------------------------------------------------------------------
+ * 3x3 convolution of the nearest-2x upsampled image, the upsample folded
+ * into the gather and never materialised ([QI] module doc; `Rec::conv_s`
+ * with `up`; [VAE] `upsample2x` then `Conv2d::apply` for the definition).
+ * x is the HALF-resolution H x W image; the output is 2H x 2W. Tap (ky,kx)
+ * at output (r,c) reads x[(r+ky-1)/2][(c+kx-1)/2] when 0 <= r+ky-1 < 2H
+ * and 0 <= c+kx-1 < 2W, else 0 (zero padding in upsampled coordinates).
+ *   x: f16 [H*W][cin_p]; w: f16 [cout_p][9][cin_p]; y: f32 [4*H*W][cout_p]
+ * A guarded input ([QI] `guard`) is undone with oscale = 2^g.
+ * --------------------------------------------------------------------- */
+int conv3x3_up2_nhwc(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout_p,
+                     const float *bias, float oscale, float *y, void *stream);
+
+/* The convolution family with one more output mode.
+ *   mode 0: 1x1 conv ([QI] module doc: 1x1 convs as plain GEMMs),
+ *           w = [cout_p][cin_p]; mode 1: 3x3 as conv3x3_nhwc;
+ *   mode 2: 3x3 on the nearest-2x upsample as conv3x3_up2_nhwc.
+ *   accumulate = 0: y = oscale*acc (+bias)
+ *   accumulate = 1: y = y + oscale*acc (+bias)  -- the residual add of
+ *                   [QI] `Rec::combine` mode 0 folded into the epilogue. */
+int ig_conv_nhwc_ex(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w,
+                    int cout_p, const float *bias, float oscale, int accumulate, float *y,
+                    void *stream);
+
+/* ---------------------------------------------------------------------
+ * NT GEMM ([QI] `mmc`: B is the "plane" [N][K], A the activations [M][K];
+ * the 1x1 convs and every attention product of [QI] `attention`):
+ *   C[m][n] = oscale * sum_k A[m][k] * B[n][k] (+ bias[n])
+ *   a: f16 [M][lda]; b: f16 [N][ldb]; c: [M][ldc], f32 or (c_is_f16) f16.
+ * Requires K % 32 == 0, N % 64 == 0, lda/ldb multiples of 8, ldc >= N;
+ * M is arbitrary (rows are masked).
+ * --------------------------------------------------------------------- */
+int gemm1x1(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int N, int ldb,
+            const float *bias, float oscale, void *c, int ldc, int c_is_f16, void *stream);
+
+/* As gemm1x1 with the f32 output accumulated: C += oscale*A.B^T (+bias). */
+int gemm1x1_acc(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int N, int ldb,
+                const float *bias, float oscale, float *c, int ldc, void *stream);
+
+/* ---------------------------------------------------------------------
+ * Per-pixel RMS_norm over the channels ([QI] RMSN_SRC, `Rec::rmsn`):
+ *   v = x[p][:] + bias (bias on read, optional)
+ *   y[p][c] = f16( v_c * sqrt(c_real) / max(||v||_2, eps) * gamma[c] )
+ *   then, if silu, y <- y / (1 + e^-y) before the f16 store.
+ * The sum runs over all cp channels (the pad holds zeros); sqrt uses
+ * c_real, the real channel count.
+ *   x: f32 [M][cp]; bias: f32 [cp] or NULL; gamma: f32 [cp], zero in pad;
+ *   y: f16 [M][cp]. cp: multiple of 64, at most 1024. eps: 1e-12 on the
+ *   pages.
+ * --------------------------------------------------------------------- */
+int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bias,
+                     const float *gamma, int silu, float eps, uint16_t *y, void *stream);
+
+/* ---------------------------------------------------------------------
+ * The range-guarded f16 cast of the raw residual stream ([QI] `guard`,
+ * CAST_SRC, `Rec::cast`): y = f16((x + bias) * 2^-guard_log2); the
+ * consuming conv multiplies 2^guard_log2 back in its f32 epilogue.
+ *   x: f32 [M][C]; bias: f32 [C] or NULL; y: f16 [M][C];
+ *   C % 4 == 0; guard_log2 in 0..14 (8 on the pages).
+ * --------------------------------------------------------------------- */
+int guard_cast(const float *x, int M, int C, const float *bias, int guard_log2, uint16_t *y,
+               void *stream);
+
+/* ---------------------------------------------------------------------
+ * The residual combine ([QI] `Rec::combine`), f32 [M][C]:
+ *   mode 0: x += h + hb;  mode 1: x = s + sb + h + hb;  mode 2: x = h + hb.
+ *   hb, sb: [C] or NULL (zero). C % 4 == 0.
+ * --------------------------------------------------------------------- */
+int ig_combine(float *x, const float *h, const float *hb, const float *s, const float *sb, int M,
+               int C, int mode, void *stream);
+
+/* ---------------------------------------------------------------------
+ * Row softmax of attention scores ([QI] `attention`: S f32 -> P f16;
+ * [VAE] `AttnBlock::apply`: max-subtracted exp, divided by the row sum):
+ *   P[r][j] = f16( exp(S[r][j] - max_r) / sum_{j<valid} exp(S[r][j] - max_r) )
+ * for j < valid, and P[r][j] = 0 for valid <= j < ncols (padded keys).
+ *   S: f32 [rows][lds]; P: f16 [rows][ldp]; ncols <= min(lds, ldp).
+ * --------------------------------------------------------------------- */
+int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols, uint16_t *P,
+                        int ldp, void *stream);
+
+/* Latent ingest ([QI] `decode`: the NCHW latent becomes an NHWC f16 conv
+ * input): y[p][c] = f16(z[c][p]) for c < zc, 0 for zc <= c < cp.
+ *   z: f32 [zc][M]; y: f16 [M][cp]. */
+int ig_latent_to_nhwc_f16(const float *z, int zc, int M, int cp, uint16_t *y, void *stream);
+
+/* Output stage ([QI] OUT_SRC): out[ch][p] = y[p][ch] (+ bias[ch]) for
+ * ch < nch. y: f32 [M][ld]; bias: [nch] or NULL; out: f32 [nch][M]. */
+int ig_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, float *out,
+                    void *stream);
+
+/* The DupUp shortcut ([QI] DUPUP_SRC and `run_blocks`): a channel shuffle
+ * of the half-resolution input added onto the 2x grid,
+ *   x[2y+sy][2x+sx][o] += src[y][x][(o*factor + (ft-1)*4 + 2*sy + sx) / repeats]
+ * for o < cout, sy, sx in {0, 1}. With factor = repeats = 4 and ft = 1 it is
+ * the nearest-2x broadcast of src added into x (in = out channels).
+ *   src: f32 [H*W][cin_p]; x: f32 [4*H*W][cout_p]; every shuffled channel
+ *   index must be < cin_p. */
+int ig_dupup_add(const float *src, int H, int W, int cin_p, float *x, int cout, int cout_p,
+                 int factor, int repeats, int ft, void *stream);
+
+/* Zero rows [r0, r1) of an f16 matrix with row length ld (a fill kernel,
+ * safe under stream capture). */
+int ig_zero_rows_f16(uint16_t *y, int r0, int r1, int ld, void *stream);
+
+/* ---------------------------------------------------------------------
+ * The whole decoder on one stream ([QI] `decode`, `Rec::resnet`,
+ * `attention`, `run_blocks`, `output_rows`; [VAE] `VaeDecoder::decode`):
+ *   f16(latent) -> conv_in -> resnet -> attention -> resnet
+ *   -> per up stage: resnets, x = 2^g conv_up2(f16(x 2^-g)) + b
+ *   -> f16(RMS_norm(x; norm_out) -> SiLU) -> conv_out -> NCHW output.
+ * Every weight is device memory the caller owns, packed by
+ * ig_pack_conv_weights; biases and gammas are f32 zero-padded to the
+ * padded widths. All widths are padded to multiples of 64.
+ * --------------------------------------------------------------------- */
+typedef struct ig_conv_w {
+    const uint16_t *w; /* packed plane [cout_p][k*k][cin_p] */
+    const float *b;    /* [cout_p], or NULL for no bias */
+    int cin, cout;     /* real channel counts */
+    int cin_p, cout_p; /* padded widths */
+    int k;             /* 1 or 3 */
+} ig_conv_w;
+
+typedef struct ig_resnet_w {
+    const float *g1; /* [cin_p] gamma of the first RMS_norm */
+    ig_conv_w c1;    /* 3x3 cin -> cout */
+    const float *g2; /* [cout_p] gamma of the second RMS_norm */
+    ig_conv_w c2;    /* 3x3 cout -> cout */
+    int has_sc;      /* 1: a 1x1 shortcut cin -> cout (guarded input) */
+    ig_conv_w sc;
+} ig_resnet_w;
+
+typedef struct ig_attn_w {
+    const float *gamma;      /* [c] RMS_norm gamma (no SiLU) */
+    ig_conv_w q, k, v, proj; /* 1x1 c -> c; c % 64 == 0, unpadded */
+} ig_attn_w;
+
+typedef struct ig_up_w {
+    int n_res;
+    ig_resnet_w res[IG_MAX_RES];
+    int has_up;   /* 1: a nearest-2x upsample conv ends the stage */
+    ig_conv_w up; /* 3x3 */
+} ig_up_w;
+
+typedef struct ig_decoder {
+    int zc;            /* latent channels */
+    ig_conv_w conv_in; /* 3x3 zc -> c */
+    ig_resnet_w mid[2];
+    ig_attn_w attn;
+    int n_up;
+    ig_up_w ups[IG_MAX_UP];
+    const float *norm_out_gamma; /* [cp] */
+    int norm_out_c;              /* real channels of norm_out */
+    ig_conv_w conv_out;          /* 3x3 c -> out channels (<= 64) */
+} ig_decoder;
+
+/* Workspace bytes decoder_forward needs for an h0 x w0 latent with query
+ * chunks of q_chunk rows (q_chunk <= 0: the library's default). Returns 0
+ * if the descriptor or the sizes are invalid (see ig_last_error()). */
+size_t ig_decoder_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_chunk);
+
+/* Decode one latent. latent: f32 NCHW [zc][h0*w0]; out: f32 NCHW
+ * [conv_out.cout][H*W] with H = h0 * 2^(stages with has_up), likewise W.
+ * guard_log2 in 0..14; ws: device workspace of ws_bytes >=
+ * ig_decoder_workspace_bytes(). On a validation error nothing is
+ * enqueued and out is untouched. */
+int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2,
+                    int q_chunk, void *ws, size_t ws_bytes, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IG_CONV_H */

@@ -1,0 +1,388 @@
+"""Per-kernel parity of the HIP path against the CPU oracle, through the C
+ABI, on the seeded inputs of the per-kernel configurations (and smaller,
+ragged and padded shapes). Every output buffer starts as NaN so a test
+also proves the kernel wrote every element it owns."""
+
+import numpy as np
+import pytest
+import torch
+
+import implicit_gemm_conv_nhwc_amd as ig
+import oracle as O
+import synth
+from gpu_util import (CONV_TOL, conv_err, cpad, dev, f16_ulps, host, nan_f16, nan_f32,
+                      nhwc_to_chw, packed, pad_last, padded_vec, sample_pixels)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    print("device:", torch.cuda.get_device_name(0), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# weight packing (a layout: exact)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("cout,cin,k", [(128, 128, 3), (3, 128, 3), (288, 288, 3), (256, 512, 1)])
+def test_pack_weights_layout(cout, cin, k):
+    w = synth.normal(9, 1, (cout, cin, k, k), 1.0, np.float16)
+    plane = host(packed(w))
+    want = np.zeros((cpad(cout), k * k, cpad(cin)), np.float16)
+    want[:cout, :, :cin] = w.reshape(cout, cin, k * k).transpose(0, 2, 1)
+    assert np.array_equal(plane.view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# RMS_norm
+# ---------------------------------------------------------------------------
+
+
+def _norm_case(x_nhwc, gamma, c_real, cp, bias=None, silu=True):
+    H, W, _ = x_nhwc.shape
+    M = H * W
+    xd = dev(pad_last(x_nhwc.reshape(M, -1), cp))
+    g = padded_vec(gamma, cp)
+    b = padded_vec(bias, cp) if bias is not None else None
+    y = nan_f16((M, cp))
+    ig.rmsnorm_silu_f16(xd, M, cp, c_real, b, g, int(silu), 1e-12, y)
+    got = host(y)
+    ref = O.f16(O.rmsnorm(x_nhwc.reshape(M, -1).T, gamma, bias=bias, silu=silu)).T
+    return got, ref
+
+
+def _assert_f16_close(got_real, ref):
+    u = f16_ulps(got_real, ref.astype(np.float16))
+    assert np.max(u) <= 1, "max ulp %d" % np.max(u)
+    exact = float(np.mean(u == 0))
+    assert exact >= 0.999, "exact fraction %.5f" % exact
+    return exact
+
+
+def test_rmsnorm_config1():
+    d = synth.config1()
+    got, ref = _norm_case(d["x"], d["gamma"], 128, 128)
+    assert not np.isnan(got).any()
+    _assert_f16_close(got, ref)
+
+
+@pytest.mark.parametrize("c,cp,with_bias,silu", [(288, 320, True, True), (144, 192, False, True),
+                                                 (128, 128, True, False), (64, 64, True, True),
+                                                 (512, 512, False, True), (576, 576, True, True),
+                                                 (1000, 1024, True, False)])
+def test_rmsnorm_widths_bias_padding(c, cp, with_bias, silu):
+    H, W = 7, 9  # M = 63, not a multiple of the 16-pixel block
+    x = synth.normal(11, c, (H, W, c), 4.0)
+    gamma = synth.uniform(11, c + 1, (c,), 0.5, 1.5)
+    bias = synth.normal(11, c + 2, (c,), 0.02) if with_bias else None
+    got, ref = _norm_case(x, gamma, c, cp, bias, silu)
+    assert not np.isnan(got).any()
+    assert np.all(got[:, c:] == 0), "padded channels must stay zero"
+    _assert_f16_close(got[:, :c], ref)
+
+
+def test_rmsnorm_zero_and_single_pixel():
+    x = np.zeros((1, 1, 128), np.float32)
+    got, _ = _norm_case(x, np.ones(128, np.float32), 128, 128)
+    assert np.all(got == 0)
+    x = synth.normal(12, 0, (1, 1, 128), 1.0)
+    got, ref = _norm_case(x, np.ones(128, np.float32), 128, 128, silu=False)
+    _assert_f16_close(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# guarded cast
+# ---------------------------------------------------------------------------
+
+
+def test_guard_cast_config2_is_exact():
+    d = synth.config2()
+    H, W, C = d["x"].shape
+    M = H * W
+    y = nan_f16((M, C))
+    ig.guard_cast(dev(d["x"].reshape(M, C)), M, C, None, d["guard_log2"], y)
+    got = host(y)
+    ref = O.guard_cast(d["x"].reshape(M, C), d["guard_log2"])
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("g", [0, 8, 14])
+def test_guard_cast_bias_and_range(g):
+    M, C = 333, 64
+    x = synth.normal(13, g, (M, C), 1.0e10)  # std 1e5: past the f16 range
+    b = synth.normal(13, 100 + g, (C,), 0.02)
+    y = nan_f16((M, C))
+    ig.guard_cast(dev(x), M, C, dev(b), g, y)
+    got = host(y)
+    ref = O.guard_cast(x.T, g, bias=b).T  # the oracle is channel-first
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    _assert_f16_close(got[fin], ref[fin])
+    if g == 8:
+        assert fin.all()  # 2^-8 keeps |x| < 65504 * 256 finite
+
+
+# ---------------------------------------------------------------------------
+# 3x3 convolution
+# ---------------------------------------------------------------------------
+
+
+def _conv_isolated(H, W, cin, cout, mode, seed, oscale=1.0, with_bias=True):
+    """Seeded f16 input shared by both sides; returns (got, ref) as [C,H,W]."""
+    x16 = synth.normal(14, seed, (H, W, cin), 1.0, np.float16)
+    k = 1 if mode == 0 else 3
+    w = synth.normal(14, seed + 1, (cout, cin, k, k), 1.0 / (k * k * cin), np.float16)
+    b = synth.normal(14, seed + 2, (cout,), 0.02) if with_bias else None
+    cin_p, cout_p = cpad(cin), cpad(cout)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    y = nan_f32((Ho * Wo, cout_p))
+    bd = padded_vec(b, cout_p) if with_bias else None
+    ig.conv_nhwc_ex(dev(pad_last(x16.reshape(H * W, cin), cin_p)), H, W, cin_p, mode, packed(w),
+                    cout_p, bd, oscale, 0, y)
+    got = host(y)
+    assert not np.isnan(got).any(), "output not fully written"
+    assert np.all(got[:, cout:] == 0), "padded output channels must be zero"
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    if mode == 2:
+        ref = oscale * O.conv2d_up2(xc, w) + (0 if b is None else b[:, None, None])
+    else:
+        ref = oscale * O.conv2d(xc, w) + (0 if b is None else b[:, None, None])
+    return nhwc_to_chw(got[:, :cout], Ho, Wo), ref
+
+
+@pytest.mark.parametrize("H,W,cin,cout", [(64, 64, 128, 128), (13, 29, 64, 192), (1, 1, 64, 64),
+                                          (5, 1, 128, 64), (1, 7, 64, 128), (33, 17, 320, 320),
+                                          (9, 70, 256, 512)])
+def test_conv3x3_isolated(H, W, cin, cout):
+    got, ref = _conv_isolated(H, W, cin, cout, 1, seed=H * 7 + W)
+    err, rms, ratio = conv_err(got, ref)
+    print("conv3x3 %dx%d %d->%d: max|d| %.3e rms %.3e ratio %.2e" % (H, W, cin, cout, err, rms, ratio))
+    assert ratio <= CONV_TOL
+    assert ratio <= 1e-4  # identical f16 inputs: only f32 accumulation order differs
+
+
+@pytest.mark.parametrize("H,W,cin,cout", [(9, 13, 64, 128), (1, 1, 64, 64), (16, 3, 128, 192)])
+def test_conv3x3_up2_isolated(H, W, cin, cout):
+    got, ref = _conv_isolated(H, W, cin, cout, 2, seed=100 + H, oscale=256.0)
+    err, rms, ratio = conv_err(got, ref)
+    print("up2 %dx%d %d->%d: ratio %.2e" % (H, W, cin, cout, ratio))
+    assert ratio <= CONV_TOL and ratio <= 1e-4
+
+
+@pytest.mark.parametrize("H,W,cin,cout", [(11, 23, 256, 256), (1, 1, 64, 64), (32, 32, 512, 256)])
+def test_conv1x1_isolated(H, W, cin, cout):
+    got, ref = _conv_isolated(H, W, cin, cout, 0, seed=200 + H)
+    assert conv_err(got, ref)[2] <= 1e-4
+
+
+def test_conv_accumulate_epilogue():
+    H, W, c = 10, 12, 64
+    x16 = synth.normal(15, 0, (H * W, c), 1.0, np.float16)
+    w = synth.normal(15, 1, (c, c, 3, 3), 1.0 / (9 * c), np.float16)
+    b = synth.normal(15, 2, (c,), 0.02)
+    y0 = synth.normal(15, 3, (H * W, c), 1.0)
+    y = dev(y0)
+    ig.conv_nhwc_ex(dev(x16), H, W, c, 1, packed(w), c, dev(b), 0.5, 1, y)
+    got = nhwc_to_chw(host(y), H, W)
+    ref = nhwc_to_chw(y0.astype(np.float64), H, W) + 0.5 * O.conv2d(nhwc_to_chw(x16.astype(np.float64), H, W), w) + b[:, None, None]
+    assert conv_err(got, ref)[2] <= 1e-4
+
+
+def test_config1_norm_then_conv():
+    """The whole config-1 unit: RMS_norm + SiLU -> f16 -> 3x3 conv (+bias)."""
+    d = synth.config1()
+    H, W, C = d["x"].shape
+    xn = nan_f16((H * W, C))
+    ig.rmsnorm_silu_f16(dev(d["x"].reshape(H * W, C)), H * W, C, C, None, dev(d["gamma"]), 1, 1e-12, xn)
+    y = nan_f32((H * W, C))
+    ig.conv3x3_nhwc(xn, H, W, C, packed(d["w"]), C, dev(d["b"]), 1.0, y)
+    got = nhwc_to_chw(host(y), H, W)
+    xref = O.f16(O.rmsnorm(nhwc_to_chw(d["x"], H, W), d["gamma"], silu=True))
+    ref = O.conv2d(xref, d["w"], d["b"])
+    err, rms, ratio = conv_err(got, ref)
+    print("config1: max|d| %.3e rms %.3e ratio %.2e" % (err, rms, ratio))
+    assert ratio <= CONV_TOL
+
+
+# ---------------------------------------------------------------------------
+# config 2: guarded up conv + 1x1 shortcut, added in f32
+# ---------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def cfg2_run():
+    d = synth.config2()
+    H, W, C = d["x"].shape
+    M = H * W
+    g = d["guard_log2"]
+    gs = float(2 ** g)
+    xg = nan_f16((M, C))
+    ig.guard_cast(dev(d["x"].reshape(M, C)), M, C, None, g, xg)
+    up = nan_f32((4 * M, C))
+    ig.conv3x3_up2_nhwc(xg, H, W, C, packed(d["w_up"]), C, dev(d["b_up"]), gs, up)
+    sc = nan_f32((M, C))
+    plane_sc = packed(d["w_sc"])
+    ig.gemm1x1(xg, M, C, C, plane_sc, C, C, dev(d["b_sc"]), gs, sc, C, 0)
+    tot = up.clone()
+    ig.dupup_add(sc, H, W, C, tot, C, C, 4, 4, 1)
+    xq = nhwc_to_chw(O.guard_cast(d["x"].reshape(M, C), g), H, W)
+    return d, host(up), host(sc), host(tot), xq
+
+
+def test_config2_shortcut_gemm(cfg2_run):
+    d, _, sc, _, xq = cfg2_run
+    H, W, C = d["x"].shape
+    ref = 2.0 ** d["guard_log2"] * O.conv2d(xq, d["w_sc"]) + d["b_sc"][:, None, None]
+    err, rms, ratio = conv_err(nhwc_to_chw(sc, H, W), ref)
+    print("config2 shortcut: ratio %.2e" % ratio)
+    assert ratio <= CONV_TOL and ratio <= 1e-4
+
+
+def test_config2_up_conv_sampled(cfg2_run):
+    d, up, _, _, xq = cfg2_run
+    H, W, C = d["x"].shape
+    pix = sample_pixels(2 * H, 2 * W, 1024, seed=2)
+    ref = 2.0 ** d["guard_log2"] * O.conv2d_at(xq, d["w_up"], pix, up2=True) + d["b_up"][None, :]
+    err, rms, ratio = conv_err(up[pix], ref)
+    print("config2 up conv (%d px): ratio %.2e" % (len(pix), ratio))
+    assert not np.isnan(up).any()
+    assert ratio <= CONV_TOL and ratio <= 1e-4
+
+
+def test_config2_sum_sampled(cfg2_run):
+    d, _, _, tot, xq = cfg2_run
+    H, W, C = d["x"].shape
+    gs = 2.0 ** d["guard_log2"]
+    pix = sample_pixels(2 * H, 2 * W, 1024, seed=3)
+    up = gs * O.conv2d_at(xq, d["w_up"], pix, up2=True) + d["b_up"][None, :]
+    src = (pix // (2 * W)) // 2 * W + (pix % (2 * W)) // 2  # nearest-2x source pixel
+    sc = gs * O.conv2d_at(xq, d["w_sc"], src) + d["b_sc"][None, :]
+    err, rms, ratio = conv_err(tot[pix], up + sc)
+    print("config2 up + shortcut: ratio %.2e" % ratio)
+    assert ratio <= CONV_TOL
+
+
+# ---------------------------------------------------------------------------
+# config 3: the large-tile conv and its padded variants
+# ---------------------------------------------------------------------------
+
+
+def _cfg3(c, H, W, n_sample=None):
+    d = synth.config3(c, H, W)
+    cp = cpad(c)
+    M = H * W
+    xd = dev(pad_last(d["x"].reshape(M, c), cp))
+    xn = nan_f16((M, cp))
+    ig.rmsnorm_silu_f16(xd, M, cp, c, None, padded_vec(d["gamma"], cp), 0, 1e-12, xn)
+    y = nan_f32((M, cp))
+    ig.conv3x3_nhwc(xn, H, W, cp, packed(d["w"]), cp, padded_vec(d["b"], cp), 1.0, y)
+    got = host(y)
+    assert not np.isnan(got).any()
+    assert np.all(got[:, c:] == 0), "padded output channels must be zero"
+    xref = O.f16(O.rmsnorm(nhwc_to_chw(d["x"], H, W), d["gamma"]))
+    if n_sample is None:
+        ref = O.conv2d(xref, d["w"], d["b"])
+        return conv_err(nhwc_to_chw(got[:, :c], H, W), ref)
+    pix = sample_pixels(H, W, n_sample, seed=c)
+    ref = O.conv2d_at(xref, d["w"], pix, d["b"])
+    return conv_err(got[pix, :c], ref)
+
+
+@pytest.mark.parametrize("c", [128, 288, 144])
+def test_config3_small_full(c):
+    err, rms, ratio = _cfg3(c, 48, 40)
+    print("config3 %d @48x40: ratio %.2e" % (c, ratio))
+    assert ratio <= CONV_TOL
+
+
+@pytest.mark.parametrize("c", [128, 288, 144])
+def test_config3_full_size_sampled(c):
+    err, rms, ratio = _cfg3(c, 512, 512, n_sample=1024)
+    print("config3 %d @512x512 (sampled): ratio %.2e" % (c, ratio))
+    assert ratio <= CONV_TOL
+
+
+# ---------------------------------------------------------------------------
+# GEMM epilogues, softmax, combine, ingest, output
+# ---------------------------------------------------------------------------
+
+
+def test_gemm_f16_out_with_bias():
+    M, K, N = 300, 512, 1024
+    a = synth.normal(16, 0, (M, K), 1.0, np.float16)
+    b = synth.normal(16, 1, (N, K), 1.0 / K, np.float16)
+    bias = synth.normal(16, 2, (N,), 0.02)
+    c = nan_f16((M, N))
+    ig.gemm1x1(dev(a), M, K, K, dev(b), N, K, dev(bias), 1.0, c, N, 1)
+    got = host(c)
+    ref = O.f16(a.astype(np.float64) @ b.astype(np.float64).T + bias)
+    # both sides round to f16; near zero the f32 accumulation error is
+    # several f16 ulps of a tiny value, so the bar is one ulp of the value
+    # or 1e-5 of the output RMS, whichever is larger
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    ulp = np.abs(np.spacing(ref.astype(np.float16)).astype(np.float64))
+    d = np.abs(got.astype(np.float64) - ref)
+    assert np.all(d <= np.maximum(ulp, 1e-5 * rms))
+    assert np.mean(d == 0) >= 0.99
+
+
+def test_gemm_long_k_scaled():
+    M, K, N = 200, 4096, 128
+    a = synth.normal(17, 0, (M, K), 1.0, np.float16)
+    b = synth.normal(17, 1, (N, K), 1.0, np.float16)
+    c = nan_f32((M, N))
+    ig.gemm1x1(dev(a), M, K, K, dev(b), N, K, None, 1.0 / 64, c, N, 0)
+    ref = (a.astype(np.float64) @ b.astype(np.float64).T) / 64
+    assert conv_err(host(c), ref)[2] <= 1e-4
+
+
+def test_softmax_rows():
+    rows, valid, ncols, ld = 37, 1000, 1024, 1024
+    s = synth.normal(18, 0, (rows, ld), 9.0)
+    p = nan_f16((rows, ld))
+    ig.softmax_rows_f16(dev(s), rows, ld, valid, ncols, p, ld)
+    got = host(p)
+    ref = O.f16(O.softmax_rows(s[:, :valid]))
+    assert np.all(got[:, valid:ncols] == 0)
+    u = f16_ulps(got[:, :valid], ref.astype(np.float16))
+    assert np.max(u) <= 2 and np.mean(u == 0) >= 0.99
+
+
+def test_combine_modes():
+    M, C = 77, 128
+    x0 = synth.normal(19, 0, (M, C), 1.0)
+    h = synth.normal(19, 1, (M, C), 1.0)
+    s = synth.normal(19, 2, (M, C), 1.0)
+    hb = synth.normal(19, 3, (C,), 1.0)
+    sb = synth.normal(19, 4, (C,), 1.0)
+    for mode, ref in ((0, x0 + h + hb), (1, s + sb + h + hb), (2, h + hb)):
+        x = dev(x0)
+        ig.combine(x, dev(h), dev(hb), dev(s), dev(sb), M, C, mode)
+        assert np.allclose(host(x), ref, rtol=1e-6, atol=1e-6)
+
+
+def test_latent_ingest_and_output():
+    zc, H, W = 16, 5, 7
+    z = synth.normal(20, 0, (zc, H, W), 1.0)
+    y = nan_f16((H * W, 64))
+    ig.latent_to_nhwc_f16(dev(z), zc, H * W, 64, y)
+    got = host(y)
+    assert np.array_equal(got[:, :zc].astype(np.float64), O.f16(z.reshape(zc, -1).T))
+    assert np.all(got[:, zc:] == 0)
+    yy = synth.normal(20, 1, (H * W, 64), 1.0)
+    b = synth.normal(20, 2, (3,), 1.0)
+    out = nan_f32((3, H * W))
+    ig.nhwc_to_nchw(dev(yy), H * W, 64, 3, dev(b), out)
+    assert np.allclose(host(out), yy[:, :3].T + b[:, None], rtol=1e-7, atol=1e-7)
+
+
+def test_rejected_call_leaves_output_untouched():
+    y = nan_f32((16, 64))
+    x = torch.zeros((16, 100), dtype=torch.float16, device="cuda")
+    w = torch.zeros((64, 9, 100), dtype=torch.float16, device="cuda")
+    with pytest.raises(ig.IgError) as e:
+        ig.conv3x3_nhwc(x, 4, 4, 100, w, 64, None, 1.0, y)
+    assert e.value.code == -2
+    assert torch.isnan(y).all()
