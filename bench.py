@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the resident decoder's conv path on one MI355X.
+
+One step = one whole decode (decoder_forward) of the synthetic decoder at
+1024x1024 output: latent [16, 128, 128] ~ N(0,1)*8, conv_in gain 2^11 (the
+stream passes the f16 range), guard 2^-8, every tensor resident in HBM.
+`value` is the decode's algorithmic TFLOP/s (real channels; 3x3 and 1x1
+convs at 2*M*cin*cout*k^2, attention at 2*m^2*C per product plus its four
+projections); `decode_s` is seconds per decode.
+
+Also measured, in the same process and on the stream the kernels run on:
+  * roofline: the dominant kernel, the 3x3 implicit-GEMM conv at
+    512x512x128 -> 128 (77.31 GFLOP per launch), against the dense f16
+    MFMA peak of 2.5 PFLOP/s; inputs and outputs rotate through a pool
+    larger than the 256 MB Infinity Cache;
+  * roofline_norm: RMS_norm + f16 store at 512x512x128 (201 MB moved per
+    launch: f32 read + f16 write) against 8 TB/s HBM;
+  * cpu_baseline: the CPU oracle decoding the 256x256 configuration (a
+    bounded sample of the same decoder), in TFLOP/s.
+
+`python bench.py --digest-trace <kernel_trace.csv>` turns a rocprofv3
+kernel trace of this command into the per-kernel summary kept in profiles/.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+ROOF_KERNEL = "k_igemm<1, 256, 128, false>"  # the 3x3 conv instantiation for 512^2 x 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+
+def decode_flops(spec, h0, w0):
+    """Algorithmic FLOP of one decode (real channel counts)."""
+    f = 0.0
+    M = h0 * w0
+    f += 2.0 * M * spec.zc * spec.c_in * 9  # conv_in
+
+    def resnet(cin, cout, M):
+        v = 2.0 * M * cin * cout * 9 + 2.0 * M * cout * cout * 9
+        if cin != cout:
+            v += 2.0 * M * cin * cout
+        return v
+
+    c = spec.c_in
+    f += 2 * resnet(c, c, M)
+    C = spec.attn_c
+    f += 4 * 2.0 * M * C * C + 2 * 2.0 * M * M * C  # q, k, v, proj; QK^T and P.V
+    for cs in spec.stages:
+        for r in range(spec.n_res):
+            f += resnet(c if r == 0 else cs, cs, M)
+        c = cs
+        M *= 4
+        f += 2.0 * M * c * c * 9  # the up conv at the doubled size
+    f += 2.0 * M * c * spec.out_c * 9  # conv_out
+    return f
+
+
+# ---------------------------------------------------------------------------
+# measurements
+# ---------------------------------------------------------------------------
+
+
+def bench_decode(steps, warmup, h0, q_chunk):
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+    import synth
+
+    spec = synth.decoder_spec()
+    w = synth.decoder_weights(spec, seed_config=4, conv_in_gain=2.0 ** 11)
+    z = synth.decoder_latent(h0, h0, zc=spec.zc, config=5, scale=8.0)
+    dd = ig.DeviceDecoder(w)
+    zd = torch.from_numpy(z).cuda()
+    ws = dd.alloc_workspace(h0, h0, q_chunk)
+    H = h0 << dd.n_up
+    out = torch.empty((dd.out_c, H, H), dtype=torch.float32, device="cuda")
+    log("decode %dx%d: workspace %.2f GB" % (H, H, ws[1] / 1e9))
+    for _ in range(warmup):
+        dd.forward(zd, h0, h0, guard_log2=8, q_chunk=q_chunk, ws=ws, out=out)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        dd.forward(zd, h0, h0, guard_log2=8, q_chunk=q_chunk, ws=ws, out=out)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    finite = bool(torch.isfinite(out).all().item())
+    flops = decode_flops(spec, h0, h0)
+    del ws
+    return {"wall_s": wall, "event_ms": ev_ms, "flops": flops, "finite": finite, "H": H, "spec": spec}
+
+
+def bench_conv_roofline(reps, H=512, W=512, C=128):
+    """The 3x3 conv of the 512^2 x 128 -> 128 configuration, timed with HIP
+    events on the launch stream, buffers rotated through > 1 GB."""
+    import numpy as np
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+    import synth
+
+    d = synth.config3(C, H, W)
+    M = H * W
+    dev = torch.device("cuda")
+    w16 = torch.from_numpy(d["w"]).to(dev)
+    plane = torch.empty((C, 9, C), dtype=torch.float16, device=dev)
+    ig.pack_conv_weights(w16, C, C, 3, C, C, plane)
+    bias = torch.from_numpy(d["b"]).to(dev)
+    gamma = torch.from_numpy(d["gamma"]).to(dev)
+    x32 = torch.from_numpy(d["x"].reshape(M, C)).to(dev)
+    per_set = M * C * (2 + 4)
+    nsets = max(2, int(np.ceil(1.2e9 / per_set)))
+    xs = [torch.empty((M, C), dtype=torch.float16, device=dev) for _ in range(nsets)]
+    ys = [torch.empty((M, C), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    for t in xs:
+        ig.rmsnorm_silu_f16(x32, M, C, C, None, gamma, 0, 1e-12, t)
+    for i in range(3):
+        ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets])
+    e1.record()
+    torch.cuda.synchronize()
+    avg_ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * M * C * C * 9
+    byts = M * C * 2 + C * 9 * C * 2 + M * C * 4
+    ok = bool(torch.isfinite(ys[(reps - 1) % nsets]).all().item())
+    return {"avg_ms": avg_ms, "flops": flops, "bytes": byts, "launches": reps + 3, "finite": ok,
+            "sets": nsets}
+
+
+def bench_norm_roofline(reps, H=512, W=512, C=128):
+    import numpy as np
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+    import synth
+
+    d = synth.config3(C, H, W)
+    M = H * W
+    dev = torch.device("cuda")
+    gamma = torch.from_numpy(d["gamma"]).to(dev)
+    per_set = M * C * 6
+    nsets = max(2, int(np.ceil(1.2e9 / per_set)))
+    x0 = torch.from_numpy(d["x"].reshape(M, C)).to(dev)
+    xs = [x0.clone() for _ in range(nsets)]
+    ys = [torch.empty((M, C), dtype=torch.float16, device=dev) for _ in range(nsets)]
+    for i in range(3):
+        ig.rmsnorm_silu_f16(xs[i], M, C, C, None, gamma, 1, 1e-12, ys[i])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        ig.rmsnorm_silu_f16(xs[i % nsets], M, C, C, None, gamma, 1, 1e-12, ys[i % nsets])
+    e1.record()
+    torch.cuda.synchronize()
+    avg_ms = e0.elapsed_time(e1) / reps
+    return {"avg_ms": avg_ms, "bytes": M * C * 6, "sets": nsets}
+
+
+def cpu_baseline(min_seconds=10.0):
+    """The oracle (as it is) decoding the 256x256 configuration on the host."""
+    import oracle as O
+    import synth
+
+    spec = synth.decoder_spec()
+    w = synth.decoder_weights(spec, seed_config=4)
+    z = synth.decoder_latent(32, 32, zc=spec.zc, config=4)
+    O.decode(w, z, guard_log2=8, q_chunk=256)  # build + warm the library
+    n, t = 0, 0.0
+    while t < min_seconds or n == 0:
+        t0 = time.perf_counter()
+        O.decode(w, z, guard_log2=8, q_chunk=256)
+        t += time.perf_counter() - t0
+        n += 1
+    flops = decode_flops(spec, 32, 32) * n
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d oracle decode(s) of the 256x256 configuration (latent 32x32x16, same "
+                      "decoder, f64 direct loops), %.1f s" % (n, t)}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 trace digest
+# ---------------------------------------------------------------------------
+
+
+def digest_trace(path, roof_launches):
+    """Per-kernel totals of a rocprofv3 kernel trace, plus the average of the
+    roofline region's launches of the dominant kernel (its last
+    `roof_launches` dispatches: that region runs after the decodes)."""
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    stats = {}
+    seq = []
+    for r in rows:
+        name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+        s = stats.setdefault(name, [0, 0.0])
+        s[0] += 1
+        s[1] += t
+        seq.append((int(r["Start_Timestamp"]), name, t, r.get("Grid_Size", r.get("Grid_Size_X", ""))))
+    seq.sort()
+    tot = sum(v[1] for v in stats.values())
+    print("kernel | calls | total us | avg us | share")
+    for name, (n, t) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        short = name if len(name) < 90 else name[:87] + "..."
+        print("%s | %d | %.1f | %.2f | %.1f%%" % (short, n, t, t / n, 100 * t / tot))
+    roof = [x for x in seq if ROOF_KERNEL.replace(" ", "") in x[1].replace(" ", "")]
+    last = roof[-roof_launches:]
+    if last:
+        avg = sum(x[2] for x in last) / len(last)
+        print("roofline region: last %d dispatches of %s (grid %s): avg %.2f us" % (
+            len(last), ROOF_KERNEL, last[-1][3], avg))
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--latent", type=int, default=128, help="latent side (output = 8x)")
+    ap.add_argument("--q-chunk", type=int, default=0)
+    ap.add_argument("--roof-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--digest-trace", default=None)
+    args = ap.parse_args()
+
+    if args.digest_trace:
+        digest_trace(args.digest_trace, args.roof_reps + 3)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the decoder on a single MI355X "
+              "(--gpus %d requested). Multi-GPU sharding is a design note only." % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("device:", torch.cuda.get_device_name(0))
+
+    dec = bench_decode(args.steps, args.warmup, args.latent, args.q_chunk)
+    ms = dec["wall_s"] * 1000.0 / args.steps
+    ev_ms = dec["event_ms"] / args.steps
+    tflops = dec["flops"] / (ms / 1000.0) / 1e12
+    log("decode %d^2: %.3f ms/step (events %.3f), %.1f TFLOP/s, finite=%s" % (
+        dec["H"], ms, ev_ms, tflops, dec["finite"]))
+
+    conv = bench_conv_roofline(args.roof_reps)
+    conv_tf = conv["flops"] / (conv["avg_ms"] / 1000.0) / 1e12
+    log("conv3x3 512^2x128: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (
+        conv["avg_ms"] * 1000, conv_tf, 100 * conv_tf / MFMA_F16_PEAK_TFLOPS))
+    norm = bench_norm_roofline(args.roof_reps)
+    norm_gbs = norm["bytes"] / (norm["avg_ms"] / 1000.0) / 1e9
+    log("rmsnorm 512^2x128: %.2f us, %.0f GB/s (%.1f%% of HBM)" % (
+        norm["avg_ms"] * 1000, norm_gbs, 100 * norm_gbs / HBM_PEAK_GBS))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+        log("cpu baseline: %.4f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+
+    spec = dec["spec"]
+    res = {
+        "metric": "3x3 conv TFLOP/s (f16->f32, % MFMA peak) + full decode s at 1024^2",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "synthetic VAE decoder, %dx%d output, whole frame resident in HBM" % (dec["H"], dec["H"]),
+            "latent": [spec.zc, args.latent, args.latent],
+            "channels": [spec.c_in] + list(spec.stages),
+            "resnets_per_stage": spec.n_res,
+            "attention_tokens": args.latent * args.latent,
+            "guard_log2": 8,
+            "q_chunk": args.q_chunk or "default",
+        },
+        "decode_s": round(ms / 1000.0, 6),
+        "decode_tflop": round(dec["flops"] / 1e12, 4),
+        "output_finite": dec["finite"],
+        "roofline": {
+            "kernel": "conv3x3_nhwc %s, 512x512x128->128" % ROOF_KERNEL,
+            "bound": "mfma",
+            "achieved": round(conv_tf, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(conv_tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(conv["avg_ms"] * 1000, 3),
+            "algorithmic_bytes": conv["bytes"],
+        },
+        "roofline_norm": {
+            "kernel": "rmsnorm_silu_f16 512x512x128",
+            "bound": "hbm",
+            "achieved": round(norm_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(norm_gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(norm["avg_ms"] * 1000, 3),
+        },
+        "cpu_baseline": cpu,
+        "context": "pages: 0.49-0.61 s per 1024^2 decode on an RTX PRO 4000 Blackwell "
+                   "(Qwen-Image-2.1 VAE, real weights; other model and machine)",
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

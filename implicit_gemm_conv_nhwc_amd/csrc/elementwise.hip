@@ -292,7 +292,10 @@ __global__ __launch_bounds__(256) void k_out(const float *__restrict__ y, int M,
 }
 
 // ---------------------------------------------------------------------
-// weight plane: OIHW [cout][cin][k][k] -> [cout_p][k*k][cin_p], zero pad
+// weight planes from OIHW [cout][cin][k][k], zero padded: 1x1 ->
+// [cout_p][cin_p] (the GEMM's B rows); 3x3 -> [cin_p/16][9][cout_p][16]
+// (for each 16-channel slice and tap, the output channels' 16 weights are
+// contiguous, so a conv stage reads its weights as one block)
 // ---------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pack(const _Float16 *__restrict__ w, int cout, int cin,
                                               int kk, int cout_p, int cin_p,
@@ -300,10 +303,18 @@ __global__ __launch_bounds__(256) void k_pack(const _Float16 *__restrict__ w, in
 {
     const int64_t n = (int64_t)cout_p * kk * cin_p;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int ci = (int)(i % cin_p);
-        const int64_t ot = i / cin_p;
-        const int tap = (int)(ot % kk);
-        const int o = (int)(ot / kk);
+        int ci, tap, o;
+        if (kk == 1) {  // [cout_p][cin_p]
+            ci = (int)(i % cin_p);
+            o = (int)(i / cin_p);
+            tap = 0;
+        } else {  // [cin_p/16][9][cout_p][16]
+            const int c16 = (int)(i & 15);
+            const int64_t rest = i >> 4;
+            o = (int)(rest % cout_p);
+            tap = (int)((rest / cout_p) % kk);
+            ci = (int)(rest / ((int64_t)cout_p * kk)) * 16 + c16;
+        }
         plane[i] = (o < cout && ci < cin) ? w[((int64_t)o * cin + ci) * kk + tap] : (_Float16)0.f;
     }
 }

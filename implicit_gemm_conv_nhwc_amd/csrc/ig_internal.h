@@ -38,8 +38,11 @@ struct IgemmArgs {
     int out_f16;
 };
 
-// Launch the MFMA implicit GEMM for `mode`; picks the tile shape.
+// Launch the MFMA implicit GEMM for `mode`; picks the tile shape. The 3x3
+// modes go to the patch-reusing convolution kernel.
 void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s);
+// The 3x3 convolutions (kConv3x3, kConv3x3Up2) with per-tile input patches.
+void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------------
 // memory-bound kernels

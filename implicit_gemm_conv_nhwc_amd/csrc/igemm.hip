@@ -35,62 +35,68 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));  // per-thread row state, in registers
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
 
 constexpr int BK = 32;           // K elements per pipeline step
 constexpr int LDS_ROW = BK + 8;  // halves per LDS row (64 B data + 16 B pad)
 constexpr int NT = 256;          // threads per workgroup
 
-// Per-thread gather state for A: output pixel coordinates (convs) or the
-// row pointer (GEMM) of each row this thread loads.
-template <int MODE, int A_PER>
-struct AGather {
-    int oy[A_PER], ox[A_PER];
-    const _Float16 *row[A_PER];
-};
+// Buffer resource over `bytes` bytes at `base`: loads at offsets at or past
+// `bytes` return zero, which is how the gather reads the convolution's zero
+// padding and masks rows past M without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+constexpr int kOOB = 0x7fffffff;  // an offset past every resource
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 template <int MODE, int A_PER, int B_PER>
-__device__ __forceinline__ void load_step(const IgemmArgs &p, const AGather<MODE, A_PER> &g,
-                                          const _Float16 *const (&b_row)[B_PER], int q, int ks,
-                                          int Hout, int Wout, uint4 (&ra)[A_PER], uint4 (&rb)[B_PER])
+__device__ __forceinline__ void load_step(const IgemmArgs &p, __amdgpu_buffer_rsrc_t ra_src,
+                                          int4v g_oy, int4v g_ox, const _Float16 *b_base,
+                                          int64_t b_stride, int q, int ks,
+                                          int Hout, int Wout, u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER])
 {
     int kb;
     if (MODE == kGemm) {
         kb = ks * BK;
 #pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (g.row[j]) v = *reinterpret_cast<const uint4 *>(g.row[j] + kb);
-            ra[j] = v;
-        }
+        for (int j = 0; j < A_PER; ++j)  // rows past M are past the resource
+            ra[j] = buf_load16(ra_src, (g_oy[j] * p.lda + kb + q * 8) * 2);
     } else {
         const int c = ks / 9;
         const int tap = ks - 9 * c;
         const int dy = tap / 3, dx = tap - 3 * dy;
         kb = tap * p.cin_p + c * BK;
-        const _Float16 *abase = p.a + c * BK + q * 8;
+        const int cofs = c * BK + q * 8;
 #pragma unroll
         for (int j = 0; j < A_PER; ++j) {
-            const int uy = g.oy[j] + dy - 1, ux = g.ox[j] + dx - 1;
+            const int uy = g_oy[j] + dy - 1, ux = g_ox[j] + dx - 1;
             const bool ok = (uy >= 0) & (uy < Hout) & (ux >= 0) & (ux < Wout);
             const int sy = (MODE == kConv3x3Up2) ? (uy >> 1) : uy;
             const int sx = (MODE == kConv3x3Up2) ? (ux >> 1) : ux;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ok) v = *reinterpret_cast<const uint4 *>(abase + (int64_t)(sy * p.W + sx) * p.cin_p);
-            ra[j] = v;
+            const int off = ok ? ((sy * p.W + sx) * p.cin_p + cofs) * 2 : kOOB;
+            ra[j] = buf_load16(ra_src, off);
         }
     }
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j) rb[j] = *reinterpret_cast<const uint4 *>(b_row[j] + kb);
+    for (int j = 0; j < B_PER; ++j) rb[j] = *reinterpret_cast<const u32x4 *>(b_base + j * b_stride + kb);
 }
 
 template <int BM, int BN, int A_PER, int B_PER>
 __device__ __forceinline__ void store_step(_Float16 (*sA)[LDS_ROW], _Float16 (*sB)[LDS_ROW], int rbase,
-                                           int q, const uint4 (&ra)[A_PER], const uint4 (&rb)[B_PER])
+                                           int q, const u32x4 (&ra)[A_PER], const u32x4 (&rb)[B_PER])
 {
 #pragma unroll
-    for (int j = 0; j < A_PER; ++j) *reinterpret_cast<uint4 *>(&sA[rbase + 64 * j][q * 8]) = ra[j];
+    for (int j = 0; j < A_PER; ++j) *reinterpret_cast<u32x4 *>(&sA[rbase + 64 * j][q * 8]) = ra[j];
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j) *reinterpret_cast<uint4 *>(&sB[rbase + 64 * j][q * 8]) = rb[j];
+    for (int j = 0; j < B_PER; ++j) *reinterpret_cast<u32x4 *>(&sB[rbase + 64 * j][q * 8]) = rb[j];
 }
 
 template <int FM, int FN, int WTM, int WTN>
@@ -120,6 +126,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     constexpr int WTM = BM / 2, WTN = BN / 2;        // wave tile
     constexpr int FM = WTM / 32, FN = WTN / 32;      // 32x32 MFMA tiles per wave
     constexpr int A_PER = BM / 64, B_PER = BN / 64;  // 16-byte loads per thread per step
+    static_assert(A_PER <= 4, "row state holds at most 4 rows");
 
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM][LDS_ROW];
     __shared__ __attribute__((aligned(16))) _Float16 sB[2][BN][LDS_ROW];
@@ -143,25 +150,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int Wout = (MODE == kConv3x3Up2) ? 2 * p.W : p.W;
     const int Hout = (MODE == kConv3x3Up2) ? 2 * p.H : p.H;
 
-    AGather<MODE, A_PER> g;
+    // per-thread gather state: output pixel (convs) or block row (GEMM) of
+    // each row this thread loads
+    int4v g_oy = {0, 0, 0, 0}, g_ox = {0, 0, 0, 0};
+    __amdgpu_buffer_rsrc_t a_src;
+    if (MODE == kGemm) {
+        // the block's rows only: offsets stay small, rows past M read zero
+        const int rows = (p.M - m0) < BM ? (p.M - m0) : BM;
+        a_src = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)rows * p.lda * 2);
 #pragma unroll
-    for (int j = 0; j < A_PER; ++j) {
-        const int m = m0 + rbase + 64 * j;
-        if (MODE == kGemm) {
-            g.row[j] = (m < p.M) ? p.a + (int64_t)m * p.lda + q * 8 : nullptr;
-            g.oy[j] = 0;
-            g.ox[j] = 0;
-        } else {
-            g.row[j] = nullptr;
+        for (int j = 0; j < A_PER; ++j) {
+            g_oy[j] = rbase + 64 * j;
+            g_ox[j] = 0;
+        }
+    } else {
+        a_src = make_rsrc(p.a, (uint32_t)p.H * p.W * p.cin_p * 2);
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j) {
+            const int m = m0 + rbase + 64 * j;
             const bool in = m < p.M;
             const int oy = m / Wout;
-            g.oy[j] = in ? oy : -(1 << 28);  // an out-of-range row fails every bounds test
-            g.ox[j] = m - oy * Wout;
+            g_oy[j] = in ? oy : -(1 << 28);  // an out-of-range row fails every bounds test
+            g_ox[j] = m - oy * Wout;
         }
     }
-    const _Float16 *b_row[B_PER];
-#pragma unroll
-    for (int j = 0; j < B_PER; ++j) b_row[j] = p.b + (int64_t)(n0 + rbase + 64 * j) * p.ldb + q * 8;
+    // B rows n0 + rbase + 64j
+    const _Float16 *b_base = p.b + (int64_t)(n0 + rbase) * p.ldb + q * 8;
+    const int64_t b_stride = (int64_t)64 * p.ldb;
 
     const int nks = (MODE == kGemm) ? (p.K / BK) : 9 * (p.cin_p / BK);
 
@@ -176,15 +191,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int frow = lane & 31;      // fragment row (A) / column (B)
     const int fk = (lane >> 5) * 8;  // this lane's 8 K elements within 16
 
-    uint4 ra[A_PER], rb[B_PER];
-    load_step<MODE, A_PER, B_PER>(p, g, b_row, q, 0, Hout, Wout, ra, rb);
+    u32x4 ra[A_PER], rb[B_PER];
+    load_step<MODE, A_PER, B_PER>(p, a_src, g_oy, g_ox, b_base, b_stride, q, 0, Hout, Wout, ra, rb);
     store_step<BM, BN, A_PER, B_PER>(sA[0], sB[0], rbase, q, ra, rb);
     __syncthreads();
 
     int cur = 0;
     for (int ks = 0; ks < nks - 1; ++ks) {
-        load_step<MODE, A_PER, B_PER>(p, g, b_row, q, ks + 1, Hout, Wout, ra, rb);
+        // the next step's loads go out first and stay first: the MFMAs of
+        // this step hide their latency
+        load_step<MODE, A_PER, B_PER>(p, a_src, g_oy, g_ox, b_base, b_stride, q, ks + 1, Hout, Wout, ra, rb);
+        __builtin_amdgcn_sched_barrier(0);
         mma_step<FM, FN, WTM, WTN>(sA[cur], sB[cur], wm, wn, frow, fk, acc);
+        __builtin_amdgcn_sched_barrier(0);
         store_step<BM, BN, A_PER, B_PER>(sA[cur ^ 1], sB[cur ^ 1], rbase, q, ra, rb);
         __syncthreads();
         cur ^= 1;
@@ -252,8 +271,8 @@ void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s)
         if (a.out_f16) launch_mode<kGemm, true>(a, s);
         else launch_mode<kGemm, false>(a, s);
         break;
-    case kConv3x3: launch_mode<kConv3x3, false>(a, s); break;
-    case kConv3x3Up2: launch_mode<kConv3x3Up2, false>(a, s); break;
+    case kConv3x3:
+    case kConv3x3Up2: launch_conv_halo(mode, a, s); break;
     default: break;
     }
 }

@@ -57,11 +57,16 @@ const char *ig_last_error(void);
 int ig_version(void);
 
 /* ---------------------------------------------------------------------
- * Weight packing ([QI] `qconv`): an OIHW f16 conv weight w[cout][cin][k][k]
- * becomes the plane[cout_p][k*k][cin_p] the convolutions read: row o holds
- * (tap, channel) pairs, tap = ky*k + kx, plane[o][tap][ci] =
- * w[o][ci][ky][kx], zero for o >= cout or ci >= cin.
- * k must be 1 or 3; cout_p >= cout, cin_p >= cin, both multiples of 64.
+ * Weight packing ([QI] `qconv`: the f16 "plane" of a conv, zero padded,
+ * K ordered (tap, channel) with tap = ky*3 + kx). From an OIHW f16 weight
+ * w[cout][cin][k][k]:
+ *   k = 1: plane[o][ci] = w[o][ci][0][0]                 -- [cout_p][cin_p]
+ *   k = 3: plane[c][tap][o][e] = w[o][16c + e][ky][kx]    -- [cin_p/16][9][cout_p][16]
+ * zero for o >= cout or channel >= cin. The 3x3 layout keeps, for each
+ * 16-channel slice and tap, the 16 weights of every output channel
+ * together, so a convolution stage reads its weights as one contiguous
+ * block; the plane holds the same numbers as the pages' [cout_p][9][cin_p].
+ * cout_p >= cout, cin_p >= cin, both multiples of 64.
  * --------------------------------------------------------------------- */
 int ig_pack_conv_weights(const uint16_t *w, int cout, int cin, int k, int cout_p, int cin_p,
                          uint16_t *plane, void *stream);
@@ -75,7 +80,8 @@ int ig_pack_conv_weights(const uint16_t *w, int cout, int cin, int k, int cout_p
  * where src(p,tap) is pixel (r+ky-1, c+kx-1) of the H x W image, zero
  * outside it. GEMM shape M = H*W, N = cout_p, K = 9*cin_p.
  *   x:     f16 NHWC [H*W][cin_p]        (cin_p: multiple of 64)
- *   w:     f16 plane [cout_p][9][cin_p] (cout_p: multiple of 64)
+ *   w:     f16 3x3 plane from ig_pack_conv_weights, [cin_p/16][9][cout_p][16]
+ *          (cout_p: multiple of 64)
  *   bias:  f32 [cout_p] or NULL
  *   y:     f32 NHWC [H*W][cout_p]
  * --------------------------------------------------------------------- */
@@ -89,7 +95,7 @@ int conv3x3_nhwc(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, 
  * x is the HALF-resolution H x W image; the output is 2H x 2W. Tap (ky,kx)
  * at output (r,c) reads x[(r+ky-1)/2][(c+kx-1)/2] when 0 <= r+ky-1 < 2H
  * and 0 <= c+kx-1 < 2W, else 0 (zero padding in upsampled coordinates).
- *   x: f16 [H*W][cin_p]; w: f16 [cout_p][9][cin_p]; y: f32 [4*H*W][cout_p]
+ *   x: f16 [H*W][cin_p]; w: f16 3x3 plane (as conv3x3_nhwc); y: f32 [4*H*W][cout_p]
  * A guarded input ([QI] `guard`) is undone with oscale = 2^g.
  * --------------------------------------------------------------------- */
 int conv3x3_up2_nhwc(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout_p,
@@ -97,7 +103,7 @@ int conv3x3_up2_nhwc(const uint16_t *x, int H, int W, int cin_p, const uint16_t 
 
 /* The convolution family with one more output mode.
  *   mode 0: 1x1 conv ([QI] module doc: 1x1 convs as plain GEMMs),
- *           w = [cout_p][cin_p]; mode 1: 3x3 as conv3x3_nhwc;
+ *           w = the 1x1 plane [cout_p][cin_p]; mode 1: 3x3 as conv3x3_nhwc;
  *   mode 2: 3x3 on the nearest-2x upsample as conv3x3_up2_nhwc.
  *   accumulate = 0: y = oscale*acc (+bias)
  *   accumulate = 1: y = y + oscale*acc (+bias)  -- the residual add of
@@ -198,7 +204,7 @@ int ig_zero_rows_f16(uint16_t *y, int r0, int r1, int ld, void *stream);
  * padded widths. All widths are padded to multiples of 64.
  * --------------------------------------------------------------------- */
 typedef struct ig_conv_w {
-    const uint16_t *w; /* packed plane [cout_p][k*k][cin_p] */
+    const uint16_t *w; /* plane from ig_pack_conv_weights (layout by k) */
     const float *b;    /* [cout_p], or NULL for no bias */
     int cin, cout;     /* real channel counts */
     int cin_p, cout_p; /* padded widths */

@@ -29,10 +29,14 @@ def setup_module(module):
 @pytest.mark.parametrize("cout,cin,k", [(128, 128, 3), (3, 128, 3), (288, 288, 3), (256, 512, 1)])
 def test_pack_weights_layout(cout, cin, k):
     w = synth.normal(9, 1, (cout, cin, k, k), 1.0, np.float16)
-    plane = host(packed(w))
-    want = np.zeros((cpad(cout), k * k, cpad(cin)), np.float16)
-    want[:cout, :, :cin] = w.reshape(cout, cin, k * k).transpose(0, 2, 1)
-    assert np.array_equal(plane.view(np.uint16), want.view(np.uint16))
+    plane = host(packed(w)).reshape(-1)
+    full = np.zeros((cpad(cout), cpad(cin), k * k), np.float16)
+    full[:cout, :cin] = w.reshape(cout, cin, k * k)
+    if k == 1:  # [cout_p][cin_p]
+        want = full[:, :, 0]
+    else:  # [cin_p/16][9][cout_p][16]
+        want = full.reshape(cpad(cout), cpad(cin) // 16, 16, 9).transpose(1, 3, 0, 2)
+    assert np.array_equal(plane.view(np.uint16), np.ascontiguousarray(want).reshape(-1).view(np.uint16))
 
 
 # ---------------------------------------------------------------------------
