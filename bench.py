@@ -36,7 +36,29 @@ if ROOT not in sys.path:
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-ROOF_KERNEL = "k_igemm<1, 256, 128, false>"  # the 3x3 conv instantiation for 512^2 x 128
+ROOF_KERNEL = "k_conv_halo<1, 128>"  # the 3x3 conv instantiation for 512^2 x 128
+CONV_SRC = os.path.join(ROOT, "implicit_gemm_conv_nhwc_amd", "csrc", "conv_halo.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_512x512x128_traffic.json")
+
+
+def conv_source_hash():
+    import hashlib
+
+    with open(CONV_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline conv from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != conv_source_hash():
+        return None
+    return t.get("bytes_per_launch")
 
 
 def log(*a):
@@ -212,6 +234,39 @@ def cpu_baseline(min_seconds=10.0):
 # ---------------------------------------------------------------------------
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size (torch elementwise kernel), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print("copy calibration: %d launches, %d bytes read and %d written per launch" % (reps, nbytes, nbytes))
+
+
+def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
+    """Average of `counter` over the roofline conv launches, scaled by the
+    counter's reading for the plain copy (bytes moved / counter value)."""
+    import csv
+
+    def rows(path):
+        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+    conv = [float(r["Counter_Value"]) for r in sorted(rows(conv_csv), key=lambda r: int(r["Start_Timestamp"]))
+            if ROOF_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", "")
+            or "k_conv_halo" in r["Kernel_Name"] and "ILi1ELi128" in r["Kernel_Name"]][-roof_launches:]
+    cp = [float(r["Counter_Value"]) for r in rows(copy_csv) if "mul" in r["Kernel_Name"].lower()
+          or "elementwise" in r["Kernel_Name"].lower()]
+    scale = nbytes / (sum(cp) / len(cp))
+    avg = sum(conv) / len(conv)
+    print("%s: conv %.1f (n=%d), copy %.1f per %d bytes -> scale %.4f bytes/unit -> %.1f MB per launch" % (
+        counter, avg, len(conv), sum(cp) / len(cp), nbytes, scale, avg * scale / 1e6))
+    return avg * scale
+
+
 def digest_trace(path, roof_launches):
     """Per-kernel totals of a rocprofv3 kernel trace, plus the average of the
     roofline region's launches of the dominant kernel (its last
@@ -255,10 +310,21 @@ def main():
     ap.add_argument("--roof-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--digest-trace", default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--digest-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     args = ap.parse_args()
 
     if args.digest_trace:
         digest_trace(args.digest_trace, args.roof_reps + 3)
+        return 0
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+    if args.digest_pmc:
+        f = digest_pmc(args.digest_pmc[0], args.digest_pmc[2], "FETCH_SIZE", args.roof_reps + 3)
+        w = digest_pmc(args.digest_pmc[1], args.digest_pmc[3], "WRITE_SIZE", args.roof_reps + 3)
+        print(json.dumps({"source_sha256_16": conv_source_hash(), "fetch_bytes_per_launch": round(f),
+                          "write_bytes_per_launch": round(w), "bytes_per_launch": round(f + w)}))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -327,7 +393,7 @@ def main():
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(conv_tf / MFMA_F16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(conv["avg_ms"] * 1000, 3),
             "algorithmic_bytes": conv["bytes"],
         },

@@ -9,26 +9,28 @@
 // and `upsample2x`, for the definition (stride 1, zero padding 1).
 //
 // Design (not the pages' 128x64 cooperative-matrix tiling):
-//  * a workgroup owns an output tile of 8 rows x 32 columns x BN channels;
-//    its 4 wave64s split it 2 (rows) x 2 (channels): each wave computes 4
-//    output rows x 32 columns x BN/2 channels as 4 x BN/64 tiles of
-//    v_mfma_f32_32x32x16_f16 (one output row = one 32-row MFMA operand);
+//  * one workgroup of 8 wave64s per CU owns an output tile of 16 rows x 32
+//    columns x BN channels; the waves split it 4 (rows) x 2 (channels):
+//    each wave computes 4 output rows x 32 columns x BN/2 channels as
+//    4 x BN/64 tiles of v_mfma_f32_32x32x16_f16 (one output row is one
+//    32-row MFMA operand);
 //  * the reduction runs in stages of 16 input channels. A stage brings into
-//    LDS the input patch the tile needs -- (8+2) x (32+2) pixels, or
-//    (4+2) x (16+2) half-resolution pixels for the folded upsample -- and
-//    the 16-channel slice of all nine taps' weights. All nine taps then read
-//    the same patch at shifted offsets, so every input byte is fetched once
-//    per tile instead of once per tap;
+//    LDS the input patch the tile needs -- (16+2) x (32+2) pixels, or
+//    (8+2) x (16+2) half-resolution pixels for the folded upsample -- and
+//    the 16-channel slice of all nine taps' weights (one contiguous block
+//    of the [cin_p/16][9][cout_p][16] plane). All nine taps read the same
+//    patch at shifted offsets, so every input byte is fetched once per tile;
+//  * stages are double-buffered in LDS and filled by direct-to-LDS loads
+//    (global/buffer_load ... lds): the next stage streams in while the
+//    current one feeds 72 MFMAs per wave, with no register staging and one
+//    barrier per stage. Loads past the image return zero, which is the
+//    convolution's zero padding;
 //  * for each tap column dx a wave loads the fragments of the patch rows it
 //    needs once and uses them for the three tap rows dy (output row r at
 //    tap row dy reads patch row r + dy; for the upsample, (r + dy + 1) / 2);
-//  * LDS rows are 32 bytes (16 channels): consecutive lanes read
-//    consecutive 32-byte rows, which the gfx950 LDS serves without bank
-//    conflicts; the patch is zero outside the image (buffer loads past the
-//    resource return zero), which is the convolution's zero padding;
-//  * the next stage's global loads are issued before the current stage's
-//    72 MFMAs per wave and land in registers; two workgroups per CU
-//    (48 KB of LDS each) overlap one's LDS refill with the other's MFMAs;
+//    LDS rows are 32 bytes, which gfx950 serves without bank conflicts;
+//  * the f32 tile leaves through LDS: every tile row goes out as one
+//    contiguous run of 16-byte stores;
 //  * workgroups are dealt round robin to the 8 XCDs; the tile order is
 //    remapped so each XCD works on a contiguous band of rows (shared halos
 //    and weights stay in its L2).
@@ -41,11 +43,10 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
-template <int N>
-using uvec = unsigned __attribute__((ext_vector_type(N)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int NT = 256;  // threads per workgroup (4 waves)
-constexpr int TH = 8;    // output rows per tile
+constexpr int NT = 512;  // threads per workgroup (8 waves)
+constexpr int TH = 16;   // output rows per tile
 constexpr int TW = 32;   // output columns per tile
 constexpr int CK = 16;   // input channels per stage
 constexpr int FM = 4;    // output rows per wave
@@ -57,13 +58,10 @@ struct Geo {
     static constexpr int PH = (MODE == kConv3x3) ? TH + 2 : TH / 2 + 2;
     static constexpr int PW = (MODE == kConv3x3) ? TW + 2 : TW / 2 + 2;
     static constexpr int AROWS = (MODE == kConv3x3) ? FM + 2 : FM / 2 + 2;
-    // first patch row of wave row-group wm
+    // first patch row of wave row group wm
     __device__ static constexpr int row0(int wm) { return (MODE == kConv3x3) ? FM * wm : (FM / 2) * wm; }
-    // patch row (relative to row0) read by wave output row i at tap row dy
-    __device__ static constexpr int arow(int i, int dy)
-    {
-        return (MODE == kConv3x3) ? i + dy : ((FM * 0 + i + dy + 1) >> 1);
-    }
+    // patch row (relative to row0) read by the wave's output row i at tap row dy
+    __device__ static constexpr int arow(int i, int dy) { return (MODE == kConv3x3) ? i + dy : (i + dy + 1) >> 1; }
     // patch column read by tile column x at tap column dx
     __device__ static int pcol(int x, int dx) { return (MODE == kConv3x3) ? x + dx : ((x + dx + 1) >> 1); }
 };
@@ -73,35 +71,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 template <int MODE, int BN>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_conv_halo(IgemmArgs p)
+__global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
 {
     using G = Geo<MODE>;
     constexpr int PH = G::PH, PW = G::PW, AROWS = G::AROWS;
-    constexpr int A_UNITS = PH * PW * 2;  // 16-byte units (pixel, channel half) per stage
-    constexpr int B_UNITS = 9 * BN * 2;   // (tap, n, channel half)
-    constexpr int A_PER = (A_UNITS + NT - 1) / NT;
-    constexpr int B_PER = (B_UNITS + NT - 1) / NT;
-    constexpr int FN = BN / 64;  // 32-channel fragments per wave
-    static_assert(A_PER <= 4, "patch units per thread");
-    // the output tile leaves through LDS, two tile rows at a time
-    constexpr int OUT_ROWS = 2;
-    constexpr int OUT_BYTES = OUT_ROWS * TW * BN * 4;
-    constexpr int STAGE_BYTES = (A_UNITS + B_UNITS) * 16;
-    static_assert(OUT_BYTES <= STAGE_BYTES, "output staging fits the stage buffer");
+    constexpr int A_UNITS = PH * PW * 2;                 // 16-byte units (pixel, channel half)
+    constexpr int A_INSTR = (A_UNITS + 63) / 64;         // wave loads per stage for the patch
+    constexpr int A_PAD = A_INSTR * 64;                  // patch region, padded to whole loads
+    constexpr int B_UNITS = 9 * BN * 2;                  // (tap, n, channel half)
+    constexpr int B_INSTR = B_UNITS / 64;
+    constexpr int T_INSTR = A_INSTR + B_INSTR;
+    constexpr int PER_WAVE = (T_INSTR + 7) / 8;
+    constexpr int A_PER_WAVE = (A_INSTR + 7) / 8;        // patch loads of the busiest wave
+    constexpr int STAGE = A_PAD + B_UNITS;               // units per stage buffer
+    constexpr int FN = BN / 64;                          // 32-channel fragments per wave
+    static_assert(B_UNITS % 64 == 0, "whole weight loads");
+    static_assert(A_PER_WAVE <= 4, "patch offsets per lane");
+    // the output tile leaves through LDS, 4 tile rows per pass
+    static_assert(4 * TW * BN * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
 
-    __shared__ __attribute__((aligned(16))) u32x4 lds[A_UNITS + B_UNITS];
-    u32x4 *sA = lds;            // [PH * PW][2]
-    u32x4 *sB = lds + A_UNITS;  // [9][BN][2]
+    __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int wm = wave >> 1, wn = wave & 1;
     const int fx = lane & 31;  // tile column (A) / channel within a fragment (B)
     const int fh = lane >> 5;  // channel half of the stage: 8*fh .. 8*fh+7
@@ -125,61 +119,37 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const __amdgpu_buffer_rsrc_t a_src = make_rsrc(p.a, (uint32_t)H * W * cin_p * 2);
     // stage st of the blocked plane [cin_p/16][9][cout_p][16]
     const int64_t b_stage = (int64_t)9 * cout_p * CK;
-    const _Float16 *b_tile = p.b + (int64_t)n0 * CK;
+    const _Float16 *b_tile = p.b + (int64_t)n0 * CK + lane * 8;
 
-    // byte offset (stage 0) of each patch unit this thread loads; kOOB for
-    // pixels outside the image and for units past the patch
+    // this lane's patch source (stage 0 byte offset) for each patch load of
+    // its wave: load index ii = wave + 8k covers units ii*64 .. ii*64+63
     int4v aoff = {kOOB, kOOB, kOOB, kOOB};
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-        const int u = tid + NT * i;
+    for (int k = 0; k < A_PER_WAVE; ++k) {
+        const int u = (wave + 8 * k) * 64 + lane;
         const int pix = u >> 1, half = u & 1;
         const int pr = pix / PW, pc = pix - (pix / PW) * PW;
         const int sy = py0 + pr, sx = px0 + pc;
         const bool ok = (u < A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
-        aoff[i] = ok ? ((sy * W + sx) * cin_p + half * 8) * 2 : kOOB;
+        aoff[k] = ok ? ((sy * W + sx) * cin_p + half * 8) * 2 : kOOB;
     }
 
-    uvec<4 * A_PER> ra;
-    uvec<4 * B_PER> rb;
-    auto gload = [&](int st) __attribute__((always_inline)) {
-        const int cb = st * CK * 2;
+    // issue the direct-to-LDS loads of stage st into buffer buf
+    auto issue = [&](int st, int buf) __attribute__((always_inline)) {
+        u32x4 *base = lds + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int off = aoff[i] == kOOB ? kOOB : aoff[i] + cb;
-            const u32x4 v = buf_load16(a_src, off);
-            ra[4 * i + 0] = v.x;
-            ra[4 * i + 1] = v.y;
-            ra[4 * i + 2] = v.z;
-            ra[4 * i + 3] = v.w;
-        }
-        const _Float16 *bs = b_tile + st * b_stage;
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int u = tid + NT * i;
-            const int tap = u / (2 * BN);
-            const int rem = u - tap * (2 * BN);  // n * 2 + half: contiguous within a tap
-            u32x4 v = {0, 0, 0, 0};
-            if (B_UNITS % NT == 0 || u < B_UNITS)
-                v = *reinterpret_cast<const u32x4 *>(bs + (int64_t)tap * cout_p * CK + rem * 8);
-            rb[4 * i + 0] = v.x;
-            rb[4 * i + 1] = v.y;
-            rb[4 * i + 2] = v.z;
-            rb[4 * i + 3] = v.w;
-        }
-    };
-    auto lstore = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int u = tid + NT * i;
-            if (A_UNITS % NT == 0 || u < A_UNITS)
-                sA[u] = u32x4{ra[4 * i], ra[4 * i + 1], ra[4 * i + 2], ra[4 * i + 3]};
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int u = tid + NT * i;
-            if (B_UNITS % NT == 0 || u < B_UNITS)
-                sB[u] = u32x4{rb[4 * i], rb[4 * i + 1], rb[4 * i + 2], rb[4 * i + 3]};
+        for (int k = 0; k < PER_WAVE; ++k) {
+            const int ii = wave + 8 * k;
+            if (ii < A_INSTR) {
+                const int off = aoff[k] == kOOB ? kOOB : aoff[k] + st * CK * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(a_src, (lds_void *)(base + ii * 64), 16, off, 0, 0, 0);
+            } else if (ii < T_INSTR) {
+                const int jj = ii - A_INSTR;
+                const int tap = (jj * 64) / (2 * BN);
+                const int rem = jj * 64 - tap * (2 * BN);  // first (n, half) unit of this load
+                const _Float16 *src = b_tile + st * b_stage + (int64_t)tap * cout_p * CK + rem * 8;
+                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(base + A_PAD + jj * 64), 16, 0, 0);
+            }
         }
     };
 
@@ -194,14 +164,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int ar0 = G::row0(wm);
     const int nst = cin_p / CK;
 
-    gload(0);
-    lstore();
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int st = 0; st < nst; ++st) {
-        const bool more = st + 1 < nst;
-        if (more) gload(st + 1);
-        __builtin_amdgcn_sched_barrier(0);
+        const int buf = st & 1;
+        if (st + 1 < nst) issue(st + 1, buf ^ 1);
+        const u32x4 *sA = lds + buf * STAGE;
+        const u32x4 *sB = sA + A_PAD;
 #pragma unroll
         for (int dx = 0; dx < 3; ++dx) {
             half8 af[AROWS];
@@ -224,20 +195,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
                                                                            acc[i][j], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();  // every wave is done reading this stage
-        if (more) {
-            lstore();
-            __syncthreads();
-        }
+        // the next stage has landed (own loads) and every wave is done with
+        // this one (barrier)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     }
 
     // epilogue through LDS: accumulator element (i, j, r) of lane l is tile
     // pixel (4 wm + i, 8 (r / 4) + 4 (l / 32) + r % 4), channel
-    // wn BN/2 + 32 j + l % 32. Pass q stages tile rows {q, q + 4} (wave row
-    // i = q of both wave row groups) as [2][TW][BN] f32, then every thread
-    // writes 16 contiguous bytes: each tile row leaves as one TW*BN*4-byte
-    // run (contiguous in y when BN equals the output row width).
+    // wn BN/2 + 32 j + l % 32. Pass q stages tile rows {q, 4 + q, 8 + q,
+    // 12 + q} (wave row i = q of the four wave row groups) as [4][TW][BN]
+    // f32; then every thread writes 16 contiguous bytes, so each tile row
+    // leaves as one run of TW * BN * 4 bytes (contiguous when BN is the
+    // output row width).
     const float osc = p.oscale;
     const bool accum = p.accumulate != 0;
     float *stg = reinterpret_cast<float *>(lds);
@@ -255,14 +225,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
                 stg[(wm * TW + px) * BN + wn * (BN / 2) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
             }
         __syncthreads();
-        constexpr int V4 = OUT_ROWS * TW * BN / 4;  // 16-byte pieces in the staging area
+        constexpr int V4 = 4 * TW * BN / 4;  // 16-byte pieces staged per pass
 #pragma unroll
         for (int v = tid; v < V4; v += NT) {
             const int e = v * 4;
-            const int rr = e / (TW * BN);  // 0: tile row q, 1: tile row q + 4
+            const int wr = e / (TW * BN);  // wave row group: tile row FM * wr + q
             const int px = (e / BN) % TW;
             const int ch = e % BN;
-            const int oy = y0 + rr * FM + q, ox = x0 + px;
+            const int oy = y0 + FM * wr + q, ox = x0 + px;
             if (oy < Hout && ox < Wout) {
                 float4 val = reinterpret_cast<const float4 *>(stg)[v];
                 float *dst = out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch;
@@ -305,3 +275,4 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
 }
 
 }  // namespace ig
+
