@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-ROOF_KERNEL = "k_conv_halo<1, 128>"  # the 3x3 conv instantiation for 512^2 x 128
+ROOF_KERNEL = "k_conv_halo<1, 128, 8>"  # the 3x3 conv instantiation for 512^2 x 128
 CONV_SRC = os.path.join(ROOT, "implicit_gemm_conv_nhwc_amd", "csrc", "conv_halo.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_512x512x128_traffic.json")
 
@@ -257,7 +257,7 @@ def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
 
     conv = [float(r["Counter_Value"]) for r in sorted(rows(conv_csv), key=lambda r: int(r["Start_Timestamp"]))
             if ROOF_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", "")
-            or "k_conv_halo" in r["Kernel_Name"] and "ILi1ELi128" in r["Kernel_Name"]][-roof_launches:]
+            or "k_conv_halo" in r["Kernel_Name"] and "ILi1ELi128ELi8" in r["Kernel_Name"]][-roof_launches:]
     cp = [float(r["Counter_Value"]) for r in rows(copy_csv) if "mul" in r["Kernel_Name"].lower()
           or "elementwise" in r["Kernel_Name"].lower()]
     scale = nbytes / (sum(cp) / len(cp))

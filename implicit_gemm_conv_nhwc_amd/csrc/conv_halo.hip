@@ -9,11 +9,12 @@
 // and `upsample2x`, for the definition (stride 1, zero padding 1).
 //
 // Design (not the pages' 128x64 cooperative-matrix tiling):
-//  * one workgroup of 8 wave64s per CU owns an output tile of 16 rows x 32
-//    columns x BN channels; the waves split it 4 (rows) x 2 (channels):
-//    each wave computes 4 output rows x 32 columns x BN/2 channels as
-//    4 x BN/64 tiles of v_mfma_f32_32x32x16_f16 (one output row is one
-//    32-row MFMA operand);
+//  * a workgroup owns an output tile of 16 rows x 32 columns x BN
+//    channels: 8 wave64s with BN = 128 (one workgroup per CU), or 4 with
+//    BN = 64 (two per CU) when the 128-channel tiles would not fill the
+//    chip. Each wave computes 4 output rows x 32 columns x 64 channels as
+//    4 x 2 tiles of v_mfma_f32_32x32x16_f16 (one output row is one 32-row
+//    MFMA operand);
 //  * the reduction runs in stages of 16 input channels. A stage brings into
 //    LDS the input patch the tile needs -- (16+2) x (32+2) pixels, or
 //    (8+2) x (16+2) half-resolution pixels for the folded upsample -- and
@@ -28,7 +29,11 @@
 //  * for each tap column dx a wave loads the fragments of the patch rows it
 //    needs once and uses them for the three tap rows dy (output row r at
 //    tap row dy reads patch row r + dy; for the upsample, (r + dy + 1) / 2);
-//    LDS rows are 32 bytes, which gfx950 serves without bank conflicts;
+//  * LDS holds a pixel's (or an output channel's) 16 channels as two
+//    16-byte halves, the halves swapped on every other group of 8
+//    columns: a fragment read (32 lanes on consecutive columns, the other
+//    32 on the other half) then touches 16 distinct bank groups in each
+//    pass, where the plain 32-byte pitch would conflict two ways;
 //  * the f32 tile leaves through LDS: every tile row goes out as one
 //    contiguous run of 16-byte stores;
 //  * workgroups are dealt round robin to the 8 XCDs; the tile order is
@@ -42,10 +47,9 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int NT = 512;  // threads per workgroup (8 waves)
 constexpr int TH = 16;   // output rows per tile
 constexpr int TW = 32;   // output columns per tile
 constexpr int CK = 16;   // input channels per stage
@@ -71,10 +75,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-template <int MODE, int BN>
-__global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
+template <int MODE, int BN, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
+void k_conv_halo(IgemmArgs p)
 {
     using G = Geo<MODE>;
+    constexpr int NT = 64 * NW;                          // threads per workgroup
+    constexpr int WN = NW / 4;                           // wave groups along the channels
     constexpr int PH = G::PH, PW = G::PW, AROWS = G::AROWS;
     constexpr int A_UNITS = PH * PW * 2;                 // 16-byte units (pixel, channel half)
     constexpr int A_INSTR = (A_UNITS + 63) / 64;         // wave loads per stage for the patch
@@ -82,12 +89,13 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
     constexpr int B_UNITS = 9 * BN * 2;                  // (tap, n, channel half)
     constexpr int B_INSTR = B_UNITS / 64;
     constexpr int T_INSTR = A_INSTR + B_INSTR;
-    constexpr int PER_WAVE = (T_INSTR + 7) / 8;
-    constexpr int A_PER_WAVE = (A_INSTR + 7) / 8;        // patch loads of the busiest wave
+    constexpr int PER_WAVE = (T_INSTR + NW - 1) / NW;
+    constexpr int A_PER_WAVE = (A_INSTR + NW - 1) / NW;  // patch loads of the busiest wave
     constexpr int STAGE = A_PAD + B_UNITS;               // units per stage buffer
-    constexpr int FN = BN / 64;                          // 32-channel fragments per wave
+    constexpr int FN = BN / (32 * WN);                   // 32-channel fragments per wave
     static_assert(B_UNITS % 64 == 0, "whole weight loads");
-    static_assert(A_PER_WAVE <= 4, "patch offsets per lane");
+    static_assert(A_PER_WAVE <= 8, "patch offsets per lane");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     // the output tile leaves through LDS, 4 tile rows per pass
     static_assert(4 * TW * BN * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
 
@@ -96,7 +104,7 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int fx = lane & 31;  // tile column (A) / channel within a fragment (B)
     const int fh = lane >> 5;  // channel half of the stage: 8*fh .. 8*fh+7
 
@@ -119,16 +127,18 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
     const __amdgpu_buffer_rsrc_t a_src = make_rsrc(p.a, (uint32_t)H * W * cin_p * 2);
     // stage st of the blocked plane [cin_p/16][9][cout_p][16]
     const int64_t b_stage = (int64_t)9 * cout_p * CK;
-    const _Float16 *b_tile = p.b + (int64_t)n0 * CK + lane * 8;
+    // weight unit (n, stored half) holds channel half stored ^ bit 3 of n
+    const _Float16 *b_tile = p.b + (int64_t)n0 * CK + (lane ^ ((lane >> 4) & 1)) * 8;
 
     // this lane's patch source (stage 0 byte offset) for each patch load of
-    // its wave: load index ii = wave + 8k covers units ii*64 .. ii*64+63
-    int4v aoff = {kOOB, kOOB, kOOB, kOOB};
+    // its wave: load index ii = wave + NW k covers units ii*64 .. ii*64+63
+    int8v aoff = {kOOB, kOOB, kOOB, kOOB, kOOB, kOOB, kOOB, kOOB};
 #pragma unroll
     for (int k = 0; k < A_PER_WAVE; ++k) {
-        const int u = (wave + 8 * k) * 64 + lane;
-        const int pix = u >> 1, half = u & 1;
+        const int u = (wave + NW * k) * 64 + lane;
+        const int pix = u >> 1;
         const int pr = pix / PW, pc = pix - (pix / PW) * PW;
+        const int half = (u & 1) ^ ((pc >> 3) & 1);  // stored half -> channel half
         const int sy = py0 + pr, sx = px0 + pc;
         const bool ok = (u < A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
         aoff[k] = ok ? ((sy * W + sx) * cin_p + half * 8) * 2 : kOOB;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
         u32x4 *base = lds + buf * STAGE;
 #pragma unroll
         for (int k = 0; k < PER_WAVE; ++k) {
-            const int ii = wave + 8 * k;
+            const int ii = wave + NW * k;
             if (ii < A_INSTR) {
                 const int off = aoff[k] == kOOB ? kOOB : aoff[k] + st * CK * 2;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(a_src, (lds_void *)(base + ii * 64), 16, off, 0, 0, 0);
@@ -163,6 +173,7 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
 
     const int ar0 = G::row0(wm);
     const int nst = cin_p / CK;
+    const int wh = fh ^ ((fx >> 3) & 1);  // stored half of this lane's weight fragment
 
     issue(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -177,16 +188,17 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
         for (int dx = 0; dx < 3; ++dx) {
             half8 af[AROWS];
             const int pc = G::pcol(fx, dx);
+            const int ph = fh ^ ((pc >> 3) & 1);
 #pragma unroll
             for (int a = 0; a < AROWS; ++a)
-                af[a] = __builtin_bit_cast(half8, sA[((ar0 + a) * PW + pc) * 2 + fh]);
+                af[a] = __builtin_bit_cast(half8, sA[((ar0 + a) * PW + pc) * 2 + ph]);
 #pragma unroll
             for (int dy = 0; dy < 3; ++dy) {
                 const int tap = dy * 3 + dx;
                 half8 bf[FN];
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bf[j] = __builtin_bit_cast(half8, sB[(tap * BN + wn * (BN / 2) + j * 32 + fx) * 2 + fh]);
+                    bf[j] = __builtin_bit_cast(half8, sB[(tap * BN + wn * (BN / WN) + j * 32 + fx) * 2 + wh]);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
     float *stg = reinterpret_cast<float *>(lds);
     float bv[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bv[j] = p.bias ? p.bias[n0 + wn * (BN / 2) + j * 32 + fx] : 0.f;
+    for (int j = 0; j < FN; ++j) bv[j] = p.bias ? p.bias[n0 + wn * (BN / WN) + j * 32 + fx] : 0.f;
     float *out = reinterpret_cast<float *>(p.c);
 #pragma unroll
     for (int q = 0; q < FM; ++q) {
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int px = (r >> 2) * 8 + fh * 4 + (r & 3);
-                stg[(wm * TW + px) * BN + wn * (BN / 2) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
+                stg[(wm * TW + px) * BN + wn * (BN / WN) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
             }
         __syncthreads();
         constexpr int V4 = 4 * TW * BN / 4;  // 16-byte pieces staged per pass
@@ -250,13 +262,13 @@ __global__ __launch_bounds__(NT) void k_conv_halo(IgemmArgs p)
     }
 }
 
-template <int MODE, int BN>
+template <int MODE, int BN, int NW>
 void launch_t(const IgemmArgs &a, hipStream_t s)
 {
     const int Hout = (MODE == kConv3x3Up2) ? 2 * a.H : a.H;
     const int Wout = (MODE == kConv3x3Up2) ? 2 * a.W : a.W;
     const int grid = ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW) * (a.N / BN);
-    hipLaunchKernelGGL((k_conv_halo<MODE, BN>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 
 }  // namespace
@@ -264,15 +276,20 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return;
-    const bool bn128 = (a.N % 128) == 0;
+    // 8 waves on 16x32x128 tiles (one workgroup per CU) when there are
+    // enough of them to fill the chip; otherwise 4 waves on 16x32x64 tiles
+    // (two workgroups per CU, twice the tiles)
+    const int Hout = (mode == kConv3x3Up2) ? 2 * a.H : a.H;
+    const int Wout = (mode == kConv3x3Up2) ? 2 * a.W : a.W;
+    const int64_t pix_tiles = (int64_t)((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW);
+    const bool bn128 = (a.N % 128) == 0 && pix_tiles * (a.N / 128) >= 256;
     if (mode == kConv3x3) {
-        if (bn128) launch_t<kConv3x3, 128>(a, s);
-        else launch_t<kConv3x3, 64>(a, s);
+        if (bn128) launch_t<kConv3x3, 128, 8>(a, s);
+        else launch_t<kConv3x3, 64, 4>(a, s);
     } else {
-        if (bn128) launch_t<kConv3x3Up2, 128>(a, s);
-        else launch_t<kConv3x3Up2, 64>(a, s);
+        if (bn128) launch_t<kConv3x3Up2, 128, 8>(a, s);
+        else launch_t<kConv3x3Up2, 64, 4>(a, s);
     }
 }
 
 }  // namespace ig
-

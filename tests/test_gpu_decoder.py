@@ -3,6 +3,9 @@ and latents: u8 PSNR >= 60 dB over the whole frame, plus the guard's effect
 on a stream past the f16 range, query-chunk invariance and the workspace
 contract."""
 
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +18,7 @@ from gpu_util import dev, host, nan_f32
 pytestmark = pytest.mark.gpu
 
 PSNR_MIN = 60.0
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def _run(dd, z, guard_log2=8, q_chunk=0):
@@ -97,3 +101,47 @@ def test_workspace_too_small_leaves_output_untouched(full_decoder):
         ig.decoder_forward(dd.desc, z, 32, 32, 8, 0, ws, need // 2, out)
     assert e.value.code == -3
     assert torch.isnan(out).all()
+
+
+def _load_golden(size):
+    sys.path.insert(0, GOLDEN)
+    import make_decode_golden as mg
+
+    path = mg.golden_path(size)
+    if not os.path.exists(path):
+        pytest.skip("no stored oracle rows for %d^2 (tests/golden/make_decode_golden.py)" % size)
+    with np.load(path) as g:
+        return mg, {k: g[k] for k in g.files}
+
+
+@pytest.mark.parametrize("size", [1024, 2048])
+def test_full_size_decode_against_stored_oracle_rows(size):
+    """The full-size decode, launched as the benchmark launches it (default
+    query chunk, guard 8, latent N(0,1)*8, conv_in gain 2^11), against the
+    oracle's stored rows: u8 PSNR >= 60 dB over every sampled row, plus the
+    float rows' max |d| relative to their RMS (reported)."""
+    mg, g = _load_golden(size)
+    w, z = mg.inputs(size)
+    assert float(np.max(g["guard_max"])) > 65504.0  # the guard is exercised
+    dd = ig.DeviceDecoder(w)
+    h0 = size // 8
+    out = dd.forward(dev(z), h0, h0, guard_log2=mg.GUARD_LOG2, q_chunk=0)
+    rows = torch.from_numpy(g["rows"].astype(np.int64)).cuda()
+    frows = torch.from_numpy(g["frows"].astype(np.int64)).cuda()
+    got_rows = host(out.index_select(1, rows))
+    got_f = host(out.index_select(1, frows))
+    assert bool(torch.isfinite(out).all())
+    del out, dd
+    torch.cuda.empty_cache()
+    d = O.to_u8(got_rows) - g["u8"].astype(np.float64)
+    mse = float(np.mean(d * d))
+    p = float("inf") if mse == 0 else 10.0 * np.log10(255.0 ** 2 / mse)
+    ref_f = g["f32"].astype(np.float64)
+    unclipped = np.abs(ref_f) <= 1.0
+    p_unclipped = O.psnr_u8(got_f[unclipped], ref_f[unclipped])
+    rel = float(np.max(np.abs(got_f - ref_f)) / np.sqrt(np.mean(ref_f ** 2)))
+    print("%d^2: sampled-row PSNR %.2f dB (unclipped float rows %.2f dB), max|d|/RMS %.3e, "
+          "u8 levels off: %d of %d" % (size, p, p_unclipped, rel, int(np.count_nonzero(d)), d.size),
+          flush=True)
+    assert p >= PSNR_MIN
+    assert p_unclipped >= PSNR_MIN

@@ -5,7 +5,11 @@ the composition's plumbing and the guard's behaviour (page "cortiq-engine
 0.8.3, src/gpu_wgpu/qi21_vae.rs", `guard`: unguarded f16 casts of a stream
 past the f16 range turned most of an image into NaN)."""
 
+import os
+import sys
+
 import numpy as np
+import pytest
 
 import oracle as O
 import synth
@@ -48,3 +52,29 @@ def test_guard_does_not_change_an_in_range_stream():
     # g = 8 except values below 2^-6, whose rounding differs slightly
     y0 = O.decode(w, z, guard_log2=0)
     assert O.psnr_u8(y0, y8) > 60.0
+
+
+@pytest.mark.parametrize("size", [1024, 2048])
+def test_stored_decode_rows_match_the_seeded_inputs(size):
+    """The stored oracle rows of the full-size decode belong to the inputs the
+    seeded generator draws today (a change to the generator would make them
+    stale)."""
+    import hashlib
+    import json
+
+    gdir = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    meta_path = os.path.join(gdir, "decode_%d_rows.json" % size)
+    if not os.path.exists(meta_path):
+        pytest.skip("no stored rows for %d^2" % size)
+    sys.path.insert(0, gdir)
+    import make_decode_golden as mg
+
+    meta = json.load(open(meta_path))
+    w, z = mg.inputs(size)
+    assert meta["latent_digest"] == hashlib.sha256(z.tobytes()).hexdigest()[:16]
+    assert meta["weights_digest"] == mg.weights_digest(w)
+    assert max(meta["guard_max"]) > 65504.0
+    with np.load(mg.golden_path(size)) as g:
+        assert g["u8"].shape == (3, size // mg.STRIDE[size], size)
+        assert g["f32"].shape == (3, size // (8 * mg.STRIDE[size]), size)
+        assert np.array_equal(O.to_u8(g["f32"]), g["u8"][:, ::8, :].astype(np.float64))
