@@ -24,8 +24,10 @@
 //  * stages are double-buffered in LDS and filled by direct-to-LDS loads
 //    (global/buffer_load ... lds): the next stage streams in while the
 //    current one feeds 72 MFMAs per wave, with no register staging and one
-//    barrier per stage. Loads past the image return zero, which is the
-//    convolution's zero padding;
+//    barrier per stage. A wave issues its share of the next stage's loads a
+//    few at a time between its MFMA groups (patch loads first), so no wave
+//    waits on a burst of load issues before its first MFMA. Loads past the
+//    image return zero, which is the convolution's zero padding;
 //  * for each tap column dx a wave loads the fragments of the patch rows it
 //    needs once and uses them for the three tap rows dy (output row r at
 //    tap row dy reads patch row r + dy; for the upsample, (r + dy + 1) / 2);
@@ -145,10 +147,11 @@ void k_conv_halo(IgemmArgs p)
     }
 
     // issue the direct-to-LDS loads of stage st into buffer buf
-    auto issue = [&](int st, int buf) __attribute__((always_inline)) {
+    // loads k in [k0, k1) of this wave (patch loads come first)
+    auto issue = [&](int st, int buf, int k0, int k1) __attribute__((always_inline)) {
         u32x4 *base = lds + buf * STAGE;
 #pragma unroll
-        for (int k = 0; k < PER_WAVE; ++k) {
+        for (int k = k0; k < k1; ++k) {
             const int ii = wave + NW * k;
             if (ii < A_INSTR) {
                 const int off = aoff[k] == kOOB ? kOOB : aoff[k] + st * CK * 2;
@@ -175,13 +178,12 @@ void k_conv_halo(IgemmArgs p)
     const int nst = cin_p / CK;
     const int wh = fh ^ ((fx >> 3) & 1);  // stored half of this lane's weight fragment
 
-    issue(0, 0);
+    issue(0, 0, 0, PER_WAVE);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int st = 0; st < nst; ++st) {
         const int buf = st & 1;
-        if (st + 1 < nst) issue(st + 1, buf ^ 1);
         const u32x4 *sA = lds + buf * STAGE;
         const u32x4 *sB = sA + A_PAD;
 #pragma unroll
@@ -195,6 +197,10 @@ void k_conv_halo(IgemmArgs p)
 #pragma unroll
             for (int dy = 0; dy < 3; ++dy) {
                 const int tap = dy * 3 + dx;
+                // the next stage's loads, spread over the nine tap groups so
+                // the waves go straight to their MFMAs after the barrier
+                const int g = dx * 3 + dy;  // group order
+                if (st + 1 < nst) issue(st + 1, buf ^ 1, (g * PER_WAVE + 8) / 9, ((g + 1) * PER_WAVE + 8) / 9);
                 half8 bf[FN];
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
