@@ -14,7 +14,11 @@
 //    x = 2^g*acc + b_sc before that add -- two f32 stream passes fewer per
 //    resnet unit;
 //  * q and k leave their GEMMs as f16 with the bias added (the pages' conv
-//    then cast(+bias)), and the attention output projection adds into x.
+//    then cast(+bias)), and the attention output projection adds into x;
+//  * the chunk's f32 score matrix is never stored: a first GEMM pass keeps
+//    only per-row softmax statistics, a second recomputes the same scores
+//    and writes P directly (the same P, without 6 bytes per score of HBM
+//    traffic).
 #include <cmath>
 
 #include "ig_internal.h"
@@ -119,6 +123,8 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     pl.qc = q_chunk > 0 ? q_chunk : 16384;
     if (pl.qc > pl.m) pl.qc = pl.m;
     upd(pl.max_xn, (int64_t)pl.mp * c);
+    if ((uint64_t)pl.qc * pl.mp * 2 >= (3ULL << 30))
+        return fail(IG_EUNSUPPORTED, "query chunk %d x %d keys: probabilities exceed 3 GiB; pass a smaller q_chunk", pl.qc, pl.mp);
     if ((e = plan_resnet(d->mid[1], "mid.1", c, cp, M, pl))) return e;
     for (int s = 0; s < d->n_up; ++s) {
         const ig_up_w &u = d->ups[s];
@@ -167,7 +173,9 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     pl.off_k = take(mp * C * 2);
     pl.off_vt = take(C * mp * 2);
     pl.off_o = take(mp * C * 4);
-    pl.off_s = take(qc * mp * 4);
+    // per-row partial softmax statistics of a query chunk, then the rows'
+    // final (max, 1 / sum)
+    pl.off_s = take((qc * gemm2_stat_parts((int)mp) * 2 + qc * 2) * 4);
     pl.off_p = take(qc * mp * 2);
     pl.total = o;
     return IG_OK;
@@ -253,10 +261,29 @@ struct Run {
         // V^T [C][mp] = Wv . xn^T; V's bias comes after P.V (P's rows sum to 1)
         gemm(wv, C, C, C, xn, mp, C, nullptr, 1.f, vt16, mp, 1, 0);
         const float scale = 1.0f / sqrtf((float)C);
+        // per chunk: the scores' row statistics, then P, never storing the
+        // scores themselves; then O = P.V
+        const int nparts = gemm2_stat_parts(mp);
+        float *rowstat = S + (int64_t)qc * nparts * 2;
         for (int q0 = 0; q0 < m; q0 += qc) {
             const int rows = (m - q0) < qc ? (m - q0) : qc;
-            gemm(q16 + (int64_t)q0 * C, rows, C, C, k16, mp, C, nullptr, scale, S, mp, 0, 0);
-            launch_softmax(S, rows, mp, m, mp, P, mp, s);
+            Gemm2Args g{};
+            g.a = q16 + (int64_t)q0 * C;
+            g.b = k16;
+            g.M = rows;
+            g.N = mp;
+            g.K = C;
+            g.lda = C;
+            g.ldb = C;
+            g.valid = m;
+            g.oscale = scale;
+            g.stats = S;
+            launch_gemm2(kEpiStats, g, s);
+            launch_rowstat(S, nparts, rows, rowstat, s);
+            g.c = P;
+            g.ldc = mp;
+            g.rowstat = rowstat;
+            launch_gemm2(kEpiProb, g, s);
             gemm(P, rows, mp, mp, vt16, C, mp, nullptr, 1.f, o32 + (int64_t)q0 * C, C, 0, 0);
         }
         launch_guard_cast(o32, m, C, a.v.b, 0, xn, s);

@@ -45,6 +45,34 @@ void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s);
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------------
+// plain NT GEMM C = oscale * A.B^T with the attention's softmax epilogues
+// ---------------------------------------------------------------------
+enum GemmEpi { kEpiF32 = 0, kEpiF16 = 1, kEpiStats = 2, kEpiProb = 3 };
+
+struct Gemm2Args {
+    const _Float16 *a;     // A [M][lda]
+    const _Float16 *b;     // B [N][ldb]
+    void *c;               // C [M][ldc]: f32 (kEpiF32), f16 (kEpiF16, kEpiProb)
+    const float *bias;     // [N] or null (kEpiF32, kEpiF16)
+    float *stats;          // kEpiStats: [M][gemm2_stat_parts(N)] (max, sum) pairs
+    const float *rowstat;  // kEpiProb: [M] (max, 1 / sum) pairs
+    int M, N, K;
+    int lda, ldb, ldc;
+    int valid;             // kEpiStats, kEpiProb: columns >= valid are masked
+    int accumulate;        // kEpiF32: C += result
+    float oscale;
+};
+
+// true when the shapes, strides and alignment fit k_gemm2 (K % 64 == 0,
+// N % 64 == 0, 16-byte rows and pointers, operands below 3.75 GiB)
+bool gemm2_supported(const Gemm2Args &a);
+void launch_gemm2(int epi, const Gemm2Args &a, hipStream_t s);
+// partial statistics per row that kEpiStats writes for N columns
+int gemm2_stat_parts(int N);
+// rowstat[r] = (max, 1 / sum) from the partial statistics of row r
+void launch_rowstat(const float *stats, int nparts, int rows, float *rowstat, hipStream_t s);
+
+// ---------------------------------------------------------------------
 // memory-bound kernels
 // ---------------------------------------------------------------------
 void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias,

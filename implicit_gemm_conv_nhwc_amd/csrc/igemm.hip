@@ -267,10 +267,30 @@ void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return;
     switch (mode) {
-    case kGemm:
-        if (a.out_f16) launch_mode<kGemm, true>(a, s);
-        else launch_mode<kGemm, false>(a, s);
+    case kGemm: {
+        // the direct-to-LDS GEMM when the shapes allow it
+        Gemm2Args g{};
+        g.a = a.a;
+        g.b = a.b;
+        g.c = a.c;
+        g.bias = a.bias;
+        g.M = a.M;
+        g.N = a.N;
+        g.K = a.K;
+        g.lda = a.lda;
+        g.ldb = a.ldb;
+        g.ldc = a.ldc;
+        g.accumulate = a.accumulate;
+        g.oscale = a.oscale;
+        if (gemm2_supported(g) && !(a.out_f16 && a.accumulate)) {
+            launch_gemm2(a.out_f16 ? kEpiF16 : kEpiF32, g, s);
+        } else if (a.out_f16) {
+            launch_mode<kGemm, true>(a, s);
+        } else {
+            launch_mode<kGemm, false>(a, s);
+        }
         break;
+    }
     case kConv3x3:
     case kConv3x3Up2: launch_conv_halo(mode, a, s); break;
     default: break;
