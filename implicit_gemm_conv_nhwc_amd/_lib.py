@@ -68,6 +68,7 @@ _smax = _sig("ig_softmax_rows_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _
 _lat = _sig("ig_latent_to_nhwc_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp])
 _out = _sig("ig_nhwc_to_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
 _zero = _sig("ig_zero_rows_f16", [_vp, _c_int, _c_int, _c_int, _vp])
+_conv_out = _sig("ig_conv3x3_out_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp])
 _dupup = _sig("ig_dupup_add", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _vp])
 
@@ -161,6 +162,11 @@ def latent_to_nhwc_f16(z, zc, M, cp, y, stream=None):
 
 def nhwc_to_nchw(y, M, ld, nch, bias, out, stream=None):
     return _check(_out(_ptr(y), M, ld, nch, _ptr(bias), _ptr(out), _stream(stream)))
+
+
+def conv3x3_out_nchw(x, H, W, cin_p, w, cout, cout_p, bias, out, stream=None):
+    return _check(_conv_out(_ptr(x), H, W, cin_p, _ptr(w), cout, cout_p, _ptr(bias), _ptr(out),
+                            _stream(stream)))
 
 
 def zero_rows_f16(y, r0, r1, ld, stream=None):

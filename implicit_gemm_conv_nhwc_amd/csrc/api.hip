@@ -280,6 +280,25 @@ int ig_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, f
     return check_launch("output launch");
 }
 
+int ig_conv3x3_out_nchw(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout, int cout_p,
+                        const float *bias, float *out, void *stream)
+{
+    clear_error();
+    if (H < 0 || W < 0) return fail(IG_EINVAL, "bad image %dx%d", H, W);
+    if (cin_p <= 0 || cin_p % 64 || cout <= 0 || cout_p < cout || cout_p % 64)
+        return fail(IG_EINVAL, "bad channel counts cin_p=%d cout=%d cout_p=%d", cin_p, cout, cout_p);
+    if (cout > 16) return fail(IG_EUNSUPPORTED, "output conv takes at most 16 channels, got %d", cout);
+    if ((int64_t)H * W * cin_p * 2 >= (3LL << 30)) return fail(IG_EUNSUPPORTED, "input too large");
+    if ((int64_t)H * W == 0) return IG_OK;
+    int r;
+    if ((r = check_ptr(x, "x", true)) || (r = check_ptr(w, "w", true)) || (r = check_ptr(out, "out", false)))
+        return r;
+    (void)hipGetLastError();
+    launch_conv_out(reinterpret_cast<const _Float16 *>(x), H, W, cin_p, reinterpret_cast<const _Float16 *>(w),
+                    cout, cout_p, bias, out, reinterpret_cast<hipStream_t>(stream));
+    return check_launch("output conv launch");
+}
+
 int ig_zero_rows_f16(uint16_t *y, int r0, int r1, int ld, void *stream)
 {
     clear_error();

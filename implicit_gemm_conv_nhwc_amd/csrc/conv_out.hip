@@ -1,0 +1,155 @@
+// The decoder's last 3x3 convolution, whose output has only a few real
+// channels (RGB), written straight into the NCHW frame with the bias:
+// out[o][p] = b[o] + sum_{tap, c} W[o][tap][c] x[src(p, tap)][c], o < cout.
+//
+// Page "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs", `output_rows`
+// (conv_out on the normalised stream, then OUT_SRC: NHWC rows + bias into
+// the NCHW frame); page "cortiq-engine 0.7.6, src/vae.rs", `Conv2d::apply`
+// (stride 1, zero padding 1).
+//
+// Padding the output channels to the convolution kernels' 64 would make
+// this the decoder's most expensive conv (21x the useful MFMA work, plus an
+// f32 [M][64] intermediate and a transpose pass). Here the output channels
+// are the 16 rows of a v_mfma_f32_16x16x32_f16 (weights as the A operand,
+// channels >= cout zero) and 16 pixels its columns, so lanes 0..15 hold the
+// real channels of 16 consecutive pixels and store them as 64-byte runs of
+// NCHW rows. The convolution is then bound by reading its f16 input once.
+//  * a workgroup of 4 waves owns 8 rows x 32 columns of output pixels; each
+//    wave 2 rows, i.e. 4 groups of 16 pixels; three workgroups share a CU,
+//    so enough loads are in flight to cover HBM latency;
+//  * the reduction runs in stages of 32 input channels: the (8+2) x (32+2)
+//    patch of the stage's channels streams into double-buffered LDS by
+//    direct-to-LDS loads (zero outside the image); the stage's weights (9
+//    taps, the lane's output channel, 8 of the 32 channels) are read from
+//    the blocked weight plane into registers;
+//  * a patch pixel's 32 channels are 4 units of 16 bytes, unit u stored at
+//    u ^ ((pixel >> 2) & 3), so the 16 lanes reading one unit of 16
+//    consecutive pixels touch 16 distinct bank groups.
+#include "ig_internal.h"
+
+namespace ig {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int NT = 256;                     // 4 waves
+constexpr int OH = 8, OW = 32;              // output tile
+constexpr int PH = OH + 2, PW = OW + 2;     // input patch
+constexpr int CS = 32;                      // input channels per stage
+constexpr int UPP = CS * 2 / 16;            // 16-byte units per patch pixel
+constexpr int A_UNITS = PH * PW * UPP;
+constexpr int A_INSTR = (A_UNITS + 63) / 64;
+constexpr int STAGE = A_INSTR * 64;         // units per stage buffer
+constexpr int PER_WAVE = (A_INSTR + 3) / 4;
+constexpr unsigned kOOB = 0xfffff000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+__global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x, int H, int W, int cin_p,
+                                                 const _Float16 *__restrict__ plane, int cout, int cout_p,
+                                                 const float *__restrict__ bias, float *__restrict__ out)
+{
+    __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;  // pixel column in a group; K quarter / output row block
+
+    const int tiles_x = (W + OW - 1) / OW;
+    const int y0 = (blockIdx.x / tiles_x) * OH, x0 = (blockIdx.x % tiles_x) * OW;
+    const __amdgpu_buffer_rsrc_t src = make_rsrc(x, (uint32_t)H * W * cin_p * 2);
+
+    // this lane's source offset (stage 0) for each of its wave's patch loads
+    unsigned aoff[PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+        const int u = (wave + 4 * k) * 64 + lane;
+        const int pix = u / UPP, su = u % UPP;
+        const int cu = su ^ ((pix >> 2) & 3);  // stored unit -> channel unit
+        const int pr = pix / PW, pc = pix % PW;
+        const int sy = y0 - 1 + pr, sx = x0 - 1 + pc;
+        const bool ok = (u < A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
+        aoff[k] = ok ? ((unsigned)(sy * W + sx) * (unsigned)cin_p + 8u * cu) * 2u : kOOB;
+    }
+    auto issue = [&](int st, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < PER_WAVE; ++k) {
+            const int ii = wave + 4 * k;
+            if (ii < A_INSTR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)(lds + buf * STAGE + ii * 64), 16,
+                                                         (int)aoff[k], st * CS * 2, 0, 0);
+        }
+    };
+
+    constexpr int NG = 2 * OW / 16;  // groups of 16 pixels per wave
+    f32x4 acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // A operand: output channel o = lane % 16, channels 8 * (lane / 16) ..
+    // + 7 of the stage; zero for o >= cout
+    const int o = col;
+    const int nst = cin_p / CS;
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nst) issue(st + 1, buf ^ 1);
+        half8 wt[9];
+        // blocked plane [cin_p/16][9][cout_p][16]: channel 32 st + 8 grp + e
+        const int c16 = 2 * st + (grp >> 1), ci = 8 * (grp & 1);
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            if (o < cout)
+                wt[t] = *reinterpret_cast<const half8 *>(plane + ((int64_t)(c16 * 9 + t) * cout_p + o) * 16 + ci);
+            else
+                wt[t] = half8{};
+        }
+        const u32x4 *sA = lds + buf * STAGE;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            const int dy = t / 3, dx = t % 3;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                // group g of this wave: output row 2 wave + g / (OW / 16), columns 16 (g % (OW / 16)) ..
+                const int pr = 2 * wave + g / (OW / 16) + dy, pc = 16 * (g % (OW / 16)) + col + dx;
+                const int pix = pr * PW + pc;
+                const half8 xf = __builtin_bit_cast(half8, sA[pix * UPP + (grp ^ ((pix >> 2) & 3))]);
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wt[t], xf, acc[g], 0, 0, 0);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    // lane (grp, col) holds output channels 4 grp + r of pixel column col
+    const int64_t HW = (int64_t)H * W;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int oy = y0 + 2 * wave + g / (OW / 16), ox = x0 + 16 * (g % (OW / 16)) + col;
+        if (oy >= H || ox >= W) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ch = 4 * grp + r;
+            if (ch < cout) out[ch * HW + (int64_t)oy * W + ox] = acc[g][r] + (bias ? bias[ch] : 0.f);
+        }
+    }
+}
+
+}  // namespace
+
+void launch_conv_out(const _Float16 *x, int H, int W, int cin_p, const _Float16 *plane, int cout, int cout_p,
+                     const float *bias, float *out, hipStream_t s)
+{
+    if (H <= 0 || W <= 0) return;
+    const int grid = ((H + OH - 1) / OH) * ((W + OW - 1) / OW);
+    hipLaunchKernelGGL(k_conv_out, dim3(grid), dim3(NT), 0, s, x, H, W, cin_p, plane, cout, cout_p, bias, out);
+}
+
+}  // namespace ig

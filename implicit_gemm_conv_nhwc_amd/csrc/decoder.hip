@@ -154,7 +154,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     if ((e = check_conv_w(d->conv_out, "conv_out", 3))) return e;
     if (d->conv_out.cin != c || d->conv_out.cin_p != cp) return fail(IG_EINVAL, "conv_out input %d, stream %d", d->conv_out.cin, c);
     upd(pl.max_xn, M * cp);
-    upd(pl.max_h, M * d->conv_out.cout_p);
+    if (d->conv_out.cout > 16) upd(pl.max_h, M * d->conv_out.cout_p);  // else straight to the frame
     pl.H = H;
     pl.W = W;
     // layout
@@ -353,8 +353,14 @@ int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, 
         }
     }
     launch_rmsnorm(r.x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, r.xn, s);
-    r.conv(kConv3x3, r.xn, H, W, d.conv_out, d.conv_out.b, 1.f, 0, r.h);
-    launch_nhwc_to_nchw(r.h, H * W, d.conv_out.cout_p, d.conv_out.cout, nullptr, out, s);
+    if (d.conv_out.cout <= 16) {
+        // few output channels: straight into the NCHW frame
+        launch_conv_out(r.xn, H, W, d.conv_out.cin_p, reinterpret_cast<const _Float16 *>(d.conv_out.w),
+                        d.conv_out.cout, d.conv_out.cout_p, d.conv_out.b, out, s);
+    } else {
+        r.conv(kConv3x3, r.xn, H, W, d.conv_out, d.conv_out.b, 1.f, 0, r.h);
+        launch_nhwc_to_nchw(r.h, H * W, d.conv_out.cout_p, d.conv_out.cout, nullptr, out, s);
+    }
     return check_launch("decoder_forward");
 }
 

@@ -88,6 +88,8 @@ void launch_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bi
                          hipStream_t s);
 void launch_pack_weights(const _Float16 *w, int cout, int cin, int k, int cout_p, int cin_p,
                          _Float16 *plane, hipStream_t s);
+void launch_conv_out(const _Float16 *x, int H, int W, int cin_p, const _Float16 *plane, int cout, int cout_p,
+                     const float *bias, float *out, hipStream_t s);
 void launch_zero_rows_f16(_Float16 *y, int r0, int r1, int ld, hipStream_t s);
 void launch_dupup(const float *src, int H, int W, int cin_p, float *x, int cout, int cout_p,
                   int factor, int repeats, int ft, hipStream_t s);

@@ -179,6 +179,18 @@ int ig_latent_to_nhwc_f16(const float *z, int zc, int M, int cp, uint16_t *y, vo
 int ig_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, float *out,
                     void *stream);
 
+/* The decoder's output convolution ([QI] `output_rows` and OUT_SRC; [VAE]
+ * `Conv2d::apply`): a 3x3 conv (stride 1, zero padding 1) with few output
+ * channels, written into the NCHW frame with the bias,
+ *   out[o][y*W + x] = b[o] + sum_{ky,kx,c} w[o][c][ky][kx] x[(y+ky-1)*W + x+kx-1][c]
+ * for o < cout.
+ *   x: f16 NHWC [H*W][cin_p], cin_p a multiple of 64, 16-byte aligned;
+ *   w: the blocked 3x3 plane of ig_pack_conv_weights (cout_p >= cout);
+ *   bias: f32 [cout] or NULL; out: f32 [cout][H*W].
+ * cout must be 1..16 (IG_EUNSUPPORTED otherwise). */
+int ig_conv3x3_out_nchw(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout, int cout_p,
+                        const float *bias, float *out, void *stream);
+
 /* The DupUp shortcut ([QI] DUPUP_SRC and `run_blocks`): a channel shuffle
  * of the half-resolution input added onto the 2x grid,
  *   x[2y+sy][2x+sx][o] += src[y][x][(o*factor + (ft-1)*4 + 2*sy + sx) / repeats]

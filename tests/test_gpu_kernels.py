@@ -181,6 +181,34 @@ def test_conv1x1_isolated(H, W, cin, cout):
     assert conv_err(got, ref)[2] <= 1e-4
 
 
+@pytest.mark.parametrize("H,W,cin,cout", [(17, 45, 128, 3), (8, 32, 64, 1), (40, 70, 192, 16), (33, 31, 128, 5),
+                                          (1, 1, 64, 3), (64, 64, 128, 3)])
+def test_output_conv_nchw(H, W, cin, cout):
+    """The decoder's output conv: few output channels, NCHW frame + bias,
+    against the oracle's convolution on the same f16 input."""
+    seed = 300 + H + cout
+    x16 = synth.normal(16, seed, (H, W, cin), 1.0, np.float16)
+    w = synth.normal(16, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
+    b = synth.normal(16, seed + 2, (cout,), 0.02)
+    cin_p, cout_p = cpad(cin), cpad(cout)
+    out = nan_f32((cout, H * W))
+    ig.conv3x3_out_nchw(dev(pad_last(x16.reshape(H * W, cin), cin_p)), H, W, cin_p, packed(w), cout, cout_p,
+                        padded_vec(b, cout_p), out)
+    got = host(out).reshape(cout, H, W)
+    assert not np.isnan(got).any(), "output not fully written"
+    ref = O.conv2d(nhwc_to_chw(x16.astype(np.float64), H, W), w) + b[:, None, None]
+    err, rms, ratio = conv_err(got, ref)
+    print("output conv %dx%d %d->%d: ratio %.2e" % (H, W, cin, cout, ratio))
+    assert ratio <= 1e-4
+
+
+def test_output_conv_rejects_wide_output():
+    with pytest.raises(ig.IgError) as e:
+        ig.conv3x3_out_nchw(dev(np.zeros((4, 64), np.float16)), 2, 2, 64, dev(np.zeros(9 * 64 * 64, np.float16)),
+                            17, 64, None, nan_f32((17, 4)))
+    assert e.value.code == -2
+
+
 def test_conv_accumulate_epilogue():
     H, W, c = 10, 12, 64
     x16 = synth.normal(15, 0, (H * W, c), 1.0, np.float16)
