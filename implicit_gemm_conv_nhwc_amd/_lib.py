@@ -68,6 +68,8 @@ _smax = _sig("ig_softmax_rows_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _
 _lat = _sig("ig_latent_to_nhwc_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp])
 _out = _sig("ig_nhwc_to_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
 _zero = _sig("ig_zero_rows_f16", [_vp, _c_int, _c_int, _c_int, _vp])
+_conv_norm = _sig("ig_conv3x3_norm_nhwc", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp,
+                                          _c_float, _vp, _c_int, _c_float, _vp, _vp, _vp])
 _conv_out = _sig("ig_conv3x3_out_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp])
 _dupup = _sig("ig_dupup_add", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _vp])
@@ -162,6 +164,12 @@ def latent_to_nhwc_f16(z, zc, M, cp, y, stream=None):
 
 def nhwc_to_nchw(y, M, ld, nch, bias, out, stream=None):
     return _check(_out(_ptr(y), M, ld, nch, _ptr(bias), _ptr(out), _stream(stream)))
+
+
+def conv3x3_norm_nhwc(x, H, W, cin_p, mode, w, cout_p, c_real, bias, oscale, gamma, silu, eps, y, yn,
+                      stream=None):
+    return _check(_conv_norm(_ptr(x), H, W, cin_p, mode, _ptr(w), cout_p, c_real, _ptr(bias), oscale,
+                             _ptr(gamma), silu, eps, _ptr(y), _ptr(yn), _stream(stream)))
 
 
 def conv3x3_out_nchw(x, H, W, cin_p, w, cout, cout_p, bias, out, stream=None):

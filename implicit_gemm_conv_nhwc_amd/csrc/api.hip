@@ -170,6 +170,46 @@ int ig_conv_nhwc_ex(const uint16_t *x, int H, int W, int cin_p, int mode, const 
     return conv_any(x, H, W, cin_p, mode, w, cout_p, bias, oscale, accumulate, y, stream);
 }
 
+int ig_conv3x3_norm_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
+                         int c_real, const float *bias, float oscale, const float *gamma, int silu, float eps,
+                         float *y, uint16_t *yn, void *stream)
+{
+    clear_error();
+    if (mode != 1 && mode != 2) return fail(IG_EINVAL, "mode %d is not a 3x3 mode", mode);
+    if (cout_p != 64 && cout_p != 128)
+        return fail(IG_EUNSUPPORTED, "the fused norm needs cout_p 64 or 128, got %d", cout_p);
+    if (c_real <= 0 || c_real > cout_p) return fail(IG_EINVAL, "c_real=%d outside 1..cout_p", c_real);
+    if (!(eps > 0.f)) return fail(IG_EINVAL, "eps must be positive");
+    bool empty;
+    int r = check_conv(x, H, W, cin_p, w, cout_p, bias, y ? y : reinterpret_cast<float *>(yn), mode, &empty);
+    if (r || empty) return r;
+    if ((r = check_ptr(gamma, "gamma")) || (r = check_ptr(yn, "yn"))) return r;
+    IgemmArgs a{};
+    a.a = reinterpret_cast<const _Float16 *>(x);
+    a.b = reinterpret_cast<const _Float16 *>(w);
+    a.bias = bias;
+    a.c = y;
+    a.M = H * W * (mode == 2 ? 4 : 1);
+    a.N = cout_p;
+    a.K = 9 * cin_p;
+    a.lda = cin_p;
+    a.ldb = a.K;
+    a.ldc = cout_p;
+    a.H = H;
+    a.W = W;
+    a.cin_p = cin_p;
+    a.oscale = oscale;
+    a.ngamma = gamma;
+    a.ny = reinterpret_cast<_Float16 *>(yn);
+    a.norm_c = c_real;
+    a.norm_silu = silu ? 1 : 0;
+    a.norm_eps = eps;
+    a.write_out = y ? 1 : 0;
+    (void)hipGetLastError();
+    launch_conv_halo(mode == 1 ? kConv3x3 : kConv3x3Up2, a, reinterpret_cast<hipStream_t>(stream));
+    return check_launch("conv+norm launch");
+}
+
 int gemm1x1(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int N, int ldb,
             const float *bias, float oscale, void *c, int ldc, int c_is_f16, void *stream)
 {

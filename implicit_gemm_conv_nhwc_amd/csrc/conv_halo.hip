@@ -38,6 +38,10 @@
 //    pass, where the plain 32-byte pitch would conflict two ways;
 //  * the f32 tile leaves through LDS: every tile row goes out as one
 //    contiguous run of 16-byte stores;
+//  * when the tile spans all of a pixel's channels (N = 64 or 128) the
+//    epilogue can instead emit the pixel's RMS_norm (+ SiLU) as f16 from the
+//    staged rows -- the next step of the pages' resnet and output recipes --
+//    so the f32 result is neither stored nor read back;
 //  * workgroups are dealt round robin to the 8 XCDs; the tile order is
 //    remapped so each XCD works on a contiguous band of rows (shared halos
 //    and weights stay in its L2).
@@ -77,7 +81,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-template <int MODE, int BN, int NW>
+template <int MODE, int BN, int NW, bool NORM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 void k_conv_halo(IgemmArgs p)
 {
@@ -244,37 +248,78 @@ void k_conv_halo(IgemmArgs p)
             }
         __syncthreads();
         constexpr int V4 = 4 * TW * BN / 4;  // 16-byte pieces staged per pass
+        if (!NORM || p.write_out) {
 #pragma unroll
-        for (int v = tid; v < V4; v += NT) {
-            const int e = v * 4;
-            const int wr = e / (TW * BN);  // wave row group: tile row FM * wr + q
-            const int px = (e / BN) % TW;
-            const int ch = e % BN;
+            for (int v = tid; v < V4; v += NT) {
+                const int e = v * 4;
+                const int wr = e / (TW * BN);  // wave row group: tile row FM * wr + q
+                const int px = (e / BN) % TW;
+                const int ch = e % BN;
+                const int oy = y0 + FM * wr + q, ox = x0 + px;
+                if (oy < Hout && ox < Wout) {
+                    float4 val = reinterpret_cast<const float4 *>(stg)[v];
+                    float *dst = out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch;
+                    if (accum) {
+                        const float4 o = *reinterpret_cast<const float4 *>(dst);
+                        val.x += o.x;
+                        val.y += o.y;
+                        val.z += o.z;
+                        val.w += o.w;
+                    }
+                    *reinterpret_cast<float4 *>(dst) = val;
+                }
+            }
+        }
+        if (NORM) {
+            // the staged 4 x TW pixels' RMS_norm: TPP consecutive lanes per
+            // pixel, 32 channels each (the tile holds every channel: BN = N)
+            constexpr int TPP = NT / (4 * TW);
+            static_assert(BN / TPP == 32, "32 channels per lane");
+            const int pi = tid / TPP, cb = (tid % TPP) * 32;
+            const int wr = pi / TW, px = pi % TW;
+            const float4 *sv = reinterpret_cast<const float4 *>(stg + (wr * TW + px) * BN + cb);
+            float4 v[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                v[k] = sv[k];
+                ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+            }
+#pragma unroll
+            for (int off = TPP / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, TPP);
+            const float inv = sqrtf((float)p.norm_c) / fmaxf(sqrtf(ss), p.norm_eps);
             const int oy = y0 + FM * wr + q, ox = x0 + px;
             if (oy < Hout && ox < Wout) {
-                float4 val = reinterpret_cast<const float4 *>(stg)[v];
-                float *dst = out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch;
-                if (accum) {
-                    const float4 o = *reinterpret_cast<const float4 *>(dst);
-                    val.x += o.x;
-                    val.y += o.y;
-                    val.z += o.z;
-                    val.w += o.w;
+                const float4 *g4 = reinterpret_cast<const float4 *>(p.ngamma + cb);
+                _Float16 *dst = p.ny + ((int64_t)oy * Wout + ox) * BN + cb;
+#pragma unroll
+                for (int k = 0; k < 8; k += 2) {
+                    float o[8] = {v[k].x, v[k].y, v[k].z, v[k].w, v[k + 1].x, v[k + 1].y, v[k + 1].z, v[k + 1].w};
+                    const float4 ga = g4[k], gb = g4[k + 1];
+                    const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+                    half8 h;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float y = o[e] * inv * gm[e];
+                        // fast divide: the epilogue is on the critical path
+                        if (p.norm_silu) y = __fdividef(y, 1.0f + __expf(-y));
+                        h[e] = (_Float16)y;
+                    }
+                    *reinterpret_cast<half8 *>(dst + 4 * k) = h;
                 }
-                *reinterpret_cast<float4 *>(dst) = val;
             }
         }
         __syncthreads();
     }
 }
 
-template <int MODE, int BN, int NW>
+template <int MODE, int BN, int NW, bool NORM = false>
 void launch_t(const IgemmArgs &a, hipStream_t s)
 {
     const int Hout = (MODE == kConv3x3Up2) ? 2 * a.H : a.H;
     const int Wout = (MODE == kConv3x3Up2) ? 2 * a.W : a.W;
     const int grid = ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW) * (a.N / BN);
-    hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW, NORM>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 
 }  // namespace
@@ -289,6 +334,17 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
     const int Wout = (mode == kConv3x3Up2) ? 2 * a.W : a.W;
     const int64_t pix_tiles = (int64_t)((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW);
     const bool bn128 = (a.N % 128) == 0 && pix_tiles * (a.N / 128) >= 256;
+    if (a.ngamma) {
+        // the fused RMS_norm needs every channel of a pixel in one tile
+        if (mode == kConv3x3) {
+            if (a.N == 128) launch_t<kConv3x3, 128, 8, true>(a, s);
+            else launch_t<kConv3x3, 64, 4, true>(a, s);
+        } else {
+            if (a.N == 128) launch_t<kConv3x3Up2, 128, 8, true>(a, s);
+            else launch_t<kConv3x3Up2, 64, 4, true>(a, s);
+        }
+        return;
+    }
     if (mode == kConv3x3) {
         if (bn128) launch_t<kConv3x3, 128, 8>(a, s);
         else launch_t<kConv3x3, 64, 4>(a, s);

@@ -140,6 +140,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
             if ((e = check_conv_w(u.up, nm, 3))) return e;
             if (u.up.cin != c || u.up.cin_p != cp) return fail(IG_EINVAL, "%s: input %d, stream %d", nm, u.up.cin, c);
             upd(pl.max_xn, M * cp);
+            upd(pl.max_xg, M * cp);
             H *= 2;
             W *= 2;
             M *= 4;
@@ -212,6 +213,36 @@ struct Run {
         launch_igemm(mode, a, s);
     }
 
+    // a 3x3 conv whose epilogue emits f16(RMS_norm(oscale*acc + bias; gamma) -> SiLU)
+    // instead of the f32 result (every channel of a pixel in one tile)
+    void conv_norm(int mode, const _Float16 *in, int H, int W, const ig_conv_w &cw, const float *bias,
+                   float oscale, const float *gamma, int c_real, _Float16 *yn)
+    {
+        IgemmArgs a{};
+        a.a = in;
+        a.b = reinterpret_cast<const _Float16 *>(cw.w);
+        a.bias = bias;
+        a.c = nullptr;
+        a.M = H * W * (mode == kConv3x3Up2 ? 4 : 1);
+        a.N = cw.cout_p;
+        a.K = 9 * cw.cin_p;
+        a.lda = cw.cin_p;
+        a.ldb = a.K;
+        a.ldc = cw.cout_p;
+        a.H = H;
+        a.W = W;
+        a.cin_p = cw.cin_p;
+        a.oscale = oscale;
+        a.ngamma = gamma;
+        a.ny = yn;
+        a.norm_c = c_real;
+        a.norm_silu = 1;
+        a.norm_eps = kEps;
+        a.write_out = 0;
+        launch_conv_halo(mode, a, s);
+    }
+    static bool fusable(const ig_conv_w &cw) { return cw.cout_p == 64 || cw.cout_p == 128; }
+
     void gemm(const _Float16 *A, int M, int K, int lda, const _Float16 *B, int N, int ldb,
               const float *bias, float oscale, void *C, int ldc, int f16, int acc)
     {
@@ -241,9 +272,17 @@ struct Run {
             launch_guard_cast(x, M, cp, nullptr, g, xg, s);
             conv(kGemm, xg, H, W, r.sc, r.sc.b, ldexpf(1.f, g), 0, x);
         }
-        conv(kConv3x3, xn, H, W, r.c1, nullptr, 1.f, 0, h);
-        launch_rmsnorm(h, M, r.c1.cout_p, r.c1.cout, r.c1.b, r.g2, 1, kEps, xn, s);
-        conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x);
+        if (fusable(r.c1)) {
+            // conv1's epilogue normalises (h + b1) itself; the f16 result
+            // goes to the h region (conv1 still reads xn)
+            _Float16 *hn = reinterpret_cast<_Float16 *>(h);
+            conv_norm(kConv3x3, xn, H, W, r.c1, r.c1.b, 1.f, r.g2, r.c1.cout, hn);
+            conv(kConv3x3, hn, H, W, r.c2, r.c2.b, 1.f, 1, x);
+        } else {
+            conv(kConv3x3, xn, H, W, r.c1, nullptr, 1.f, 0, h);
+            launch_rmsnorm(h, M, r.c1.cout_p, r.c1.cout, r.c1.b, r.g2, 1, kEps, xn, s);
+            conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x);
+        }
     }
 
     // the mid attention, single head over the m latent pixels
@@ -338,6 +377,7 @@ int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, 
     r.resnet(d.mid[1], H, W, cp);
     cp = d.mid[1].c2.cout_p;
     const float gs = ldexpf(1.f, guard_log2);
+    bool normed = false;
     for (int st = 0; st < d.n_up; ++st) {
         const ig_up_w &u = d.ups[st];
         for (int k = 0; k < u.n_res; ++k) {
@@ -345,14 +385,21 @@ int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, 
             cp = u.res[k].c2.cout_p;
         }
         if (u.has_up) {
-            launch_guard_cast(r.x, H * W, cp, nullptr, guard_log2, r.xn, s);
-            r.conv(kConv3x3Up2, r.xn, H, W, u.up, u.up.b, gs, 0, r.x);
+            launch_guard_cast(r.x, H * W, cp, nullptr, guard_log2, r.xg, s);
+            if (st == d.n_up - 1 && Run::fusable(u.up) && d.norm_out_c == u.up.cout) {
+                // the last up conv's epilogue applies norm_out + SiLU; the
+                // f32 stream is not needed after it
+                r.conv_norm(kConv3x3Up2, r.xg, H, W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, r.xn);
+                normed = true;
+            } else {
+                r.conv(kConv3x3Up2, r.xg, H, W, u.up, u.up.b, gs, 0, r.x);
+            }
             H *= 2;
             W *= 2;
             cp = u.up.cout_p;
         }
     }
-    launch_rmsnorm(r.x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, r.xn, s);
+    if (!normed) launch_rmsnorm(r.x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, r.xn, s);
     if (d.conv_out.cout <= 16) {
         // few output channels: straight into the NCHW frame
         launch_conv_out(r.xn, H, W, d.conv_out.cin_p, reinterpret_cast<const _Float16 *>(d.conv_out.w),

@@ -36,12 +36,22 @@ struct IgemmArgs {
     float oscale;
     int accumulate;     // f32 output only: c += result
     int out_f16;
+    // 3x3 convs whose tile spans all N channels: the epilogue can also
+    // emit the per-pixel RMS_norm of the result (pages' RMSN_SRC) as f16
+    // into ny [M][N]: v * sqrt(norm_c) / max(|v|, norm_eps) * gamma, then
+    // SiLU if norm_silu; with write_out = 0 the f32 result is not stored
+    const float *ngamma;  // [N], or null for no norm
+    _Float16 *ny;
+    int norm_c, norm_silu;
+    float norm_eps;
+    int write_out = 1;
 };
 
 // Launch the MFMA implicit GEMM for `mode`; picks the tile shape. The 3x3
 // modes go to the patch-reusing convolution kernel.
 void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s);
 // The 3x3 convolutions (kConv3x3, kConv3x3Up2) with per-tile input patches.
+// With a.ngamma set, N must be 64 or 128 and accumulate 0.
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------------

@@ -112,6 +112,21 @@ int ig_conv_nhwc_ex(const uint16_t *x, int H, int W, int cin_p, int mode, const 
                     int cout_p, const float *bias, float oscale, int accumulate, float *y,
                     void *stream);
 
+/* A 3x3 conv (mode 1) or folded-upsample 3x3 conv (mode 2) whose epilogue
+ * also applies the next step of the pages' recipe ([QI] `Rec::resnet`:
+ * h = conv1(xn), then xn = f16(RMS_norm(h + b1) -> SiLU); `output_rows`:
+ * norm_out after the last up conv) -- RMSN_SRC on each output pixel:
+ *   v = oscale*acc + bias; yn = f16(v * sqrt(c_real) / max(|v|_2, eps) * gamma),
+ *   then SiLU (yn / (1 + e^-yn)) if silu,
+ * so the f32 result need not be stored and re-read. Every channel of a
+ * pixel must sit in one tile: cout_p must be 64 or 128 (IG_EUNSUPPORTED
+ * otherwise); the pad channels' weights, bias and gamma must be zero.
+ *   y: f32 [M][cout_p] receives v when non-NULL; yn: f16 [M][cout_p].
+ * Other arguments and errors as ig_conv_nhwc_ex. */
+int ig_conv3x3_norm_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
+                         int c_real, const float *bias, float oscale, const float *gamma, int silu, float eps,
+                         float *y, uint16_t *yn, void *stream);
+
 /* ---------------------------------------------------------------------
  * NT GEMM ([QI] `mmc`: B is the "plane" [N][K], A the activations [M][K];
  * the 1x1 convs and every attention product of [QI] `attention`):

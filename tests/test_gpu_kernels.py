@@ -209,6 +209,57 @@ def test_output_conv_rejects_wide_output():
     assert e.value.code == -2
 
 
+@pytest.mark.parametrize("H,W,cin,cout,c_real,mode,silu,want_y", [
+    (64, 64, 128, 128, 128, 1, 1, False), (13, 29, 64, 64, 50, 1, 0, True),
+    (9, 13, 64, 128, 128, 2, 1, False), (40, 33, 192, 128, 100, 1, 1, True), (1, 1, 64, 64, 64, 2, 1, False)])
+def test_conv_with_fused_norm(H, W, cin, cout, c_real, mode, silu, want_y):
+    """A 3x3 conv whose epilogue emits f16(RMS_norm(conv + b) -> SiLU),
+    against the oracle's norm of the oracle's convolution. The conv's f32
+    accumulation moves v by ~1e-6 relative, which flips the f16 rounding of
+    a few tenths of a percent of the outputs: <= 1 ulp (or <= 1e-5 absolute
+    near zero, where the conv's error is several tiny ulps), >= 99.5% exact."""
+    seed = 400 + H + cout
+    x16 = synth.normal(17, seed, (H, W, cin), 1.0, np.float16)
+    w = np.zeros((cout, cin, 3, 3), np.float16)
+    w[:c_real] = synth.normal(17, seed + 1, (c_real, cin, 3, 3), 1.0 / (9 * cin), np.float16)
+    b = np.zeros(cout, np.float32)
+    b[:c_real] = synth.normal(17, seed + 2, (c_real,), 0.02)
+    gamma = np.zeros(cout, np.float32)
+    gamma[:c_real] = synth.uniform(17, seed + 3, (c_real,), 0.5, 1.5)
+    cin_p = cpad(cin)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    osc = 256.0 if mode == 2 else 1.0
+    yn = nan_f16((Ho * Wo, cout))
+    y = nan_f32((Ho * Wo, cout)) if want_y else None
+    ig.conv3x3_norm_nhwc(dev(pad_last(x16.reshape(H * W, cin), cin_p)), H, W, cin_p, mode, packed(w), cout,
+                         c_real, dev(b), osc, dev(gamma), silu, 1e-12, y, yn)
+    got = host(yn)
+    assert not np.isnan(got.astype(np.float32)).any()
+    assert np.all(got[:, c_real:] == 0)
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    conv = osc * (O.conv2d_up2(xc, w) if mode == 2 else O.conv2d(xc, w)) + b[:, None, None]
+    ref = O.rmsnorm(conv[:c_real].reshape(c_real, -1), gamma[:c_real], silu=bool(silu)).T
+    u = f16_ulps(got[:, :c_real], ref.astype(np.float16))
+    d = np.abs(got[:, :c_real].astype(np.float64) - ref)
+    exact = float(np.mean(u == 0))
+    print("conv+norm %dx%d %d->%d mode %d: max ulp %d, exact %.5f, max|d| %.2e" % (H, W, cin, cout, mode, u.max(),
+                                                                               exact, d.max()))
+    # near zero an ulp is tiny; there the bar is the conv's absolute error
+    # carried through the norm (outputs have RMS ~1)
+    assert np.all((u <= 1) | (d <= 1e-5)) and exact >= 0.995
+    if want_y:
+        gy = nhwc_to_chw(host(y)[:, :c_real], Ho, Wo)
+        assert conv_err(gy, conv[:c_real])[2] <= 1e-4
+
+
+def test_conv_fused_norm_needs_one_tile_per_pixel():
+    with pytest.raises(ig.IgError) as e:
+        z = dev(np.zeros((4, 64), np.float16))
+        ig.conv3x3_norm_nhwc(z, 2, 2, 64, 1, dev(np.zeros(9 * 64 * 192, np.float16)), 192, 192, None, 1.0,
+                             dev(np.zeros(192, np.float32)), 1, 1e-12, None, nan_f16((4, 192)))
+    assert e.value.code == -2
+
+
 def test_conv_accumulate_epilogue():
     H, W, c = 10, 12, 64
     x16 = synth.normal(15, 0, (H * W, c), 1.0, np.float16)
