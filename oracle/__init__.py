@@ -212,6 +212,41 @@ def rmsnorm(x, gamma, bias=None, silu=False, eps=1e-12):
 
 
 # ---------------------------------------------------------------------------
+# GroupNorm
+# ---------------------------------------------------------------------------
+
+
+def group_norm(x, groups, gamma, beta, bias=None, silu=False, eps=1e-6):
+    """GroupNorm over channel groups (vae.rs, `GroupNorm::apply`): the
+    channels split into `groups` consecutive groups of c / groups; per group,
+    over all of its channels and pixels, mean and population variance (the
+    mean of (v - mean)^2), then y = (v - mean) / sqrt(var + eps) * gamma +
+    beta. The device recipe of page "cortiq-engine 0.8.72,
+    src/gpu_wgpu/s2v_vae.rs" (GN_PART_SRC, GN_APPLY_SRC, `gn`) adds a bias
+    on read (v = x + b) and an optional SiLU. x: [c, ...] channel-first."""
+    x = _f64(x)
+    c = x.shape[0]
+    assert c % groups == 0
+    per = c // groups
+    v = x.reshape(c, -1).copy()
+    if bias is not None:
+        v += _f64(bias)[:, None]
+    g = _f64(gamma)
+    bt = _f64(beta)
+    y = np.empty_like(v)
+    for k in range(groups):
+        span = v[k * per:(k + 1) * per]
+        n = span.size
+        mean = span.sum() / n
+        var = ((span - mean) ** 2).sum() / n
+        inv = 1.0 / np.sqrt(var + eps)
+        y[k * per:(k + 1) * per] = (span - mean) * inv * g[k * per:(k + 1) * per, None] + bt[k * per:(k + 1) * per, None]
+    if silu:
+        y = y / (1.0 + np.exp(-y))
+    return y.reshape(x.shape)
+
+
+# ---------------------------------------------------------------------------
 # attention (single head over the pixels)
 # ---------------------------------------------------------------------------
 

@@ -266,6 +266,55 @@ def test_guard_subnormal_error_and_overflow():
 
 
 # ---------------------------------------------------------------------------
+# GroupNorm (the NEXT variant for FLUX-class decoders)
+# ---------------------------------------------------------------------------
+
+
+def test_group_norm_hand_case_from_pages():
+    g = _gold("group_norm_case.json")
+    x = np.array(g["x"], np.float64).reshape(2, g["h"], g["w"])
+    y = O.group_norm(x, g["groups"], np.array(g["weight"]), np.array(g["bias"])).ravel()
+    for k, v in g["expect"].items():
+        assert abs(y[int(k)] - v) < g["tol"][k], (k, y[int(k)], v)
+
+
+@pytest.mark.parametrize("c,groups,with_bias,silu", [(64, 32, False, False), (128, 32, True, False),
+                                                     (96, 8, True, True), (6, 3, False, True)])
+def test_group_norm_matches_torch_f64(c, groups, with_bias, silu):
+    rng = np.random.default_rng(c + groups)
+    x = rng.standard_normal((c, 7, 9)) * 3 + rng.standard_normal((c, 1, 1)) * 5
+    gamma = rng.uniform(0.5, 1.5, c)
+    beta = rng.standard_normal(c) * 0.1
+    b = rng.standard_normal(c) * 0.3 if with_bias else None
+    got = O.group_norm(x, groups, gamma, beta, bias=b, silu=silu)
+    xt = torch.from_numpy(x if b is None else x + b[:, None, None])[None]
+    ref = F.group_norm(xt, groups, torch.from_numpy(gamma), torch.from_numpy(beta), eps=1e-6)
+    if silu:
+        ref = F.silu(ref)
+    assert np.allclose(got, ref[0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_group_norm_invariants():
+    rng = np.random.default_rng(5)
+    c, groups = 32, 4
+    x = rng.standard_normal((c, 6, 5)) * 2 + 7
+    one, zero = np.ones(c), np.zeros(c)
+    y = O.group_norm(x, groups, one, zero).reshape(groups, -1)
+    var = x.reshape(groups, -1).var(axis=1)
+    # each group: mean 0, variance var / (var + eps)
+    assert np.allclose(y.mean(axis=1), 0, atol=1e-12)
+    assert np.allclose(y.var(axis=1), var / (var + 1e-6), rtol=1e-12)
+    # a per-group shift changes nothing
+    shift = np.repeat(rng.standard_normal(groups) * 10, c // groups)[:, None, None]
+    assert np.allclose(O.group_norm(x + shift, groups, one, zero), O.group_norm(x, groups, one, zero), atol=1e-10)
+    # one group per channel is per-channel standardisation
+    y1 = O.group_norm(x, c, one, zero)
+    xr = x.reshape(c, -1)
+    ref = (xr - xr.mean(axis=1, keepdims=True)) / np.sqrt(xr.var(axis=1, keepdims=True) + 1e-6)
+    assert np.allclose(y1.reshape(c, -1), ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
 
