@@ -15,6 +15,9 @@ Also measured, in the same process and on the stream the kernels run on:
     larger than the 256 MB Infinity Cache;
   * roofline_norm: RMS_norm + f16 store at 512x512x128 (201 MB moved per
     launch: f32 read + f16 write) against 8 TB/s HBM;
+  * roofline_cast: the guarded f16 cast at 512x512x128 (same 201 MB);
+  * roofline_groupnorm: GroupNorm(32) + SiLU at 512x512x128, algorithmic
+    201 MB (its statistics pass reads the input once more);
   * cpu_baseline: the CPU oracle decoding the 256x256 configuration (a
     bounded sample of the same decoder), in TFLOP/s.
 
@@ -207,6 +210,62 @@ def bench_norm_roofline(reps, H=512, W=512, C=128):
     return {"avg_ms": avg_ms, "bytes": M * C * 6, "sets": nsets}
 
 
+def _pool_timed(fn, reps, per_set_bytes, make_set):
+    """Time `fn(set)` over a rotating pool of input/output sets larger than
+    the Infinity Cache; returns (avg ms, sets)."""
+    import numpy as np
+    import torch
+
+    nsets = max(2, int(np.ceil(1.2e9 / per_set_bytes)))
+    sets = [make_set() for _ in range(nsets)]
+    for i in range(3):
+        fn(sets[i % nsets])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(sets[i % nsets])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps, nsets
+
+
+def bench_cast_roofline(reps, H=512, W=512, C=128):
+    """guard_cast f32 -> f16 (x 2^-8) at 512x512x128: 6 bytes per element."""
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+
+    M = H * W
+    dev = torch.device("cuda")
+    x0 = torch.randn((M, C), device=dev) * 300.0
+    ms, nsets = _pool_timed(lambda st: ig.guard_cast(st[0], M, C, None, 8, st[1]), reps, M * C * 6,
+                            lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
+    return {"avg_ms": ms, "bytes": M * C * 6, "sets": nsets}
+
+
+def bench_groupnorm_roofline(reps, H=512, W=512, C=128, groups=32):
+    """GroupNorm(32) + SiLU -> f16 at 512x512x128. Algorithmic bytes: 6 per
+    element (f32 read, f16 write); the kernels read the input twice (the
+    statistics must be complete before any output)."""
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+
+    M = H * W
+    dev = torch.device("cuda")
+    x0 = torch.randn((M, C), device=dev)
+    gamma = torch.rand(C, device=dev) + 0.5
+    beta = torch.randn(C, device=dev) * 0.1
+    nbytes = ig.groupnorm_workspace_bytes(M, C, groups)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ms, nsets = _pool_timed(
+        lambda st: ig.groupnorm_silu_f16(st[0], M, C, C, groups, None, gamma, beta, 1, 1e-6, ws, nbytes, st[1]),
+        reps, M * C * 6, lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
+    return {"avg_ms": ms, "bytes": M * C * 6, "sets": nsets}
+
+
 def cpu_baseline(min_seconds=10.0):
     """The oracle (as it is) decoding the 256x256 configuration on the host."""
     import oracle as O
@@ -354,6 +413,15 @@ def main():
     log("rmsnorm 512^2x128: %.2f us, %.0f GB/s (%.1f%% of HBM)" % (
         norm["avg_ms"] * 1000, norm_gbs, 100 * norm_gbs / HBM_PEAK_GBS))
 
+    cast = bench_cast_roofline(args.roof_reps)
+    cast_gbs = cast["bytes"] / (cast["avg_ms"] / 1000.0) / 1e9
+    log("guard_cast 512^2x128: %.2f us, %.0f GB/s (%.1f%% of HBM)" % (
+        cast["avg_ms"] * 1000, cast_gbs, 100 * cast_gbs / HBM_PEAK_GBS))
+    gn = bench_groupnorm_roofline(args.roof_reps)
+    gn_gbs = gn["bytes"] / (gn["avg_ms"] / 1000.0) / 1e9
+    log("groupnorm 512^2x128 (32 groups): %.2f us, %.0f GB/s algorithmic (%.1f%% of HBM)" % (
+        gn["avg_ms"] * 1000, gn_gbs, 100 * gn_gbs / HBM_PEAK_GBS))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
@@ -405,6 +473,24 @@ def main():
             "unit": "GB/s",
             "frac": round(norm_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(norm["avg_ms"] * 1000, 3),
+        },
+        "roofline_cast": {
+            "kernel": "guard_cast 512x512x128 (g=8)",
+            "bound": "hbm",
+            "achieved": round(cast_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(cast_gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(cast["avg_ms"] * 1000, 3),
+        },
+        "roofline_groupnorm": {
+            "kernel": "groupnorm_silu_f16 512x512x128, 32 groups (stats + finalize + apply)",
+            "bound": "hbm",
+            "achieved": round(gn_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gn_gbs / HBM_PEAK_GBS, 4),
+            "avg_us": round(gn["avg_ms"] * 1000, 3),
         },
         "cpu_baseline": cpu,
         "context": "pages: 0.49-0.61 s per 1024^2 decode on an RTX PRO 4000 Blackwell "

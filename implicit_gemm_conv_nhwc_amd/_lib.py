@@ -70,6 +70,11 @@ _out = _sig("ig_nhwc_to_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
 _zero = _sig("ig_zero_rows_f16", [_vp, _c_int, _c_int, _c_int, _vp])
 _conv_norm = _sig("ig_conv3x3_norm_nhwc", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp,
                                           _c_float, _vp, _c_int, _c_float, _vp, _vp, _vp])
+_gn_ws = lib.ig_groupnorm_workspace_bytes
+_gn_ws.argtypes = [_c_int, _c_int, _c_int]
+_gn_ws.restype = ctypes.c_size_t
+_gn = _sig("groupnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _c_float, _vp,
+                                  ctypes.c_size_t, _vp, _vp])
 _conv_out = _sig("ig_conv3x3_out_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp])
 _dupup = _sig("ig_dupup_add", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _vp])
@@ -170,6 +175,15 @@ def conv3x3_norm_nhwc(x, H, W, cin_p, mode, w, cout_p, c_real, bias, oscale, gam
                       stream=None):
     return _check(_conv_norm(_ptr(x), H, W, cin_p, mode, _ptr(w), cout_p, c_real, _ptr(bias), oscale,
                              _ptr(gamma), silu, eps, _ptr(y), _ptr(yn), _stream(stream)))
+
+
+def groupnorm_workspace_bytes(M, cp, groups):
+    return int(_gn_ws(M, cp, groups))
+
+
+def groupnorm_silu_f16(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, ws, ws_bytes, y, stream=None):
+    return _check(_gn(_ptr(x), M, cp, c_real, groups, _ptr(bias), _ptr(gamma), _ptr(beta), silu, eps, _ptr(ws),
+                      ws_bytes, _ptr(y), _stream(stream)))
 
 
 def conv3x3_out_nchw(x, H, W, cin_p, w, cout, cout_p, bias, out, stream=None):

@@ -241,6 +241,38 @@ int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bia
     return check_launch("rmsnorm launch");
 }
 
+size_t ig_groupnorm_workspace_bytes(int M, int cp, int groups)
+{
+    if (M < 0 || cp <= 0 || groups <= 0) return 0;
+    return gn_workspace_bytes(M, cp, groups);
+}
+
+int groupnorm_silu_f16(const float *x, int M, int cp, int c_real, int groups, const float *bias,
+                       const float *gamma, const float *beta, int silu, float eps, void *ws, size_t ws_bytes,
+                       uint16_t *y, void *stream)
+{
+    clear_error();
+    if (M < 0) return fail(IG_EINVAL, "M=%d is negative", M);
+    if (cp <= 0 || c_real <= 0 || c_real > cp || groups <= 0) return fail(IG_EINVAL, "bad channels cp=%d c_real=%d groups=%d", cp, c_real, groups);
+    if (!gn_supported(cp, c_real, groups))
+        return fail(IG_EUNSUPPORTED, "GroupNorm needs cp %% 4 == 0 (<= 1024) and 1..128 groups dividing c_real");
+    if (!(eps > 0.f)) return fail(IG_EINVAL, "eps must be positive");
+    if ((int64_t)M * cp >= (1LL << 40)) return fail(IG_EUNSUPPORTED, "too many elements");
+    if (M == 0) return IG_OK;
+    int r;
+    if ((r = check_ptr(x, "x")) || (r = check_ptr(gamma, "gamma")) || (r = check_ptr(beta, "beta")) ||
+        (r = check_ptr(y, "y", false)))
+        return r;
+    if (bias && (r = check_ptr(bias, "bias"))) return r;
+    if (!ws || ws_bytes < gn_workspace_bytes(M, cp, groups))
+        return fail(IG_EWORKSPACE, "GroupNorm workspace of %zu bytes, %zu needed", ws_bytes,
+                    gn_workspace_bytes(M, cp, groups));
+    (void)hipGetLastError();
+    launch_groupnorm(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, ws, reinterpret_cast<_Float16 *>(y),
+                     reinterpret_cast<hipStream_t>(stream));
+    return check_launch("groupnorm launch");
+}
+
 int guard_cast(const float *x, int M, int C, const float *bias, int guard_log2, uint16_t *y,
                void *stream)
 {

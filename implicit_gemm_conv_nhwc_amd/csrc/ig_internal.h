@@ -87,6 +87,12 @@ void launch_rowstat(const float *stats, int nparts, int rows, float *rowstat, hi
 // ---------------------------------------------------------------------
 void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias,
                     const float *gamma, int silu, float eps, _Float16 *y, hipStream_t s);
+// GroupNorm: workspace for the per-chunk statistics, support check, launch
+size_t gn_workspace_bytes(int M, int cp, int groups);
+bool gn_supported(int cp, int c_real, int groups);
+void launch_groupnorm(const float *x, int M, int cp, int c_real, int groups, const float *bias,
+                      const float *gamma, const float *beta, int silu, float eps, void *ws, _Float16 *y,
+                      hipStream_t s);
 void launch_guard_cast(const float *x, int M, int C, const float *bias, int guard_log2,
                        _Float16 *y, hipStream_t s);
 void launch_combine(float *x, const float *h, const float *hb, const float *sv, const float *sb,

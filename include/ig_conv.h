@@ -156,6 +156,24 @@ int gemm1x1_acc(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int
 int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bias,
                      const float *gamma, int silu, float eps, uint16_t *y, void *stream);
 
+/* GroupNorm into the next conv's f16 input -- the norm of FLUX-class
+ * decoders ([VAE] `GroupNorm::apply`; page "cortiq-engine 0.8.72,
+ * src/gpu_wgpu/s2v_vae.rs", GN_PART_SRC / GN_FIN_SRC / GN_APPLY_SRC, `gn`):
+ * the c_real real channels split into `groups` consecutive groups; per
+ * group, over its channels and all M pixels of v = x + bias (bias optional),
+ *   mean, var = mean((v - mean)^2),
+ *   y = (v - mean) / sqrt(var + eps) * gamma + beta, then SiLU if silu,
+ * stored as f16; pad channels (c_real <= c < cp) get 0.
+ *   x: f32 [M][cp]; bias, gamma, beta: f32 [cp]; y: f16 [M][cp];
+ *   ws: device workspace of ig_groupnorm_workspace_bytes(M, cp, groups)
+ *   bytes (per-chunk statistics; contents on return are scratch).
+ * cp must be a multiple of 4 up to 1024, groups 1..128 dividing c_real
+ * (IG_EUNSUPPORTED otherwise); IG_EWORKSPACE when ws_bytes is short. */
+size_t ig_groupnorm_workspace_bytes(int M, int cp, int groups);
+int groupnorm_silu_f16(const float *x, int M, int cp, int c_real, int groups, const float *bias,
+                       const float *gamma, const float *beta, int silu, float eps, void *ws, size_t ws_bytes,
+                       uint16_t *y, void *stream);
+
 /* ---------------------------------------------------------------------
  * The range-guarded f16 cast of the raw residual stream ([QI] `guard`,
  * CAST_SRC, `Rec::cast`): y = f16((x + bias) * 2^-guard_log2); the

@@ -101,6 +101,54 @@ def test_rmsnorm_zero_and_single_pixel():
 # ---------------------------------------------------------------------------
 
 
+# ---------------------------------------------------------------------------
+# GroupNorm (the variant for FLUX-class decoders)
+# ---------------------------------------------------------------------------
+
+
+def _gn_case(H, W, c, cp, groups, with_bias, silu, seed):
+    M = H * W
+    x = (synth.normal(18, seed, (M, c), 4.0) + synth.normal(18, seed + 1, (1, c), 9.0)).astype(np.float32)
+    gamma = synth.uniform(18, seed + 2, (c,), 0.5, 1.5)
+    beta = synth.normal(18, seed + 3, (c,), 0.1)
+    bias = synth.normal(18, seed + 4, (c,), 0.02) if with_bias else None
+    nbytes = ig.groupnorm_workspace_bytes(M, cp, groups)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = nan_f16((M, cp))
+    ig.groupnorm_silu_f16(dev(pad_last(x, cp)), M, cp, c, groups, None if bias is None else padded_vec(bias, cp),
+                          padded_vec(gamma, cp), padded_vec(beta, cp), int(silu), 1e-6, ws, nbytes, y)
+    got = host(y)
+    ref = O.group_norm(x.T, groups, gamma, beta, bias=bias, silu=silu).T
+    return got, ref
+
+
+@pytest.mark.parametrize("H,W,c,cp,groups,with_bias,silu", [
+    (64, 64, 128, 128, 32, True, True), (7, 9, 288, 320, 32, False, True), (33, 17, 512, 512, 32, True, False),
+    (1, 1, 64, 64, 32, False, True), (100, 90, 96, 128, 8, True, True), (512, 512, 128, 128, 32, True, True)])
+def test_groupnorm(H, W, c, cp, groups, with_bias, silu):
+    """GroupNorm on the GPU against the oracle (per-group statistics over
+    all pixels; the chunked statistics merge exactly up to rounding)."""
+    got, ref = _gn_case(H, W, c, cp, groups, with_bias, silu, seed=H + c)
+    assert not np.isnan(got.astype(np.float32)).any()
+    assert np.all(got[:, c:] == 0), "padded channels must be zero"
+    u = f16_ulps(got[:, :c], ref.astype(np.float16))
+    d = np.abs(got[:, :c].astype(np.float64) - ref)
+    exact = float(np.mean(u == 0))
+    print("groupnorm %dx%d c=%d g=%d: max ulp %d, exact %.5f" % (H, W, c, groups, u.max(), exact))
+    assert np.all((u <= 1) | (d <= 1e-5)) and exact >= 0.999
+
+
+def test_groupnorm_workspace_too_small():
+    M, cp = 64, 128
+    y = nan_f16((M, cp))
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    z = torch.zeros(cp, device="cuda")
+    with pytest.raises(ig.IgError) as e:
+        ig.groupnorm_silu_f16(torch.zeros((M, cp), device="cuda"), M, cp, cp, 32, None, z, z, 1, 1e-6, ws, 16, y)
+    assert e.value.code == -3
+    assert torch.isnan(y.float()).all()
+
+
 def test_guard_cast_config2_is_exact():
     d = synth.config2()
     H, W, C = d["x"].shape
