@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-ROOF_KERNEL = "k_conv_halo<1, 128, 8>"  # the 3x3 conv instantiation for 512^2 x 128
+ROOF_KERNEL = "k_conv_halo<1, 128, 8, false>"  # the 3x3 conv instantiation for 512^2 x 128
 CONV_SRC = os.path.join(ROOT, "implicit_gemm_conv_nhwc_amd", "csrc", "conv_halo.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_512x512x128_traffic.json")
 
