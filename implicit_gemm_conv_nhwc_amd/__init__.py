@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     dupup_add,
     gemm1x1,
     gemm1x1_acc,
+    attention_f16,
+    attention_workspace_bytes,
     groupnorm_silu_f16,
     groupnorm_workspace_bytes,
     guard_cast,

@@ -75,6 +75,8 @@ _gn_ws.argtypes = [_c_int, _c_int, _c_int]
 _gn_ws.restype = ctypes.c_size_t
 _gn = _sig("groupnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _c_float, _vp,
                                   ctypes.c_size_t, _vp, _vp])
+_attn_ws = _sig("ig_attention_workspace_bytes", [_c_int, _c_int], ctypes.c_size_t)
+_attn = _sig("attention_f16", [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, ctypes.c_size_t, _vp, _vp])
 _conv_out = _sig("ig_conv3x3_out_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp])
 _dupup = _sig("ig_dupup_add", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _vp])
@@ -245,3 +247,12 @@ def decoder_workspace_bytes(desc, h0, w0, q_chunk=0):
 def decoder_forward(desc, latent, h0, w0, guard_log2, q_chunk, ws, ws_bytes, out, stream=None):
     return _check(_dec(ctypes.byref(desc), _ptr(latent), h0, w0, int(guard_log2), int(q_chunk),
                        _ptr(ws), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def attention_workspace_bytes(m, C):
+    return int(_attn_ws(m, C))
+
+
+def attention_f16(q, k, vt, m, ld, C, bv, ws, ws_bytes, out, stream=None):
+    return _check(_attn(_ptr(q), _ptr(k), _ptr(vt), m, ld, C, _ptr(bv), _ptr(ws), ws_bytes, _ptr(out),
+                        _stream(stream)))

@@ -3,6 +3,7 @@
 // enqueued, so a rejected call leaves every output untouched (the
 // "declined, output untouched" contract of the page "cortiq-engine 0.8.3,
 // src/gpu_wgpu/qi21_vae.rs", `decode` and `decline`).
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 
@@ -324,6 +325,46 @@ int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols,
     launch_softmax(S, rows, lds, valid, ncols, reinterpret_cast<_Float16 *>(P), ldp,
                    reinterpret_cast<hipStream_t>(stream));
     return check_launch("softmax launch");
+}
+
+size_t ig_attention_workspace_bytes(int m, int C)
+{
+    clear_error();
+    if (m <= 0 || C != 512) {
+        fail(C != 512 ? IG_EUNSUPPORTED : IG_EINVAL, "attention m=%d C=%d (C must be 512)", m, C);
+        return 0;
+    }
+    return flash_workspace_bytes(m);
+}
+
+int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int m, int ld, int C,
+                  const float *bv, void *ws, size_t ws_bytes, uint16_t *out, void *stream)
+{
+    clear_error();
+    if (m <= 0 || m >= (1 << 22)) return fail(IG_EINVAL, "attention m=%d outside 1..2^22-1", m);
+    if (C != 512) return fail(IG_EUNSUPPORTED, "attention width %d: the single-pass kernel takes 512", C);
+    if (!flash_supported(m, ld, C))
+        return fail(IG_EINVAL, "ld=%d must be >= m rounded up to 32 (%d) and a multiple of 8", ld, (m + 31) / 32 * 32);
+    int r;
+    if ((r = check_ptr(q, "q", true)) || (r = check_ptr(k, "k", true)) || (r = check_ptr(vt, "vt", true)) ||
+        (r = check_ptr(out, "out", true)))
+        return r;
+    if (bv && (r = check_ptr(bv, "bv", true))) return r;
+    const size_t need = flash_workspace_bytes(m);
+    if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15)))
+        return fail(IG_EWORKSPACE, "attention workspace of %zu bytes, %zu needed (16-byte aligned)", ws_bytes, need);
+    FlashArgs a{};
+    a.q = reinterpret_cast<const _Float16 *>(q);
+    a.k = reinterpret_cast<const _Float16 *>(k);
+    a.vt = reinterpret_cast<const _Float16 *>(vt);
+    a.ld = ld;
+    a.m = m;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)C));
+    a.bv = bv;
+    a.out = reinterpret_cast<_Float16 *>(out);
+    (void)hipGetLastError();
+    launch_flash(a, ws, reinterpret_cast<hipStream_t>(stream));
+    return check_launch("attention launch");
 }
 
 int ig_latent_to_nhwc_f16(const float *z, int zc, int M, int cp, uint16_t *y, void *stream)

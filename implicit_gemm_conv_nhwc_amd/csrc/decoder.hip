@@ -36,6 +36,7 @@ struct Plan {
     int64_t max_xn = 0;  // f16 conv inputs
     int64_t max_xg = 0;  // f16 guarded shortcut input
     int m = 0, mp = 0, C = 0, qc = 0;
+    bool flash = false;  // single-pass attention (else query chunks)
     int H = 0, W = 0;    // output frame
     size_t off_x, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, total;
 };
@@ -120,10 +121,11 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     pl.m = (int)M;
     pl.mp = (int)((M + 63) / 64 * 64);
     pl.C = c;
+    pl.flash = q_chunk <= 0 && flash_supported(pl.m, pl.mp, c);
     pl.qc = q_chunk > 0 ? q_chunk : 16384;
     if (pl.qc > pl.m) pl.qc = pl.m;
     upd(pl.max_xn, (int64_t)pl.mp * c);
-    if ((uint64_t)pl.qc * pl.mp * 2 >= (3ULL << 30))
+    if (!pl.flash && (uint64_t)pl.qc * pl.mp * 2 >= (3ULL << 30))
         return fail(IG_EUNSUPPORTED, "query chunk %d x %d keys: probabilities exceed 3 GiB; pass a smaller q_chunk", pl.qc, pl.mp);
     if ((e = plan_resnet(d->mid[1], "mid.1", c, cp, M, pl))) return e;
     for (int s = 0; s < d->n_up; ++s) {
@@ -173,11 +175,18 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     pl.off_q = take(mp * C * 2);
     pl.off_k = take(mp * C * 2);
     pl.off_vt = take(C * mp * 2);
-    pl.off_o = take(mp * C * 4);
-    // per-row partial softmax statistics of a query chunk, then the rows'
-    // final (max, 1 / sum)
-    pl.off_s = take((qc * gemm2_stat_parts((int)mp) * 2 + qc * 2) * 4);
-    pl.off_p = take(qc * mp * 2);
+    if (pl.flash) {
+        // the single-pass kernel's key-range partials (if any)
+        pl.off_o = take(0);
+        pl.off_s = take(flash_workspace_bytes(pl.m));
+        pl.off_p = take(0);
+    } else {
+        pl.off_o = take(mp * C * 4);
+        // per-row partial softmax statistics of a query chunk, then the
+        // rows' final (max, 1 / sum)
+        pl.off_s = take((qc * gemm2_stat_parts((int)mp) * 2 + qc * 2) * 4);
+        pl.off_p = take(qc * mp * 2);
+    }
     pl.total = o;
     return IG_OK;
 }
@@ -299,6 +308,21 @@ struct Run {
         gemm(xn, mp, C, C, wk, C, C, a.k.b, 1.f, k16, C, 1, 0);
         // V^T [C][mp] = Wv . xn^T; V's bias comes after P.V (P's rows sum to 1)
         gemm(wv, C, C, C, xn, mp, C, nullptr, 1.f, vt16, mp, 1, 0);
+        if (pl.flash) {
+            // one pass over the keys, f16(O + bv) straight into xn
+            FlashArgs f{};
+            f.q = q16;
+            f.k = k16;
+            f.vt = vt16;
+            f.ld = mp;
+            f.m = m;
+            f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)C));
+            f.bv = a.v.b;
+            f.out = xn;
+            launch_flash(f, S, s);
+            gemm(xn, m, C, C, wp, C, C, a.proj.b, 1.f, x, C, 0, 1);
+            return;
+        }
         const float scale = 1.0f / sqrtf((float)C);
         // per chunk: the scores' row statistics, then P, never storing the
         // scores themselves; then O = P.V

@@ -202,6 +202,29 @@ int ig_combine(float *x, const float *h, const float *hb, const float *s, const 
 int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols, uint16_t *P,
                         int ldp, void *stream);
 
+/* ---------------------------------------------------------------------
+ * The mid attention's core in one pass over the keys ([QI] `attention`:
+ * S = q.k^T / sqrt(C), row softmax, O = P.V, V's bias after the product;
+ * [VAE] `AttnBlock::apply`: max-subtracted softmax):
+ *   out[i][c] = f16( sum_{j<m} softmax_j(q_i . k_j / sqrt(C)) vt[c][j] + bv[c] )
+ * The softmax is taken online over blocks of 32 keys (a running max and
+ * sum per query); no score or probability matrix is stored. Each block's
+ * weights are rounded to f16 relative to the running max (the chunked
+ * path rounds the normalised probabilities instead), so the two agree
+ * to f16 rounding, not bit for bit.
+ *   q, k: f16 [ld][C] row-major; rows m..ld-1 are read, never used.
+ *   vt:   f16 V^T [C][ld].
+ *   bv:   f32 [C] or NULL.      out: f16 [m][C].
+ *   ws:   device scratch of ws_bytes >= ig_attention_workspace_bytes(m, C)
+ *         (0 bytes for small m: ws may then be NULL); its contents on
+ *         entry do not matter.
+ * C must be 512 (IG_EUNSUPPORTED otherwise); ld >= m rounded up to 32,
+ * ld % 8 == 0; q, k, vt, out 16-byte aligned. m < 2^22.
+ * --------------------------------------------------------------------- */
+size_t ig_attention_workspace_bytes(int m, int C);
+int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int m, int ld, int C,
+                  const float *bv, void *ws, size_t ws_bytes, uint16_t *out, void *stream);
+
 /* Latent ingest ([QI] `decode`: the NCHW latent becomes an NHWC f16 conv
  * input): y[p][c] = f16(z[c][p]) for c < zc, 0 for zc <= c < cp.
  *   z: f32 [zc][M]; y: f16 [M][cp]. */
@@ -289,8 +312,11 @@ typedef struct ig_decoder {
     ig_conv_w conv_out;          /* 3x3 c -> out channels (<= 64) */
 } ig_decoder;
 
-/* Workspace bytes decoder_forward needs for an h0 x w0 latent with query
- * chunks of q_chunk rows (q_chunk <= 0: the library's default). Returns 0
+/* Workspace bytes decoder_forward needs for an h0 x w0 latent. q_chunk
+ * selects the attention: q_chunk <= 0 takes the single-pass kernel of
+ * attention_f16 when the attention width is 512 (else query chunks of
+ * 16384 rows); q_chunk > 0 takes the chunked path (scores' row statistics,
+ * then P, then P.V) over chunks of q_chunk query rows. Returns 0
  * if the descriptor or the sizes are invalid (see ig_last_error()). */
 size_t ig_decoder_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_chunk);
 

@@ -258,6 +258,22 @@ def softmax_rows(s):
     return e / e.sum(axis=1, keepdims=True)
 
 
+def attention_core(q, k, vt, bv=None):
+    """The attention's core as its plain definition (qi21_vae.rs,
+    `attention`; vae.rs, `AttnBlock::apply`): S = q k^T / sqrt(C) with
+    q, k [m, C] and V^T [C, m]; P = softmax over the keys (max-subtracted);
+    O = P V (+ bv). float64 throughout, no rounding of P: the reference
+    both the chunked and the single-pass kernels are measured against.
+    Returns (O [m, C], P [m, m])."""
+    q, k, vt = _f64(q), _f64(k), _f64(vt)
+    C = q.shape[1]
+    p = softmax_rows(np.matmul(q, k.T) / np.sqrt(C))
+    o = np.matmul(p, vt.T)
+    if bv is not None:
+        o = o + _f64(bv)
+    return o, p
+
+
 def attention(x, a, q_chunk=None, emulate_f16=True):
     """The mid attention on the stream x [C, m] (qi21_vae.rs, `attention`;
     vae.rs, `AttnBlock::apply`): xn = f16(RMS_norm(x; gamma_a)) (no SiLU);

@@ -64,6 +64,16 @@ def test_config4_decode_256(full_decoder):
     assert _report("config4 256^2", got, ref) >= PSNR_MIN
 
 
+def test_config4_decode_256_single_pass_attention(full_decoder):
+    w, dd = full_decoder
+    z = synth.decoder_latent(32, 32, config=4)
+    got = _run(dd, z, q_chunk=0)
+    ref = O.decode(w, z, guard_log2=8, q_chunk=256)
+    assert _report("config4 256^2, single-pass attention", got, ref) >= PSNR_MIN
+    chunked = _run(dd, z, q_chunk=256)
+    assert _report("single-pass vs chunked attention", got, chunked) >= PSNR_MIN
+
+
 def test_decode_query_chunks_agree(full_decoder):
     _, dd = full_decoder
     z = synth.decoder_latent(32, 32, config=4)
@@ -114,18 +124,19 @@ def _load_golden(size):
         return mg, {k: g[k] for k in g.files}
 
 
-@pytest.mark.parametrize("size", [1024, 2048])
-def test_full_size_decode_against_stored_oracle_rows(size):
-    """The full-size decode, launched as the benchmark launches it (default
-    query chunk, guard 8, latent N(0,1)*8, conv_in gain 2^11), against the
-    oracle's stored rows: u8 PSNR >= 60 dB over every sampled row, plus the
-    float rows' max |d| relative to their RMS (reported)."""
+@pytest.mark.parametrize("size,q_chunk", [(1024, 0), (1024, 16384), (2048, 0)])
+def test_full_size_decode_against_stored_oracle_rows(size, q_chunk):
+    """The full-size decode, launched as the benchmark launches it (guard 8,
+    latent N(0,1)*8, conv_in gain 2^11; q_chunk 0 = the single-pass
+    attention, > 0 = the chunked path), against the oracle's stored rows:
+    u8 PSNR >= 60 dB over every sampled row, plus the float rows' max |d|
+    relative to their RMS (reported)."""
     mg, g = _load_golden(size)
     w, z = mg.inputs(size)
     assert float(np.max(g["guard_max"])) > 65504.0  # the guard is exercised
     dd = ig.DeviceDecoder(w)
     h0 = size // 8
-    out = dd.forward(dev(z), h0, h0, guard_log2=mg.GUARD_LOG2, q_chunk=0)
+    out = dd.forward(dev(z), h0, h0, guard_log2=mg.GUARD_LOG2, q_chunk=q_chunk)
     rows = torch.from_numpy(g["rows"].astype(np.int64)).cuda()
     frows = torch.from_numpy(g["frows"].astype(np.int64)).cuda()
     got_rows = host(out.index_select(1, rows))
@@ -140,8 +151,8 @@ def test_full_size_decode_against_stored_oracle_rows(size):
     unclipped = np.abs(ref_f) <= 1.0
     p_unclipped = O.psnr_u8(got_f[unclipped], ref_f[unclipped])
     rel = float(np.max(np.abs(got_f - ref_f)) / np.sqrt(np.mean(ref_f ** 2)))
-    print("%d^2: sampled-row PSNR %.2f dB (unclipped float rows %.2f dB), max|d|/RMS %.3e, "
-          "u8 levels off: %d of %d" % (size, p, p_unclipped, rel, int(np.count_nonzero(d)), d.size),
+    print("%d^2 (q_chunk %d): sampled-row PSNR %.2f dB (unclipped float rows %.2f dB), max|d|/RMS %.3e, "
+          "u8 levels off: %d of %d" % (size, q_chunk, p, p_unclipped, rel, int(np.count_nonzero(d)), d.size),
           flush=True)
     assert p >= PSNR_MIN
     assert p_unclipped >= PSNR_MIN

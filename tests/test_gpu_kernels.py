@@ -517,3 +517,119 @@ def test_rejected_call_leaves_output_untouched():
         ig.conv3x3_nhwc(x, 4, 4, 100, w, 64, None, 1.0, y)
     assert e.value.code == -2
     assert torch.isnan(y).all()
+
+
+# ---------------------------------------------------------------------------
+# the single-pass attention core
+# ---------------------------------------------------------------------------
+
+
+def _attn_inputs(m, kind, seed):
+    """q, k [m][512], V^T [512][m], bv: f16 operands with the decoder's
+    scale (entries ~ N(0, 1): scores q.k / sqrt(512) ~ N(0, 1)).
+    kind: 'flat'; 'growing' (key norms grow along the sequence, so the
+    running max is raised block after block); 'self' (k = q: each query's
+    own key dominates by ~22 in the exponent)."""
+    C = 512
+    q = synth.normal(7, seed, (m, C), 1.0, np.float16)
+    k = synth.normal(7, seed + 1, (m, C), 1.0, np.float16)
+    v = synth.normal(7, seed + 2, (m, C), 1.0, np.float16)
+    bv = synth.normal(7, seed + 3, (C,), 0.02, np.float32)
+    if kind == "growing":
+        k = (k.astype(np.float64) * np.linspace(0.5, 6.0, m)[:, None]).astype(np.float16)
+    elif kind == "self":
+        k = q.copy()
+    return q, k, np.ascontiguousarray(v.T), bv
+
+
+def _attn_tol(o_ref, p, vt):
+    """Per-element bound: f16 rounding of the output (half an ulp, 2^-11
+    relative) and of every weight (2^-11 relative, the weights' f16 grid
+    relative to a running max or to the row sum), each doubled, plus f32
+    accumulation slack."""
+    pv = np.matmul(p, np.abs(vt.astype(np.float64)).T)
+    return 2.0 ** -10 * (np.abs(o_ref) + pv) + 1e-6
+
+
+def _run_flash(q, k, vt, bv, ld=None):
+    m, C = q.shape
+    ld = ld or (m + 63) // 64 * 64
+    qd = torch.zeros((ld, C), dtype=torch.float16, device="cuda")
+    kd = torch.zeros((ld, C), dtype=torch.float16, device="cuda")
+    vd = torch.zeros((C, ld), dtype=torch.float16, device="cuda")
+    qd[:m] = dev(q)
+    kd[:m] = dev(k)
+    vd[:, :m] = dev(vt)
+    nb = ig.attention_workspace_bytes(m, C)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    out = nan_f16((m, C))
+    ig.attention_f16(qd, kd, vd, m, ld, C, dev(bv), ws, nb, out)
+    torch.cuda.synchronize()
+    return host(out).astype(np.float64)
+
+
+def _check_attn(got_rows, q_rows, k, vt, bv, tag):
+    o, p = O.attention_core(q_rows, k, vt, bv)
+    tol = _attn_tol(o, p, vt)
+    err = np.abs(got_rows - o)
+    rms = float(np.sqrt(np.mean(o ** 2)))
+    print("%s: max|d| %.3e (RMS %.3e, max|d|/RMS %.2e), worst err/tol %.3f" % (
+        tag, float(err.max()), rms, float(err.max()) / rms, float((err / tol).max())), flush=True)
+    assert np.all(np.isfinite(got_rows))
+    assert np.all(err <= tol)
+
+
+@pytest.mark.parametrize("m,kind", [(1, "flat"), (100, "flat"), (1024, "flat"), (1500, "growing"),
+                                    (4096, "self"), (2000, "self")])
+def test_attention_single_pass(m, kind):
+    q, k, vt, bv = _attn_inputs(m, kind, seed=10 + m % 7)
+    got = _run_flash(q, k, vt, bv)
+    rows = np.arange(m) if m <= 2048 else np.unique(np.r_[0:64, m - 64:m, np.linspace(0, m - 1, 128).astype(int)])
+    _check_attn(got[rows], q[rows], k, vt, bv, "attention m=%d %s" % (m, kind))
+
+
+@pytest.mark.parametrize("m", [16384, 40000])
+def test_attention_single_pass_large(m):
+    """16384 = the 1024^2 decode's tokens (two key ranges merged); 40000
+    runs as one key range per workgroup (no merge)."""
+    q, k, vt, bv = _attn_inputs(m, "flat", seed=3)
+    got = _run_flash(q, k, vt, bv)
+    rows = np.unique(np.r_[0:32, m - 32:m, np.linspace(0, m - 1, 64).astype(int)])
+    _check_attn(got[rows], q[rows], k, vt, bv, "attention m=%d" % m)
+
+
+def test_attention_chunked_path_meets_the_same_bound():
+    """The chunked path (statistics GEMM, row merge, probabilities GEMM,
+    P.V) through the decoder's kernels: the same per-element bound against
+    the plain definition."""
+    m, C = 1000, 512
+    q, k, vt, bv = _attn_inputs(m, "growing", seed=21)
+    mp = 1024
+    qd = torch.zeros((mp, C), dtype=torch.float16, device="cuda")
+    kd = torch.zeros((mp, C), dtype=torch.float16, device="cuda")
+    vd = torch.zeros((C, mp), dtype=torch.float16, device="cuda")
+    qd[:m], kd[:m], vd[:, :m] = dev(q), dev(k), dev(vt)
+    S = nan_f32((m, mp))
+    ig.gemm1x1(qd, m, C, C, kd, mp, C, None, 1.0 / np.sqrt(C), S, mp, 0)
+    P = torch.zeros((m, mp), dtype=torch.float16, device="cuda")
+    ig.softmax_rows_f16(S, m, mp, m, mp, P, mp)
+    o32 = nan_f32((m, C))
+    ig.gemm1x1(P, m, mp, mp, vd, C, mp, None, 1.0, o32, C, 0)
+    out = nan_f16((m, C))
+    ig.guard_cast(o32, m, C, dev(bv), 0, out)
+    _check_attn(host(out).astype(np.float64), q, k, vt, bv, "chunked m=%d" % m)
+
+
+def test_attention_rejects_other_widths_and_short_workspace():
+    with pytest.raises(ig.IgError) as e:
+        ig.attention_f16(None, None, None, 64, 64, 256, None, None, 0, None)
+    assert e.value.code == -2
+    m = 16384
+    need = ig.attention_workspace_bytes(m, 512)
+    assert need > 0
+    q = torch.zeros((m, 512), dtype=torch.float16, device="cuda")
+    out = nan_f16((m, 512))
+    with pytest.raises(ig.IgError) as e:
+        ig.attention_f16(q, q, q, m, m, 512, None, None, 0, out)
+    assert e.value.code == -3
+    assert torch.isnan(out).all()

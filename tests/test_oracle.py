@@ -378,6 +378,46 @@ def test_attention_query_chunks_change_nothing():
         assert np.allclose(O.attention(x, a, q_chunk=ch), ref, rtol=0, atol=1e-13)
 
 
+def test_attention_core_matches_torch_sdpa():
+    g = np.random.default_rng(17)
+    m, c = 37, 24
+    q, k = g.standard_normal((m, c)) * 2, g.standard_normal((m, c)) * 2
+    v = g.standard_normal((m, c))
+    bv = g.standard_normal(c)
+    o, p = O.attention_core(q, k, v.T, bv)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(t)[None] for t in (q, k, v)))[0].numpy() + bv
+    assert np.max(np.abs(o - ref)) <= 1e-13 * np.max(np.abs(ref))
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+
+
+def test_attention_core_closed_forms():
+    g = np.random.default_rng(18)
+    m, c = 20, 8
+    v = g.standard_normal((m, c))
+    # identical keys: uniform weights, O = the mean of the V rows
+    k = np.tile(g.standard_normal(c), (m, 1))
+    o, p = O.attention_core(g.standard_normal((m, c)), k, v.T)
+    assert np.allclose(o, np.tile(v.mean(axis=0), (m, 1)), rtol=0, atol=1e-14)
+    # one key: O = V
+    o1, _ = O.attention_core(g.standard_normal((1, c)), g.standard_normal((1, c)), v[:1].T)
+    assert np.allclose(o1[0], v[0], rtol=0, atol=1e-15)
+    # a dominant key (scores 60 apart after the scale): O is that key's row
+    q = np.zeros((m, c))
+    q[:, 0] = 1.0
+    k = np.zeros((m, c))
+    k[:, 0] = np.arange(m) * (60.0 * np.sqrt(c))
+    o, _ = O.attention_core(q, k, v.T)
+    assert np.allclose(o, np.tile(v[-1], (m, 1)), rtol=0, atol=1e-20 + 1e-12)
+    # a common shift of the scores changes nothing (q gains a component
+    # along a direction all keys share)
+    q = g.standard_normal((m, c))
+    k = g.standard_normal((m, c))
+    k[:, -1] = 1.0
+    q2 = q.copy()
+    q2[:, -1] += 7.0
+    assert np.allclose(O.attention_core(q2, k, v.T)[0], O.attention_core(q, k, v.T)[0], rtol=1e-12, atol=1e-13)
+
+
 def test_softmax_rows_sum_to_one_and_shift_invariant():
     s = np.random.default_rng(16).standard_normal((5, 9)) * 20
     p = O.softmax_rows(s)
