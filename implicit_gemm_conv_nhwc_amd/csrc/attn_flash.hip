@@ -6,9 +6,10 @@
 // after the product; page "cortiq-engine 0.7.6, src/vae.rs",
 // `AttnBlock::apply`, for the max-subtracted softmax. The pages store S
 // (and P) per query chunk; here neither leaves the chip: the row softmax
-// is taken online (Milakov and Gimelshein's running max and sum, as in
-// FlashAttention), each key block's scores turning into f16 weights in
-// registers that feed the P.V product directly.
+// is accumulated block by block (the sums of exp(s - ref) and of the
+// weighted V rows, normalised at the end, as in Milakov and Gimelshein's
+// online softmax and FlashAttention), each key block's scores turning into
+// f16 weights in registers that feed the P.V product directly.
 //
 // Design:
 //  * a workgroup of 4 wave64s (one per SIMD) owns 128 queries, a wave 32 of
@@ -21,19 +22,30 @@
 //  * scores are computed transposed, S^T = K . Q^T (keys as MFMA rows), and
 //    the output as O^T = V^T . P^T: a lane then holds one query's scores
 //    and one query's output columns, so the softmax needs no cross-lane
-//    traffic beyond the lane pair sharing a query, and a rescale is a
-//    per-lane multiply. MFMA row r reads key r with bits 2 and 3 swapped,
+//    traffic beyond the lane pair sharing a query. MFMA row r reads key r
+//    with bits 2 and 3 swapped,
 //    which puts each lane's 16 scores in the key order of the P.V
 //    operand (8 consecutive keys per K step);
-//  * the running max is raised only when a block's max exceeds it by more
-//    than 2^8 in the exponential: the weights then stay <= 256 (exact in
-//    f16's range) and the rescale of the 256 output registers is rare;
-//  * LDS rows are swizzled (K: 16-byte unit u of key row k at u ^ (k & 15);
-//    V^T: unit u of column c at u ^ ((c >> 2) & 3)) so every fragment read
-//    touches 16 distinct bank groups per pass;
+//  * the weights are taken relative to a reference max per query fixed for
+//    the whole pass (the first key block's max) rather than a running max,
+//    so the 256 output registers are never rescaled inside the loop: a
+//    weight is at most 2^15, within f16's range, unless a later block's max
+//    exceeds the reference by more than that; then the workgroup runs a
+//    second pass with the range's true max as the reference;
+//  * software pipeline: an iteration computes block b's scores, then runs
+//    block b - 1's P.V product while it turns block b's scores into
+//    weights, so the softmax's VALU work overlaps the MFMAs of a single
+//    wave per SIMD; the score MFMAs are inline asm with the accumulator
+//    pinned to VGPRs, keeping every AGPR for the output;
+//  * K rows are padded to 65 units of 16 bytes in LDS and V^T units are
+//    swizzled (unit u of column c at u ^ ((c >> 2) & 3)), so every fragment
+//    read touches 16 distinct bank groups per pass;
 //  * when the queries alone give fewer workgroups than the chip has CUs,
 //    the keys are split into ranges whose partial (max, sum, O) are merged
-//    by a second kernel.
+//    by a second kernel;
+//  * the direct-to-LDS loads are issued as asm one per two score MFMAs:
+//    a vector-memory issue holds up the single wave of its SIMD for a
+//    while, and next to an MFMA that time is hidden.
 #include <math.h>
 
 #include "ig_internal.h"
@@ -55,10 +67,12 @@ constexpr int BK = 32;             // keys per block
 constexpr int KS = C / 16;         // K steps of the score product
 constexpr int CT = C / 32;         // output column tiles
 constexpr int KU = BK * C / 8;     // 16-byte units of a K block (2048)
+constexpr int KROW = C / 8 + 1;    // LDS units per K row: 64 + 1 of padding
+constexpr int KBUF = BK * KROW;    // LDS units per K buffer
 constexpr int VU = C * BK / 8;     // units of a V^T block (2048)
-constexpr int STAGE = KU + VU;     // 64 KB
 constexpr int LPW = KU / 64 / 4;   // loads per wave per block, K and V^T each (8)
-constexpr float kHeadroom = 8.f;   // log2 of the largest weight before a rescale
+constexpr int PD = 3;             // fragment reads in flight ahead of the MFMAs
+constexpr float kHeadroom = 15.f;  // log2 of the largest weight (f16 holds up to 2^16)
 constexpr float kNegBig = -1e30f;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -66,34 +80,60 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
+// A buffer descriptor as four SGPRs (raw buffer: stride 0, num_records
+// bytes, the same flags as make_rsrc), for the asm loads below.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// A 16-byte-per-lane direct-to-LDS buffer load written as asm: the loads
+// stream the next blocks into LDS while the current ones are read, and the
+// kernel orders them itself (s_waitcnt vmcnt(0) and a barrier before a
+// block is read). Seen as builtins, every LDS read after such a load would
+// get a wait for it.
+__device__ __forceinline__ void dma16(i32x4 rsrc, const void *lds_dst, int voff, int soff)
+{
+    const unsigned addr = (unsigned)(uintptr_t)lds_dst;
+    unsigned saved;
+    // M0 holds the LDS address; its previous value is restored
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(__builtin_amdgcn_readfirstlane(addr)), "v"(voff), "s"(rsrc),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory");
+}
+
 // MFMA row -> key within a block: bits 2 and 3 swapped
 __device__ __forceinline__ int key_of_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// o *= alpha in place in the accumulation registers (rare: when a running
-// max is raised). The products are written through VALU copies; the waits
-// cover the MFMA results being read and the rewritten registers feeding
-// the next MFMAs.
-__device__ __forceinline__ void rescale(f32x16 (&o)[CT], float alpha)
+// The score accumulation runs as inline-asm MFMAs whose accumulator is
+// pinned to VGPRs, so the 256 output accumulators keep the AGPRs to
+// themselves. A chain's MFMAs read their predecessor's result as SrcC with
+// the same registers (no wait states needed); the first starts from zero
+// (no SrcC read); the last pads 16 wait states so the VALU may read its
+// result right after.
+__device__ __forceinline__ void mfma_first(f32x16 &acc, half8 a, half8 b)
 {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float x = o[c][i], t;
-            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                         : "+a"(x), "=&v"(t)
-                         : "v"(alpha));
-            o[c][i] = x;
-        }
-    }
-    asm volatile("s_nop 7" ::: "memory");
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16 &acc, half8 a, half8 b)
+{
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_last(f32x16 &acc, half8 a, half8 b)
+{
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_flash(FlashArgs p)
 {
-    __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) u32x4 lds[2 * (KBUF + VU)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -114,8 +154,8 @@ void k_flash(FlashArgs p)
     const int q0 = qb * BQ + wave * 32;
 
     const __amdgpu_buffer_rsrc_t q_src = make_rsrc(p.q, (uint32_t)((uint64_t)p.ld * C * 2));
-    const __amdgpu_buffer_rsrc_t k_src = make_rsrc(p.k, (uint32_t)((uint64_t)p.ld * C * 2));
-    const __amdgpu_buffer_rsrc_t v_src = make_rsrc(p.vt, (uint32_t)((uint64_t)C * p.ld * 2));
+    const i32x4 k_src = sgpr_rsrc(p.k, (uint32_t)((uint64_t)p.ld * C * 2));
+    const i32x4 v_src = sgpr_rsrc(p.vt, (uint32_t)((uint64_t)C * p.ld * 2));
 
     // this wave's queries: lane (r, h) holds q[q0 + r][16 s + 8 h .. + 7]
     half8 qf[KS];
@@ -124,136 +164,182 @@ void k_flash(FlashArgs p)
         qf[s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
                                               q_src, ((q0 + r) * C + 16 * s + 8 * h) * 2, 0, 0));
 
-    // loads: the wave's i-th K load fills LDS key row kr = wave + 4 i (one
-    // row = 64 units, lane = stored unit); its i-th V^T load fills columns
-    // 16 kc .. 16 kc + 15 (kc = wave + 4 i), 4 units each
-    auto issue = [&](int blk, int buf) __attribute__((always_inline)) {
-        u32x4 *base = lds + buf * STAGE;
-        const int kbase = blk * BK * C * 2;  // bytes
-        const int vbase = blk * BK * 2;
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int kr = wave + 4 * i;
-            const int u = lane ^ (kr & 15);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(k_src, (lds_void *)(base + kr * 64), 16,
-                                                     (kr * C + 8 * u) * 2, kbase, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int kc = wave + 4 * i;
-            const int c = 16 * kc + (lane >> 2);
-            const int u = (lane & 3) ^ ((c >> 2) & 3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(v_src, (lds_void *)(base + KU + kc * 64), 16,
-                                                     c * p.ld * 2 + 16 * u, vbase, 0, 0);
-        }
+    // LDS: two K buffers (key rows KROW units apart), then two V^T
+    // buffers. The wave's i-th K load fills key row kr = wave + 4 i (64
+    // units from the lane's 16 bytes); its i-th V^T load fills columns
+    // 16 kc .. 16 kc + 15 (kc = wave + 4 i), 4 units each, unit u of column
+    // c at u ^ ((c >> 2) & 3). Per-lane source offsets are fixed; the load
+    // index and the block move the scalar offset.
+    u32x4 *const ldv = lds + 2 * KBUF;
+    const int kvoff = 16 * lane;
+    const int vvoff = (16 * wave + (lane >> 2)) * p.ld * 2 + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+    auto issue_k = [&](int blk, int kbuf, int i) __attribute__((always_inline)) {
+        const int kr = wave + 4 * i;
+        dma16(k_src, lds + kbuf * KBUF + kr * KROW, kvoff, (blk * BK + kr) * C * 2);
+    };
+    auto issue_v = [&](int blk, int vbuf, int i) __attribute__((always_inline)) {
+        dma16(v_src, ldv + vbuf * VU + (wave + 4 * i) * 64, vvoff, i * 64 * p.ld * 2 + blk * BK * 2);
     };
 
-    // fragment read offsets (units): K step s = 8 a + b reads unit
-    // krow * 64 + ((2 s + h) ^ (krow & 15)) = krow * 64 + 16 a + ((2 b + h) ^ (krow & 15))
-    const int krow = key_of_row(r);
-    int koff[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) koff[b] = krow * 64 + ((2 * b + h) ^ (krow & 15));
-    // V^T tile ct, K step t: column 32 ct + r, unit (2 t + h) ^ ((r >> 2) & 3)
+    // fragment reads (units): K step s of MFMA row r reads key row
+    // key_of_row(r), unit 2 s + h: with the padded rows, 16 consecutive
+    // lanes hit 16 distinct bank groups. V^T tile ct, K step t: column
+    // 32 ct + r, unit (2 t + h) ^ ((r >> 2) & 3)
+    const int krd = key_of_row(r) * KROW + h;
     int voff[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) voff[t] = KU + 4 * r + ((2 * t + h) ^ ((r >> 2) & 3));
+    for (int t = 0; t < 2; ++t) voff[t] = 4 * r + ((2 * t + h) ^ ((r >> 2) & 3));
 
+    const float sl2 = p.scale_log2;
+    float ref = kNegBig, mtrue = kNegBig, bmax = kNegBig;
+    bool over = false;
+
+    // One pass over the key range: the pipeline below, then the epilogue.
+    // Returns true (writing nothing) when the first pass must be redone.
+    auto run = [&](const bool first) __attribute__((always_inline)) -> bool {
     f32x16 o[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) o[c] = f32x16{};
-    float mrun = kNegBig, lsum = 0.f;
-    const float sl2 = p.scale_log2;
+    float lsum = 0.f;
 
-    if (b0 < b1) issue(b0, 0);
-    for (int blk = b0; blk < b1; ++blk) {
-        const int buf = (blk - b0) & 1;
+    // S^T of one block from K buffer kbuf, with hook(st) run after the MFMA
+    // of K step st. Fragments are read PD steps ahead into a ring of
+    // PD + 1; the scheduling barriers keep the reads from being hoisted
+    // further (which would exhaust the registers).
+    auto s_phase = [&](int kbuf, f32x16 &sacc, auto &&hook) __attribute__((always_inline)) {
+        const u32x4 *sk = lds + kbuf * KBUF;
+        half8 kf[PD + 1];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) kf[i] = __builtin_bit_cast(half8, sk[krd + 2 * i]);
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            if (st + PD < KS) {
+                const int s2 = st + PD;
+                kf[s2 % (PD + 1)] = __builtin_bit_cast(half8, sk[krd + 2 * s2]);
+            }
+            const half8 a = kf[st % (PD + 1)];
+            if (st == 0)
+                mfma_first(sacc, a, qf[0]);
+            else if (st + 1 < KS)
+                mfma_acc(sacc, a, qf[st]);
+            else
+                mfma_last(sacc, a, qf[st]);
+            hook(st);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // O^T += V^T . P^T from V^T buffer vbuf, with hook(g) run before the
+    // products of column tiles 2 g and 2 g + 1. Fragment f = 4 g + i holds
+    // column tile 2 g + (i & 1), K step i >> 1 (a tile's two K steps apart)
+    auto pv_phase = [&](int vbuf, const half8 (&pk)[2], auto &&hook) __attribute__((always_inline)) {
+        const u32x4 *sv = ldv + vbuf * VU;
+        auto vread = [&](int f) __attribute__((always_inline)) {
+            const int i = f & 3, g = f >> 2;
+            return __builtin_bit_cast(half8, sv[voff[i >> 1] + 128 * (2 * g + (i & 1))]);
+        };
+        half8 vf[PD + 1];
+#pragma unroll
+        for (int f = 0; f < PD; ++f) vf[f] = vread(f);
+#pragma unroll
+        for (int f = 0; f < 2 * CT; ++f) {
+            if (f + PD < 2 * CT) vf[(f + PD) % (PD + 1)] = vread(f + PD);
+            const int i = f & 3, g = f >> 2;
+            if (i == 0) hook(g);
+            o[2 * g + (i & 1)] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[f % (PD + 1)], pk[i >> 1],
+                                                                         o[2 * g + (i & 1)], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // softmax step g of a block whose scores are in sacc (lane (r, h)
+    // register j: query q0 + r, key 8 h + j (j < 8) or 16 + 8 h + (j - 8)
+    // of the block), turned in place into log2-domain scores, then into
+    // the weights 2^(t - ref) of the keys below lim. ref is the query's
+    // reference max, fixed for the pass (first: the range's first block's
+    // max); a block whose max exceeds it by more than the headroom marks
+    // the wave for a second pass with ref = the range's max.
+    auto softmax_step = [&](int g, f32x16 &t, int lim, half8 (&pk)[2], bool first) __attribute__((always_inline)) {
+        if (g == 0 || g == 1) {
+#pragma unroll
+            for (int j = 8 * g; j < 8 * g + 8; ++j) t[j] *= sl2;
+            if (g == 1 && lim < BK) {
+                // the sequence's last, partial block: keys >= m weigh 0
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = j < 8 ? 8 * h + j : 16 + 8 * h + (j - 8);
+                    if (key >= lim) t[j] = kNegBig;
+                }
+            }
+        } else if (g == 2) {
+            const float m0 = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+            const float m1 = fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7]));
+            const float m2 = fmaxf(fmaxf(t[8], t[9]), fmaxf(t[10], t[11]));
+            const float m3 = fmaxf(fmaxf(t[12], t[13]), fmaxf(t[14], t[15]));
+            bmax = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+        } else if (g == 3) {
+            const float bm = fmaxf(bmax, __shfl_xor(bmax, 32));
+            if (first) ref = bm;
+            over = over || bm > ref + kHeadroom;
+            mtrue = fmaxf(mtrue, bm);
+        } else if (g == 4 || g == 5) {
+            const int j0 = 8 * (g - 4);
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                w[e] = __builtin_amdgcn_exp2f(t[j0 + e] - ref);
+                pk[g - 4][e] = (_Float16)w[e];
+            }
+            lsum += ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+        }
+    };
+
+    // Pipeline: iteration blk computes block blk's scores (K(blk) in LDS),
+    // then runs block blk - 1's P.V while it turns block blk's scores into
+    // weights. Iteration blk loads K(blk + 1) and V^T(blk); past the
+    // range's end the loads are of a clamped, valid block and never used.
+    // A second pass runs only when a wave of the workgroup saw a block
+    // exceed its reference max by more than the headroom (scores growing
+    // by more than 2^15 in the exponential along the keys).
+    const int last = nblocks - 1;
+    f32x16 sacc;
+    half8 pprev[2], pcur[2];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) issue_k(b0, 0, i);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+        const int nk = b0 + 1 < last ? b0 + 1 : last;
+        s_phase(0, sacc, [&](int st) {
+            if (st % 4 == 1) issue_k(nk, 1, st / 4);
+            if (st % 4 == 3) issue_v(b0, 0, st / 4);
+        });
+#pragma unroll
+        for (int g = 0; g < 6; ++g) softmax_step(g, sacc, p.m - b0 * BK, pprev, first);
+    }
+    for (int blk = b0 + 1; blk < b1; ++blk) {
+        const int cur = (blk - b0) & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (blk + 1 < b1) issue(blk + 1, buf ^ 1);
-        const u32x4 *sb = lds + buf * STAGE;
-
-        // S^T = K . Q^T over the 512 channels, two accumulation chains; the
-        // fragments of the next 4 K steps are read while the current 4 run
-        // (the scheduling barriers keep the reads from being hoisted
-        // further, which would exhaust the registers)
-        f32x16 sa = f32x16{}, sc = f32x16{};
-        {
-            half8 kc[4], kn[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kc[i] = __builtin_bit_cast(half8, sb[koff[i]]);
-#pragma unroll
-            for (int g = 0; g < KS / 4; ++g) {
-                if (g + 1 < KS / 4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s2 = 4 * (g + 1) + i;
-                        kn[i] = __builtin_bit_cast(half8, sb[koff[s2 & 7] + 16 * (s2 >> 3)]);
-                    }
-                }
-                sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kc[0], qf[4 * g], sa, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kc[1], qf[4 * g + 1], sc, 0, 0, 0);
-                sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kc[2], qf[4 * g + 2], sa, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kc[3], qf[4 * g + 3], sc, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) kc[i] = kn[i];
-            }
-        }
-        // lane (r, h) register j: query q0 + r, key 8 h + j (j < 8) or
-        // 16 + 8 h + (j - 8) of the block
-        float t[16];
-        float bm = kNegBig;
-        const int kb = blk * BK;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            t[j] = (sa[j] + sc[j]) * sl2;
-            const int key = kb + (j < 8 ? 8 * h + j : 16 + 8 * h + (j - 8));
-            if (kb + BK > p.m && key >= p.m) t[j] = kNegBig;
-            bm = fmaxf(bm, t[j]);
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const bool raise = bm > mrun + kHeadroom;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-            const float alpha = raise ? __builtin_amdgcn_exp2f(mrun - bm) : 1.f;
-            if (raise) mrun = bm;
-            lsum *= alpha;
-            rescale(o, alpha);
-        }
-        half8 pk[2];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float w = __builtin_amdgcn_exp2f(t[j] - mrun);
-            lsum += w;
-            pk[j >> 3][j & 7] = (_Float16)w;
-        }
-        // O^T += V^T . P^T, two column tiles (4 fragments) at a time
-        {
-            half8 vc[4], vn[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vc[i] = __builtin_bit_cast(half8, sb[voff[i & 1] + 128 * (i >> 1)]);
-#pragma unroll
-            for (int g = 0; g < CT / 2; ++g) {
-                if (g + 1 < CT / 2) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        vn[i] = __builtin_bit_cast(half8, sb[voff[i & 1] + 128 * (2 * (g + 1) + (i >> 1))]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    o[2 * g + (i >> 1)] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_f16(vc[i], pk[i & 1], o[2 * g + (i >> 1)], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vc[i] = vn[i];
-            }
-        }
+        const int nk = blk + 1 < last ? blk + 1 : last;
+        s_phase(cur, sacc, [&](int st) {
+            if (st % 4 == 1) issue_k(nk, cur ^ 1, st / 4);
+            if (st % 4 == 3) issue_v(blk, cur, st / 4);
+        });
+        const int lim = p.m - blk * BK;
+        pv_phase(cur ^ 1, pprev, [&](int g) { softmax_step(g, sacc, lim, pcur, false); });
+        pprev[0] = pcur[0];
+        pprev[1] = pcur[1];
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    pv_phase((b1 - 1 - b0) & 1, pprev, [](int) {});
+    if (first && __syncthreads_or(over)) return true;
 
     // lane (r, h) holds output columns 32 c + 8 (j / 4) + 4 h + j % 4 of query q0 + r
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const int q = q0 + r;
-    if (q >= p.m) return;
+    if (q >= p.m) return false;
     if (p.nsplit == 1) {
         const float inv = 1.f / ltot;
 #pragma unroll
@@ -280,9 +366,20 @@ void k_flash(FlashArgs p)
             }
         }
         if (h == 0) {
-            p.ml[((int64_t)sp * p.m + q) * 2] = mrun;
+            p.ml[((int64_t)sp * p.m + q) * 2] = ref;
             p.ml[((int64_t)sp * p.m + q) * 2 + 1] = ltot;
         }
+    }
+    return false;
+    };
+
+    // A second pass runs only when a wave of the workgroup saw a block
+    // exceed its reference max by more than the headroom (scores growing
+    // by more than 2^15 in the exponential along the keys); it takes the
+    // range's max as the reference.
+    if (run(true)) {
+        ref = mtrue;
+        run(false);
     }
 }
 
