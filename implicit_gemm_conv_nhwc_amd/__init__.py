@@ -20,7 +20,10 @@ from ._lib import (  # noqa: F401
     conv3x3_out_nchw,
     conv3x3_up2_nhwc,
     conv_nhwc_ex,
+    band_plan,
+    decoder_bands_workspace_bytes,
     decoder_forward,
+    decoder_forward_bands,
     decoder_workspace_bytes,
     dupup_add,
     gemm1x1,

@@ -237,6 +237,39 @@ _dec = _sig("decoder_forward", [ctypes.POINTER(DecoderDesc), _vp, _c_int, _c_int
                                 _size_t, _vp, _vp])
 
 
+_bws_bytes = _sig("ig_decoder_bands_workspace_bytes", [ctypes.POINTER(DecoderDesc), _c_int, _c_int, _c_int, _c_int,
+                                                       _c_int], ctypes.c_size_t)
+_dec_bands = _sig("decoder_forward_bands", [ctypes.POINTER(DecoderDesc), _vp, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _vp, ctypes.c_size_t, _vp, _vp])
+_band_plan = _sig("ig_band_plan", [_c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp])
+
+
+def band_plan(n_res, has_up, h0, band_from, keep_lo, keep_hi):
+    """Host-only band planner: ((lo, hi) of block band_from's input rows,
+    [(lo, hi) fed to each block's upsample])."""
+    n = len(n_res)
+    a_res = (ctypes.c_int * max(n, 1))(*n_res)
+    a_up = (ctypes.c_int * max(n, 1))(*[int(bool(u)) for u in has_up])
+    inp = (ctypes.c_int * 2)()
+    feed = (ctypes.c_int * max(2 * n, 1))()
+    _check(_band_plan(n, ctypes.cast(a_res, _vp), ctypes.cast(a_up, _vp), h0, band_from, keep_lo, keep_hi,
+                      ctypes.cast(inp, _vp), ctypes.cast(feed, _vp)))
+    return (inp[0], inp[1]), [(feed[2 * i], feed[2 * i + 1]) for i in range(n)]
+
+
+def decoder_bands_workspace_bytes(desc, h0, w0, q_chunk, band_rows, band_from):
+    n = int(_bws_bytes(ctypes.byref(desc), h0, w0, q_chunk, band_rows, band_from))
+    if n == 0:
+        raise IgError(-1, last_error())
+    return n
+
+
+def decoder_forward_bands(desc, latent, h0, w0, guard_log2, q_chunk, band_rows, band_from, ws, ws_bytes, out,
+                          stream=None):
+    return _check(_dec_bands(ctypes.byref(desc), _ptr(latent), h0, w0, guard_log2, q_chunk, band_rows, band_from,
+                             _ptr(ws), ws_bytes, _ptr(out), _stream(stream)))
+
+
 def decoder_workspace_bytes(desc, h0, w0, q_chunk=0):
     n = _ws_bytes(ctypes.byref(desc), h0, w0, q_chunk)
     if n == 0:

@@ -53,7 +53,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x, int H, int W, int cin_p,
                                                  const _Float16 *__restrict__ plane, int cout, int cout_p,
-                                                 const float *__restrict__ bias, float *__restrict__ out)
+                                                 const float *__restrict__ bias, float *__restrict__ out,
+                                                 int r0, int r1, int64_t HWo)
 {
     __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
 
@@ -128,16 +129,16 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    // lane (grp, col) holds output channels 4 grp + r of pixel column col
-    const int64_t HW = (int64_t)H * W;
+    // lane (grp, col) holds output channels 4 grp + r of pixel column col;
+    // rows r0 .. r1 - 1 are stored, output planes HWo apart
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int oy = y0 + 2 * wave + g / (OW / 16), ox = x0 + 16 * (g % (OW / 16)) + col;
-        if (oy >= H || ox >= W) continue;
+        if (oy < r0 || oy >= r1 || ox >= W) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ch = 4 * grp + r;
-            if (ch < cout) out[ch * HW + (int64_t)oy * W + ox] = acc[g][r] + (bias ? bias[ch] : 0.f);
+            if (ch < cout) out[ch * HWo + (int64_t)oy * W + ox] = acc[g][r] + (bias ? bias[ch] : 0.f);
         }
     }
 }
@@ -145,11 +146,17 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
 }  // namespace
 
 void launch_conv_out(const _Float16 *x, int H, int W, int cin_p, const _Float16 *plane, int cout, int cout_p,
-                     const float *bias, float *out, hipStream_t s)
+                     const float *bias, float *out, hipStream_t s, int r0, int r1, int64_t HWo)
 {
     if (H <= 0 || W <= 0) return;
+    if (r1 < 0) {
+        r0 = 0;
+        r1 = H;
+        HWo = (int64_t)H * W;
+    }
     const int grid = ((H + OH - 1) / OH) * ((W + OW - 1) / OW);
-    hipLaunchKernelGGL(k_conv_out, dim3(grid), dim3(NT), 0, s, x, H, W, cin_p, plane, cout, cout_p, bias, out);
+    hipLaunchKernelGGL(k_conv_out, dim3(grid), dim3(NT), 0, s, x, H, W, cin_p, plane, cout, cout_p, bias, out, r0,
+                       r1, HWo);
 }
 
 }  // namespace ig

@@ -6,8 +6,13 @@
 // -> conv_out).
 //
 // Differences from the pages' recording, chosen for one MI355X:
-//  * the whole frame runs at once (no horizontal bands: the largest tensor
-//    of a 2048^2 decode is 2.1 GB, far inside 288 GB of HBM);
+//  * decoder_forward runs the whole frame at once (the largest tensor of a
+//    2048^2 decode is 2.1 GB, far inside 288 GB of HBM); decoder_forward_bands
+//    runs the up blocks from a chosen one on in horizontal bands with exact
+//    halos, as the pages do to bound memory (page "cortiq-engine 0.8.3,
+//    src/gpu_wgpu/qi21_vae.rs", the bands section, `grow`, `half`,
+//    `plan_band`, `run_blocks`, `output_rows`): its output is bit for bit the
+//    whole-frame decode's;
 //  * the combine passes are folded into conv epilogues: the up conv and
 //    conv_in write x = oscale*acc + b directly, the second conv of a
 //    resnet adds into the stream (x += acc + b2), and a shortcut writes
@@ -30,15 +35,54 @@ constexpr size_t kAlign = 256;
 inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 constexpr float kEps = 1e-12f;
 
+// Rows [lo, hi) of one resolution level of the frame.
+struct Rows {
+    int lo = 0, hi = 0;
+    int n() const { return hi - lo; }
+};
+
+// a 3x3 conv needs k more rows on each side of the rows it must produce,
+// clamped to the frame's h rows (the frame edge is the real zero padding)
+Rows grow(Rows r, int k, int h) { return {r.lo - k > 0 ? r.lo - k : 0, r.hi + k < h ? r.hi + k : h}; }
+// a nearest-2x upsample reads half the rows, rounded outward
+Rows half(Rows r) { return {r.lo / 2, (r.hi + 1) / 2}; }
+
+// Walk back from the kept output rows through conv_out and up blocks
+// s..n_up-1 (each: n_res resnets of two 3x3 convs, then, with has_up, the
+// upsample and its 3x3 conv): the rows of block s's input the band starts
+// from, and the rows of its input each up block feeds to its upsample.
+void plan_band(int n_up, const int *n_res, const int *has_up, int h0, int s, Rows keep, Rows &input, Rows *feed)
+{
+    int lvl[IG_MAX_UP + 1], l = 0;
+    for (int i = 0; i < n_up; ++i) {
+        lvl[i] = l;
+        l += has_up[i] ? 1 : 0;
+    }
+    Rows e = grow(keep, 1, h0 << l);  // conv_out
+    for (int i = n_up - 1; i >= s; --i) {
+        feed[i] = Rows{};
+        if (has_up[i]) {
+            const Rows a = half(grow(e, 1, h0 << (lvl[i] + 1)));
+            feed[i] = a;
+            e = a;
+        }
+        e = grow(e, 2 * n_res[i], h0 << lvl[i]);
+    }
+    input = e;
+}
+
 struct Plan {
-    int64_t max_x = 0;   // f32 stream elements
+    int64_t max_x = 0;   // f32 stream elements (the whole frame's)
+    int64_t max_xb = 0;  // f32 stream elements of a band
     int64_t max_h = 0;   // f32 conv outputs
     int64_t max_xn = 0;  // f16 conv inputs
     int64_t max_xg = 0;  // f16 guarded shortcut input
     int m = 0, mp = 0, C = 0, qc = 0;
     bool flash = false;  // single-pass attention (else query chunks)
     int H = 0, W = 0;    // output frame
-    size_t off_x, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, total;
+    int s = 0;           // up blocks s.. run in bands (s == n_up: none)
+    int band_rows = 0;   // kept output rows per band
+    size_t off_x, off_xb, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, total;
 };
 
 int check_conv_w(const ig_conv_w &c, const char *name, int k)
@@ -63,9 +107,9 @@ inline void upd(int64_t &m, int64_t v)
     if (v > m) m = v;
 }
 
-// Check one resnet against the incoming width (c, cp) and update the plan
-// for M pixels; returns the outgoing width through c, cp.
-int plan_resnet(const ig_resnet_w &r, const char *name, int &c, int &cp, int64_t M, Plan &pl)
+// Check one resnet against the incoming width (c, cp); returns the outgoing
+// width through c, cp.
+int check_resnet(const ig_resnet_w &r, const char *name, int &c, int &cp)
 {
     int e;
     if ((e = check_gamma(r.g1, name)) || (e = check_gamma(r.g2, name))) return e;
@@ -77,21 +121,32 @@ int plan_resnet(const ig_resnet_w &r, const char *name, int &c, int &cp, int64_t
         if ((e = check_conv_w(r.sc, name, 1))) return e;
         if (r.sc.cin != c || r.sc.cin_p != cp || r.sc.cout != r.c2.cout || r.sc.cout_p != r.c2.cout_p)
             return fail(IG_EINVAL, "%s: shortcut must map %d -> %d", name, c, r.c2.cout);
-        upd(pl.max_xg, M * cp);
     } else if (r.c2.cout != c || r.c2.cout_p != cp) {
         return fail(IG_EINVAL, "%s: width changes %d -> %d without a shortcut", name, c, r.c2.cout);
     }
-    upd(pl.max_xn, M * cp);
-    upd(pl.max_xn, M * r.c1.cout_p);
-    upd(pl.max_h, M * r.c1.cout_p);
-    upd(pl.max_x, M * cp);
-    upd(pl.max_x, M * r.c2.cout_p);
     c = r.c2.cout;
     cp = r.c2.cout_p;
     return IG_OK;
 }
 
-int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
+// the buffers one resnet on M pixels uses; xmax: the stream's maximum
+void size_resnet(const ig_resnet_w &r, int64_t M, int cp, int64_t &xmax, Plan &pl)
+{
+    if (r.has_sc) upd(pl.max_xg, M * cp);
+    upd(pl.max_xn, M * cp);
+    upd(pl.max_xn, M * r.c1.cout_p);
+    upd(pl.max_h, M * r.c1.cout_p);
+    upd(xmax, M * cp);
+    upd(xmax, M * r.c2.cout_p);
+}
+
+// the up blocks' real and padded widths at their inputs and outputs
+struct Widths {
+    int cp_in[IG_MAX_UP], cp_out[IG_MAX_UP];
+};
+
+// Check the whole descriptor; frame sizes to pl.H, pl.W.
+int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
 {
     if (!d) return fail(IG_EINVAL, "decoder descriptor is NULL");
     if (h0 <= 0 || w0 <= 0) return fail(IG_EINVAL, "latent size %dx%d", h0, w0);
@@ -100,13 +155,8 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     int e;
     if ((e = check_conv_w(d->conv_in, "conv_in", 3))) return e;
     if (d->conv_in.cin != d->zc) return fail(IG_EINVAL, "conv_in takes %d channels, latent has %d", d->conv_in.cin, d->zc);
-    int H = h0, W = w0;
-    int64_t M = (int64_t)H * W;
-    upd(pl.max_xn, M * d->conv_in.cin_p);
     int c = d->conv_in.cout, cp = d->conv_in.cout_p;
-    upd(pl.max_x, M * cp);
-    if ((e = plan_resnet(d->mid[0], "mid.0", c, cp, M, pl))) return e;
-    // attention over the M latent pixels at width c (unpadded)
+    if ((e = check_resnet(d->mid[0], "mid.0", c, cp))) return e;
     const ig_attn_w &a = d->attn;
     if ((e = check_gamma(a.gamma, "attn"))) return e;
     const ig_conv_w *aw[4] = {&a.q, &a.k, &a.v, &a.proj};
@@ -117,7 +167,92 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
         if (aw[i]->cin != c || aw[i]->cout != c || aw[i]->cin_p != c || aw[i]->cout_p != c)
             return fail(IG_EINVAL, "%s must map %d -> %d unpadded", an[i], c, c);
     }
-    if (M >= (1LL << 30)) return fail(IG_EUNSUPPORTED, "latent too large for the attention");
+    if ((int64_t)h0 * w0 >= (1LL << 30)) return fail(IG_EUNSUPPORTED, "latent too large for the attention");
+    if ((e = check_resnet(d->mid[1], "mid.1", c, cp))) return e;
+    int64_t H = h0, W = w0;
+    for (int s = 0; s < d->n_up; ++s) {
+        const ig_up_w &u = d->ups[s];
+        if (u.n_res < 0 || u.n_res > IG_MAX_RES) return fail(IG_EINVAL, "ups[%d].n_res=%d", s, u.n_res);
+        wd.cp_in[s] = cp;
+        for (int r = 0; r < u.n_res; ++r) {
+            char nm[32];
+            snprintf(nm, sizeof nm, "ups.%d.res.%d", s, r);
+            if ((e = check_resnet(u.res[r], nm, c, cp))) return e;
+        }
+        if (u.has_up) {
+            char nm[32];
+            snprintf(nm, sizeof nm, "ups.%d.up", s);
+            if ((e = check_conv_w(u.up, nm, 3))) return e;
+            if (u.up.cin != c || u.up.cin_p != cp) return fail(IG_EINVAL, "%s: input %d, stream %d", nm, u.up.cin, c);
+            H *= 2;
+            W *= 2;
+            if (H * W >= (1LL << 31)) return fail(IG_EUNSUPPORTED, "frame too large");
+            c = u.up.cout;
+            cp = u.up.cout_p;
+        }
+        wd.cp_out[s] = cp;
+    }
+    if ((e = check_gamma(d->norm_out_gamma, "norm_out"))) return e;
+    if (d->norm_out_c != c) return fail(IG_EINVAL, "norm_out has %d channels, stream %d", d->norm_out_c, c);
+    if ((e = check_conv_w(d->conv_out, "conv_out", 3))) return e;
+    if (d->conv_out.cin != c || d->conv_out.cin_p != cp) return fail(IG_EINVAL, "conv_out input %d, stream %d", d->conv_out.cin, c);
+    pl.H = (int)H;
+    pl.W = (int)W;
+    return IG_OK;
+}
+
+// Sizes of up blocks s0..s1-1 run on `rows` rows (of W columns) of block
+// s0's input level; feed[i]: the rows block i feeds to its upsample (NULL:
+// all). fin: the output stage follows. xmax: the stream's maximum.
+void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Rows *feed, bool fin, int cp,
+                 int64_t &xmax, Plan &pl)
+{
+    for (int s = s0; s < s1; ++s) {
+        const ig_up_w &u = d.ups[s];
+        const int64_t M = (int64_t)rows * W;
+        upd(xmax, M * cp);
+        for (int r = 0; r < u.n_res; ++r) {
+            size_resnet(u.res[r], M, cp, xmax, pl);
+            cp = u.res[r].c2.cout_p;
+        }
+        if (u.has_up) {
+            const int fr = feed ? feed[s].n() : rows;
+            upd(pl.max_xn, (int64_t)fr * W * cp);
+            upd(pl.max_xg, (int64_t)fr * W * cp);
+            rows = 2 * fr;
+            W *= 2;
+            cp = u.up.cout_p;
+            upd(xmax, (int64_t)rows * W * cp);
+        }
+    }
+    if (fin) {
+        const int64_t M = (int64_t)rows * W;
+        upd(pl.max_xn, M * cp);
+        if (d.conv_out.cout > 16) upd(pl.max_h, M * d.conv_out.cout_p);  // else straight to the frame
+    }
+}
+
+void band_structure(const ig_decoder &d, int *n_res, int *has_up)
+{
+    for (int i = 0; i < d.n_up; ++i) {
+        n_res[i] = d.ups[i].n_res;
+        has_up[i] = d.ups[i].has_up;
+    }
+}
+
+int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, int band_from, Plan &pl)
+{
+    Widths wd;
+    int e = check_decoder(d, h0, w0, wd, pl);
+    if (e) return e;
+    pl.s = (band_rows > 0 && band_from >= 0 && band_from < d->n_up) ? band_from : d->n_up;
+    pl.band_rows = pl.s < d->n_up ? band_rows : 0;
+    // the head (conv_in, mid block, attention) at the latent resolution
+    int64_t M = (int64_t)h0 * w0;
+    const int c = d->mid[0].c2.cout;
+    upd(pl.max_xn, M * d->conv_in.cin_p);
+    upd(pl.max_x, M * d->conv_in.cout_p);
+    size_resnet(d->mid[0], M, d->conv_in.cout_p, pl.max_x, pl);
     pl.m = (int)M;
     pl.mp = (int)((M + 63) / 64 * 64);
     pl.C = c;
@@ -127,39 +262,22 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     upd(pl.max_xn, (int64_t)pl.mp * c);
     if (!pl.flash && (uint64_t)pl.qc * pl.mp * 2 >= (3ULL << 30))
         return fail(IG_EUNSUPPORTED, "query chunk %d x %d keys: probabilities exceed 3 GiB; pass a smaller q_chunk", pl.qc, pl.mp);
-    if ((e = plan_resnet(d->mid[1], "mid.1", c, cp, M, pl))) return e;
-    for (int s = 0; s < d->n_up; ++s) {
-        const ig_up_w &u = d->ups[s];
-        if (u.n_res < 0 || u.n_res > IG_MAX_RES) return fail(IG_EINVAL, "ups[%d].n_res=%d", s, u.n_res);
-        for (int r = 0; r < u.n_res; ++r) {
-            char nm[32];
-            snprintf(nm, sizeof nm, "ups.%d.res.%d", s, r);
-            if ((e = plan_resnet(u.res[r], nm, c, cp, M, pl))) return e;
-        }
-        if (u.has_up) {
-            char nm[32];
-            snprintf(nm, sizeof nm, "ups.%d.up", s);
-            if ((e = check_conv_w(u.up, nm, 3))) return e;
-            if (u.up.cin != c || u.up.cin_p != cp) return fail(IG_EINVAL, "%s: input %d, stream %d", nm, u.up.cin, c);
-            upd(pl.max_xn, M * cp);
-            upd(pl.max_xg, M * cp);
-            H *= 2;
-            W *= 2;
-            M *= 4;
-            if (M >= (1LL << 31)) return fail(IG_EUNSUPPORTED, "frame too large");
-            c = u.up.cout;
-            cp = u.up.cout_p;
-            upd(pl.max_x, M * cp);
+    size_resnet(d->mid[1], M, c, pl.max_x, pl);
+    // up blocks 0..s-1 on the whole frame (and the output when no bands)
+    int lv = 0;
+    for (int i = 0; i < pl.s; ++i) lv += d->ups[i].has_up ? 1 : 0;
+    size_blocks(*d, 0, pl.s, h0, w0, nullptr, pl.s == d->n_up, d->mid[1].c2.cout_p, pl.max_x, pl);
+    if (pl.s < d->n_up) {
+        // every band from block s on; bands of band_rows kept output rows
+        int n_res[IG_MAX_UP], has_up[IG_MAX_UP];
+        band_structure(*d, n_res, has_up);
+        for (int k0 = 0; k0 < pl.H; k0 += pl.band_rows) {
+            const Rows keep{k0, k0 + pl.band_rows < pl.H ? k0 + pl.band_rows : pl.H};
+            Rows input, feed[IG_MAX_UP];
+            plan_band(d->n_up, n_res, has_up, h0, pl.s, keep, input, feed);
+            size_blocks(*d, pl.s, d->n_up, input.n(), w0 << lv, feed, true, wd.cp_in[pl.s], pl.max_xb, pl);
         }
     }
-    if ((e = check_gamma(d->norm_out_gamma, "norm_out"))) return e;
-    if (d->norm_out_c != c) return fail(IG_EINVAL, "norm_out has %d channels, stream %d", d->norm_out_c, c);
-    if ((e = check_conv_w(d->conv_out, "conv_out", 3))) return e;
-    if (d->conv_out.cin != c || d->conv_out.cin_p != cp) return fail(IG_EINVAL, "conv_out input %d, stream %d", d->conv_out.cin, c);
-    upd(pl.max_xn, M * cp);
-    if (d->conv_out.cout > 16) upd(pl.max_h, M * d->conv_out.cout_p);  // else straight to the frame
-    pl.H = H;
-    pl.W = W;
     // layout
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -169,6 +287,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, Plan &pl)
     };
     const int64_t mp = pl.mp, C = pl.C, qc = pl.qc;
     pl.off_x = take(pl.max_x * 4);
+    pl.off_xb = take(pl.max_xb * 4);
     pl.off_h = take(pl.max_h * 4);
     pl.off_xn = take(pl.max_xn * 2);
     pl.off_xg = take(pl.max_xg * 2);
@@ -272,6 +391,62 @@ struct Run {
         launch_igemm(kGemm, a, s);
     }
 
+    // Up blocks s0..s1-1 on the stream x holding rows cur (buffer row 0 =
+    // cur.lo) of W columns and padded width cp ([QI] `run_blocks`); feed[i]:
+    // the rows block i feeds to its upsample (NULL: all). Returns through
+    // cur, W, cp the rows the stream then holds; normed: the last up conv
+    // emitted norm_out's f16 input of conv_out into xn.
+    void blocks(const ig_decoder &d, int s0, int s1, const Rows *feed, Rows &cur, int &W, int &cp, bool &normed)
+    {
+        const float gs = ldexpf(1.f, g);
+        normed = false;
+        for (int st = s0; st < s1; ++st) {
+            const ig_up_w &u = d.ups[st];
+            for (int k = 0; k < u.n_res; ++k) {
+                resnet(u.res[k], cur.n(), W, cp);
+                cp = u.res[k].c2.cout_p;
+            }
+            if (u.has_up) {
+                const Rows f = feed ? feed[st] : cur;
+                const int64_t skip = (int64_t)(f.lo - cur.lo) * W;
+                launch_guard_cast(x + skip * cp, f.n() * W, cp, nullptr, g, xg, s);
+                if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout) {
+                    // the last up conv's epilogue applies norm_out + SiLU; the
+                    // f32 stream is not needed after it
+                    conv_norm(kConv3x3Up2, xg, f.n(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
+                    normed = true;
+                } else {
+                    conv(kConv3x3Up2, xg, f.n(), W, u.up, u.up.b, gs, 0, x);
+                }
+                cur = Rows{2 * f.lo, 2 * f.hi};
+                W *= 2;
+                cp = u.up.cout_p;
+            }
+        }
+    }
+
+    // norm_out + SiLU (unless fused), conv_out on the rows cur of the output
+    // level (W columns), the rows keep of them into the NCHW frame of Hf
+    // rows ([QI] `output_rows`)
+    void output(const ig_decoder &d, Rows cur, int W, int cp, bool normed, Rows keep, int Hf, float *out)
+    {
+        const int H = cur.n();
+        if (!normed) launch_rmsnorm(x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, xn, s);
+        float *o = out + (int64_t)cur.lo * W;
+        const int64_t plane = (int64_t)Hf * W;
+        if (d.conv_out.cout <= 16) {
+            // few output channels: straight into the NCHW frame
+            launch_conv_out(xn, H, W, d.conv_out.cin_p, reinterpret_cast<const _Float16 *>(d.conv_out.w),
+                            d.conv_out.cout, d.conv_out.cout_p, d.conv_out.b, o, s, keep.lo - cur.lo,
+                            keep.hi - cur.lo, plane);
+        } else {
+            conv(kConv3x3, xn, H, W, d.conv_out, d.conv_out.b, 1.f, 0, h);
+            const int64_t r0 = (int64_t)(keep.lo - cur.lo) * W;
+            launch_nhwc_to_nchw(h + r0 * d.conv_out.cout_p, keep.n() * W, d.conv_out.cout_p, d.conv_out.cout,
+                                nullptr, out + (int64_t)keep.lo * W, s, plane);
+        }
+    }
+
     // Rec::resnet with the combines folded into the epilogues
     void resnet(const ig_resnet_w &r, int H, int W, int cp)
     {
@@ -359,22 +534,14 @@ struct Run {
 
 using namespace ig;
 
-extern "C" {
+namespace {
 
-size_t ig_decoder_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_chunk)
+int run_decoder(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2, int q_chunk,
+                int band_rows, int band_from, void *ws, size_t ws_bytes, float *out, void *stream)
 {
     clear_error();
     Plan pl;
-    if (make_plan(dec, h0, w0, q_chunk, pl)) return 0;
-    return pl.total;
-}
-
-int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2,
-                    int q_chunk, void *ws, size_t ws_bytes, float *out, void *stream)
-{
-    clear_error();
-    Plan pl;
-    int e = make_plan(dec, h0, w0, q_chunk, pl);
+    int e = make_plan(dec, h0, w0, q_chunk, band_rows, band_from, pl);
     if (e) return e;
     if (guard_log2 < 0 || guard_log2 > 14) return fail(IG_EINVAL, "guard_log2=%d outside 0..14", guard_log2);
     if (!latent || !out) return fail(IG_EINVAL, "latent or out is NULL");
@@ -390,49 +557,103 @@ int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, 
           reinterpret_cast<_Float16 *>(w + pl.off_vt), reinterpret_cast<_Float16 *>(w + pl.off_p)};
     hipStream_t s = r.s;
     (void)hipGetLastError();
-    int H = h0, W = w0;
     // latent -> f16 NHWC -> conv_in, x = conv + b
-    launch_latent_ingest(latent, d.zc, H * W, d.conv_in.cin_p, r.xn, s);
-    r.conv(kConv3x3, r.xn, H, W, d.conv_in, d.conv_in.b, 1.f, 0, r.x);
-    int cp = d.conv_in.cout_p;
-    r.resnet(d.mid[0], H, W, cp);
-    cp = d.mid[0].c2.cout_p;
+    launch_latent_ingest(latent, d.zc, h0 * w0, d.conv_in.cin_p, r.xn, s);
+    r.conv(kConv3x3, r.xn, h0, w0, d.conv_in, d.conv_in.b, 1.f, 0, r.x);
+    r.resnet(d.mid[0], h0, w0, d.conv_in.cout_p);
     r.attention(d.attn);
-    r.resnet(d.mid[1], H, W, cp);
-    cp = d.mid[1].c2.cout_p;
-    const float gs = ldexpf(1.f, guard_log2);
+    r.resnet(d.mid[1], h0, w0, d.mid[0].c2.cout_p);
+    // up blocks 0..s-1 on the whole frame
+    Rows cur{0, h0};
+    int W = w0, cp = d.mid[1].c2.cout_p;
     bool normed = false;
-    for (int st = 0; st < d.n_up; ++st) {
-        const ig_up_w &u = d.ups[st];
-        for (int k = 0; k < u.n_res; ++k) {
-            r.resnet(u.res[k], H, W, cp);
-            cp = u.res[k].c2.cout_p;
-        }
-        if (u.has_up) {
-            launch_guard_cast(r.x, H * W, cp, nullptr, guard_log2, r.xg, s);
-            if (st == d.n_up - 1 && Run::fusable(u.up) && d.norm_out_c == u.up.cout) {
-                // the last up conv's epilogue applies norm_out + SiLU; the
-                // f32 stream is not needed after it
-                r.conv_norm(kConv3x3Up2, r.xg, H, W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, r.xn);
-                normed = true;
-            } else {
-                r.conv(kConv3x3Up2, r.xg, H, W, u.up, u.up.b, gs, 0, r.x);
-            }
-            H *= 2;
-            W *= 2;
-            cp = u.up.cout_p;
-        }
+    r.blocks(d, 0, pl.s, nullptr, cur, W, cp, normed);
+    if (pl.s == d.n_up) {
+        r.output(d, cur, W, cp, normed, Rows{0, pl.H}, pl.H, out);
+        return check_launch("decoder_forward");
     }
-    if (!normed) launch_rmsnorm(r.x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, r.xn, s);
-    if (d.conv_out.cout <= 16) {
-        // few output channels: straight into the NCHW frame
-        launch_conv_out(r.xn, H, W, d.conv_out.cin_p, reinterpret_cast<const _Float16 *>(d.conv_out.w),
-                        d.conv_out.cout, d.conv_out.cout_p, d.conv_out.b, out, s);
-    } else {
-        r.conv(kConv3x3, r.xn, H, W, d.conv_out, d.conv_out.b, 1.f, 0, r.h);
-        launch_nhwc_to_nchw(r.h, H * W, d.conv_out.cout_p, d.conv_out.cout, nullptr, out, s);
+    // the bands: blocks s.. from the saved whole-frame stream, each band's
+    // input rows copied into its own stream buffer
+    int n_res[IG_MAX_UP], has_up[IG_MAX_UP];
+    band_structure(d, n_res, has_up);
+    Run rb = r;
+    rb.x = reinterpret_cast<float *>(w + pl.off_xb);
+    for (int k0 = 0; k0 < pl.H; k0 += pl.band_rows) {
+        const Rows keep{k0, k0 + pl.band_rows < pl.H ? k0 + pl.band_rows : pl.H};
+        Rows input, feed[IG_MAX_UP];
+        plan_band(d.n_up, n_res, has_up, h0, pl.s, keep, input, feed);
+        const size_t row_bytes = (size_t)W * cp * sizeof(float);
+        if (hipMemcpyAsync(rb.x, r.x + (int64_t)input.lo * W * cp, row_bytes * input.n(), hipMemcpyDeviceToDevice,
+                           s) != hipSuccess)
+            return fail(IG_EHIP, "band copy failed");
+        Rows bcur = input;
+        int bW = W, bcp = cp;
+        bool bnormed = false;
+        rb.blocks(d, pl.s, d.n_up, feed, bcur, bW, bcp, bnormed);
+        rb.output(d, bcur, bW, bcp, bnormed, keep, pl.H, out);
     }
-    return check_launch("decoder_forward");
+    return check_launch("decoder_forward_bands");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ig_decoder_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_chunk)
+{
+    clear_error();
+    Plan pl;
+    if (make_plan(dec, h0, w0, q_chunk, 0, 0, pl)) return 0;
+    return pl.total;
+}
+
+int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2,
+                    int q_chunk, void *ws, size_t ws_bytes, float *out, void *stream)
+{
+    return run_decoder(dec, latent, h0, w0, guard_log2, q_chunk, 0, 0, ws, ws_bytes, out, stream);
+}
+
+size_t ig_decoder_bands_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_chunk, int band_rows,
+                                        int band_from)
+{
+    clear_error();
+    Plan pl;
+    if (make_plan(dec, h0, w0, q_chunk, band_rows, band_from, pl)) return 0;
+    return pl.total;
+}
+
+int decoder_forward_bands(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2,
+                          int q_chunk, int band_rows, int band_from, void *ws, size_t ws_bytes, float *out,
+                          void *stream)
+{
+    return run_decoder(dec, latent, h0, w0, guard_log2, q_chunk, band_rows, band_from, ws, ws_bytes, out,
+                       stream);
+}
+
+int ig_band_plan(int n_up, const int *n_res, const int *has_up, int h0, int band_from, int keep_lo,
+                 int keep_hi, int *input, int *feed)
+{
+    clear_error();
+    if (n_up < 0 || n_up > IG_MAX_UP || h0 <= 0 || !n_res || !has_up || !input || (n_up > 0 && !feed))
+        return fail(IG_EINVAL, "bad band plan arguments");
+    if (band_from < 0 || band_from > n_up) return fail(IG_EINVAL, "band_from=%d outside 0..%d", band_from, n_up);
+    int ups = 0;
+    for (int i = 0; i < n_up; ++i) {
+        if (n_res[i] < 0 || n_res[i] > IG_MAX_RES) return fail(IG_EINVAL, "n_res[%d]=%d", i, n_res[i]);
+        ups += has_up[i] ? 1 : 0;
+    }
+    if (ups >= 24 || ((int64_t)h0 << ups) >= (1LL << 30)) return fail(IG_EINVAL, "frame too tall");
+    const int hf = h0 << ups;
+    if (keep_lo < 0 || keep_hi > hf || keep_lo >= keep_hi) return fail(IG_EINVAL, "keep rows [%d, %d) outside [0, %d)", keep_lo, keep_hi, hf);
+    Rows in, fd[IG_MAX_UP];
+    plan_band(n_up, n_res, has_up, h0, band_from, Rows{keep_lo, keep_hi}, in, fd);
+    input[0] = in.lo;
+    input[1] = in.hi;
+    for (int i = 0; i < n_up; ++i) {
+        feed[2 * i] = i >= band_from ? fd[i].lo : 0;
+        feed[2 * i + 1] = i >= band_from ? fd[i].hi : 0;
+    }
+    return IG_OK;
 }
 
 }  // extern "C"

@@ -284,11 +284,11 @@ __global__ __launch_bounds__(256) void k_latent(const float *__restrict__ z, int
 // output: NHWC f32 [M][ld] (first nch channels) + bias -> NCHW [nch][M]
 // ---------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_out(const float *__restrict__ y, int M, int ld, int nch,
-                                             const float *__restrict__ bias, float *__restrict__ out)
+                                             const float *__restrict__ bias, float *__restrict__ out, int64_t HWo)
 {
     for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < M; p += (int64_t)gridDim.x * 256)
         for (int ch = 0; ch < nch; ++ch)
-            out[(int64_t)ch * M + p] = y[p * ld + ch] + (bias ? bias[ch] : 0.f);
+            out[(int64_t)ch * HWo + p] = y[p * ld + ch] + (bias ? bias[ch] : 0.f);
 }
 
 // ---------------------------------------------------------------------
@@ -414,11 +414,11 @@ void launch_latent_ingest(const float *z, int zc, int M, int cp, _Float16 *y, hi
 }
 
 void launch_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, float *out,
-                         hipStream_t s)
+                         hipStream_t s, int64_t HWo)
 {
     if (M <= 0) return;
     hipLaunchKernelGGL(k_out, dim3(blocks_for(M, 256, 1 << 20)), dim3(256), 0, s, y, M, ld, nch,
-                       bias, out);
+                       bias, out, HWo > 0 ? HWo : (int64_t)M);
 }
 
 void launch_pack_weights(const _Float16 *w, int cout, int cin, int k, int cout_p, int cin_p,

@@ -116,12 +116,17 @@ void launch_combine(float *x, const float *h, const float *hb, const float *sv, 
 void launch_softmax(const float *S, int rows, int lds, int valid, int ncols, _Float16 *P, int ldp,
                     hipStream_t s);
 void launch_latent_ingest(const float *z, int zc, int M, int cp, _Float16 *y, hipStream_t s);
+// out[ch][p] = y[p][ch] (+ bias[ch]) for p < M, output planes HWo apart
+// (HWo <= 0: M)
 void launch_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, float *out,
-                         hipStream_t s);
+                         hipStream_t s, int64_t HWo = 0);
 void launch_pack_weights(const _Float16 *w, int cout, int cin, int k, int cout_p, int cin_p,
                          _Float16 *plane, hipStream_t s);
+// the decoder's output conv into the NCHW frame; by default the whole
+// image, else rows r0 .. r1 - 1 of it with output planes HWo apart (out
+// points at the frame pixel of image row 0)
 void launch_conv_out(const _Float16 *x, int H, int W, int cin_p, const _Float16 *plane, int cout, int cout_p,
-                     const float *bias, float *out, hipStream_t s);
+                     const float *bias, float *out, hipStream_t s, int r0 = 0, int r1 = -1, int64_t HWo = 0);
 void launch_zero_rows_f16(_Float16 *y, int r0, int r1, int ld, hipStream_t s);
 void launch_dupup(const float *src, int H, int W, int cin_p, float *x, int cout, int cout_p,
                   int factor, int repeats, int ft, hipStream_t s);

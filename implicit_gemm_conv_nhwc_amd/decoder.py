@@ -121,3 +121,16 @@ class DeviceDecoder:
         L.decoder_forward(self.desc, latent, h0, w0, guard_log2, q_chunk, ws, nbytes, out,
                           stream if stream is not None else self.stream)
         return out
+
+    def forward_bands(self, latent, h0, w0, band_rows, band_from, guard_log2=8, q_chunk=0, out=None,
+                      stream=None):
+        """The banded decode: up blocks band_from.. in bands of band_rows
+        kept output rows (the same output as forward)."""
+        n = L.decoder_bands_workspace_bytes(self.desc, h0, w0, q_chunk, band_rows, band_from)
+        ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        H, W = h0 << self.n_up, w0 << self.n_up
+        if out is None:
+            out = torch.empty((self.out_c, H, W), dtype=torch.float32, device=self.device)
+        L.decoder_forward_bands(self.desc, latent, h0, w0, guard_log2, q_chunk, band_rows, band_from, ws, n, out,
+                                stream if stream is not None else self.stream)
+        return out

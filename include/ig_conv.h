@@ -328,6 +328,36 @@ size_t ig_decoder_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_c
 int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2,
                     int q_chunk, void *ws, size_t ws_bytes, float *out, void *stream);
 
+/* ---------------------------------------------------------------------
+ * Banded decode ([QI] the bands section: `grow`, `half`, `plan_band`,
+ * `run_blocks`, `output_rows`). Everything after the mid block is local in
+ * space, so up blocks band_from.. can run in horizontal bands of band_rows
+ * kept output rows: each band starts from rows of the whole-frame stream
+ * saved at block band_from's input, walked back from its kept rows (a 3x3
+ * conv needs one more row per side, an upsample halves the range rounded
+ * outward, both clamped to the frame); rows next to a band edge come out
+ * wrong but never reach a kept row, so the kept rows are bit for bit the
+ * whole-frame decode's. The workspace holds the whole-frame tensors up to
+ * block band_from and one band's tensors after it.
+ * band_rows <= 0 or band_from >= n_up: the whole frame (decoder_forward).
+ * Returns 0 from the size query on invalid arguments (ig_last_error()).
+ * --------------------------------------------------------------------- */
+size_t ig_decoder_bands_workspace_bytes(const ig_decoder *dec, int h0, int w0, int q_chunk, int band_rows,
+                                        int band_from);
+int decoder_forward_bands(const ig_decoder *dec, const float *latent, int h0, int w0, int guard_log2,
+                          int q_chunk, int band_rows, int band_from, void *ws, size_t ws_bytes, float *out,
+                          void *stream);
+
+/* The band planner alone (host only, no device work): for a decoder of
+ * n_up up blocks (block i: n_res[i] resnets of two 3x3 convs, then, if
+ * has_up[i], a nearest-2x upsample and a 3x3 conv) followed by a 3x3
+ * conv_out, latent height h0, and kept output rows [keep_lo, keep_hi):
+ * input[0..1] = the rows [lo, hi) of block band_from's input the band
+ * starts from; feed[2i..2i+1] = the rows block i (>= band_from, with
+ * has_up) feeds to its upsample, (0, 0) otherwise. feed: [2 * n_up]. */
+int ig_band_plan(int n_up, const int *n_res, const int *has_up, int h0, int band_from, int keep_lo,
+                 int keep_hi, int *input, int *feed);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,11 @@ Sources (the pages are cited by title and item):
 * qi21_vae.rs (cortiq-engine 0.8.3): module doc; RMSN_SRC; CAST_SRC;
   `guard`; `Rec::resnet`; `attention`; `run_blocks`; `output_rows`; `decode`.
 * vae.rs (cortiq-engine 0.7.6): `Conv2d::apply`; `upsample2x`; `silu`;
-  `AttnBlock::apply`; `VaeDecoder::decode`; its three unit tests.
+  `AttnBlock::apply`; `VaeDecoder::decode`; `GroupNorm::apply`; its unit
+  tests.
+* qi21_vae.rs, the bands section: `grow`, `half`, `plan_band` (the band
+  planner, pinned by the pages' walk-back test and by brute force on a
+  1-D decoder).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (library routines, closed forms, invariants, the pages' own worked values).
@@ -373,6 +377,47 @@ def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
             trace.stages["up%d" % si] = x.copy() if x.size <= (1 << 24) else None
     xn = rnd(rmsnorm(x, wts["norm_out"], silu=True))
     return conv2d(xn, wts["conv_out"]["w"], wts["conv_out"]["b"])
+
+
+# ---------------------------------------------------------------------------
+# bands (qi21_vae.rs, the bands section: `grow`, `half`, `plan_band`)
+# ---------------------------------------------------------------------------
+
+
+def rows_grow(lo, hi, k, h):
+    """Rows a 3x3-conv stack of k convs reads to produce rows [lo, hi) of an
+    h-row level: k more on each side, clamped to the level (the frame edge is
+    the convs' real zero padding)."""
+    return max(lo - k, 0), min(hi + k, h)
+
+
+def rows_half(lo, hi):
+    """Rows of the half-resolution input a nearest-2x upsample reads to
+    produce rows [lo, hi): output row r reads input row r // 2, so
+    [lo // 2, ceil(hi / 2))."""
+    return lo // 2, -(-hi // 2)
+
+
+def plan_band(n_res, has_up, h0, band_from, keep):
+    """Walk back from kept output rows through conv_out (one 3x3 conv) and
+    up blocks band_from.. in reverse (block i: n_res[i] resnets of two 3x3
+    convs, then, when has_up[i], the nearest-2x upsample and its 3x3 conv).
+    Returns (rows of block band_from's input, {i: rows block i feeds to its
+    upsample})."""
+    n_up = len(n_res)
+    lvl, l = [], 0
+    for u in has_up:
+        lvl.append(l)
+        l += 1 if u else 0
+    e = rows_grow(keep[0], keep[1], 1, h0 << l)
+    feed = {}
+    for i in range(n_up - 1, band_from - 1, -1):
+        if has_up[i]:
+            g = rows_grow(e[0], e[1], 1, h0 << (lvl[i] + 1))
+            e = rows_half(*g)
+            feed[i] = e
+        e = rows_grow(e[0], e[1], 2 * n_res[i], h0 << lvl[i])
+    return e, feed
 
 
 # ---------------------------------------------------------------------------

@@ -84,6 +84,51 @@ def test_decode_query_chunks_agree(full_decoder):
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+@pytest.mark.parametrize("band_rows,band_from", [(64, 0), (94, 1), (100, 2), (37, 2), (256, 1), (8, 2)])
+def test_banded_decode_is_bit_identical(full_decoder, band_rows, band_from):
+    """Bands with exact halos (the pages' bands section): every kept row is
+    computed by the same kernels on the same inputs as in the whole frame,
+    so the banded output equals the whole-frame output bit for bit."""
+    _, dd = full_decoder
+    z = dev(synth.decoder_latent(32, 32, config=4))
+    whole = dd.forward(z, 32, 32, q_chunk=0)
+    banded = dd.forward_bands(z, 32, 32, band_rows, band_from, q_chunk=0)
+    torch.cuda.synchronize()
+    d = float((banded - whole).abs().max())
+    print("bands of %d rows from block %d: max|d| %g" % (band_rows, band_from, d), flush=True)
+    assert torch.equal(banded, whole)
+
+
+def test_banded_decode_small_decoder_and_frame_edges():
+    spec = synth.decoder_spec(small=True)
+    w = synth.decoder_weights(spec, seed_config=4)
+    dd = ig.DeviceDecoder(w)
+    z = dev(synth.decoder_latent(5, 7, zc=spec.zc))
+    whole = dd.forward(z, 5, 7, q_chunk=8)
+    H = 5 << dd.n_up
+    for band_rows in (1, 3, H - 1, H):
+        for band_from in range(len(w["ups"])):
+            banded = dd.forward_bands(z, 5, 7, band_rows, band_from, q_chunk=8)
+            assert torch.equal(banded, whole), (band_rows, band_from)
+
+
+def test_banded_workspace_is_bounded(full_decoder):
+    _, dd = full_decoder
+    whole = ig.decoder_workspace_bytes(dd.desc, 128, 128, 0)
+    banded = ig.decoder_bands_workspace_bytes(dd.desc, 128, 128, 0, 128, 2)
+    print("1024^2 workspace: whole %.2f GB, bands of 128 rows from block 2 %.2f GB" % (whole / 1e9, banded / 1e9))
+    assert banded < whole
+
+
+def test_banded_decode_full_size_1024(full_decoder):
+    w, dd = full_decoder
+    z = dev(synth.decoder_latent(128, 128, config=5, scale=8.0))
+    whole = dd.forward(z, 128, 128, q_chunk=0)
+    banded = dd.forward_bands(z, 128, 128, 373, 1, q_chunk=0)
+    torch.cuda.synchronize()
+    assert torch.equal(banded, whole)
+
+
 def test_guard_on_a_stream_past_f16():
     spec = synth.decoder_spec()
     w = synth.decoder_weights(spec, seed_config=4, conv_in_gain=2.0 ** 11)
