@@ -52,6 +52,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int int8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -266,7 +267,9 @@ void k_conv_halo(IgemmArgs p)
                         val.z += o.z;
                         val.w += o.w;
                     }
-                    *reinterpret_cast<float4 *>(dst) = val;
+                    // streaming store: the tile is written once and not
+                    // read again by this kernel
+                    __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w}, reinterpret_cast<f32x4 *>(dst));
                 }
             }
         }
