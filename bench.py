@@ -18,6 +18,9 @@ Also measured, in the same process and on the stream the kernels run on:
   * roofline_cast: the guarded f16 cast at 512x512x128 (same 201 MB);
   * roofline_groupnorm: GroupNorm(32) + SiLU at 512x512x128, algorithmic
     201 MB (its statistics pass reads the input once more);
+  * roofline_attention: the single-pass attention core at 16384 tokens x
+    512 (the 1024^2 decode's mid block; 4 m^2 C = 550 GFLOP per launch:
+    Q.K^T and P.V) against the f16 MFMA peak;
   * cpu_baseline: the CPU oracle decoding the 256x256 configuration (a
     bounded sample of the same decoder), in TFLOP/s.
 
@@ -39,7 +42,27 @@ if ROOT not in sys.path:
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-ROOF_KERNEL = "k_conv_halo<1, 128, 8, false>"  # the 3x3 conv instantiation for 512^2 x 128
+WARM_SECONDS = 0.05  # untimed launches for this long before each roofline's timed region
+
+
+def _warm(fn, seconds=WARM_SECONDS):
+    """Launch fn(i) until `seconds` of GPU work have passed: measured, the
+    clock keeps rising for tens of milliseconds after the GPU was idle
+    (host-side setup), and the timed regions should see the steady state."""
+    import time
+
+    import torch
+
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(10):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+ROOF_KERNEL = "k_conv_halo<1, 64, 4, false>"  # the 3x3 conv instantiation for 512^2 x 128
 CONV_SRC = os.path.join(ROOT, "implicit_gemm_conv_nhwc_amd", "csrc", "conv_halo.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_512x512x128_traffic.json")
 
@@ -162,9 +185,9 @@ def bench_conv_roofline(reps, H=512, W=512, C=128):
     ys = [torch.empty((M, C), dtype=torch.float32, device=dev) for _ in range(nsets)]
     for t in xs:
         ig.rmsnorm_silu_f16(x32, M, C, C, None, gamma, 0, 1e-12, t)
-    for i in range(3):
-        ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets])
-    torch.cuda.synchronize()
+    # warm up to the steady clock (the host-side setup above leaves the GPU
+    # idle for seconds)
+    nwarm = _warm(lambda i: ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets]))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -176,7 +199,7 @@ def bench_conv_roofline(reps, H=512, W=512, C=128):
     flops = 2.0 * M * C * C * 9
     byts = M * C * 2 + C * 9 * C * 2 + M * C * 4
     ok = bool(torch.isfinite(ys[(reps - 1) % nsets]).all().item())
-    return {"avg_ms": avg_ms, "flops": flops, "bytes": byts, "launches": reps + 3, "finite": ok,
+    return {"avg_ms": avg_ms, "flops": flops, "bytes": byts, "launches": reps, "warm_launches": nwarm, "finite": ok,
             "sets": nsets}
 
 
@@ -196,8 +219,7 @@ def bench_norm_roofline(reps, H=512, W=512, C=128):
     x0 = torch.from_numpy(d["x"].reshape(M, C)).to(dev)
     xs = [x0.clone() for _ in range(nsets)]
     ys = [torch.empty((M, C), dtype=torch.float16, device=dev) for _ in range(nsets)]
-    for i in range(3):
-        ig.rmsnorm_silu_f16(xs[i], M, C, C, None, gamma, 1, 1e-12, ys[i])
+    _warm(lambda i: ig.rmsnorm_silu_f16(xs[i % nsets], M, C, C, None, gamma, 1, 1e-12, ys[i % nsets]))
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -218,9 +240,7 @@ def _pool_timed(fn, reps, per_set_bytes, make_set):
 
     nsets = max(2, int(np.ceil(1.2e9 / per_set_bytes)))
     sets = [make_set() for _ in range(nsets)]
-    for i in range(3):
-        fn(sets[i % nsets])
-    torch.cuda.synchronize()
+    _warm(lambda i: fn(sets[i % nsets]))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -264,6 +284,33 @@ def bench_groupnorm_roofline(reps, H=512, W=512, C=128, groups=32):
         lambda st: ig.groupnorm_silu_f16(st[0], M, C, C, groups, None, gamma, beta, 1, 1e-6, ws, nbytes, st[1]),
         reps, M * C * 6, lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
     return {"avg_ms": ms, "bytes": M * C * 6, "sets": nsets}
+
+
+def bench_attention_roofline(reps, m=16384, C=512):
+    """attention_f16 (single pass) at m tokens x C: 4 m^2 C FLOP per launch."""
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    q = torch.randn((m, C), device=dev, generator=g).half()
+    k = torch.randn((m, C), device=dev, generator=g).half()
+    vt = torch.randn((C, m), device=dev, generator=g).half()
+    bv = torch.zeros(C, device=dev)
+    nb = ig.attention_workspace_bytes(m, C)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((m, C), dtype=torch.float16, device=dev)
+    _warm(lambda i: ig.attention_f16(q, k, vt, m, m, C, bv, ws, nb, out))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ig.attention_f16(q, k, vt, m, m, C, bv, ws, nb, out)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"avg_ms": e0.elapsed_time(e1) / reps, "flops": 4.0 * m * m * C}
 
 
 def cpu_baseline(min_seconds=10.0):
@@ -316,7 +363,7 @@ def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
 
     conv = [float(r["Counter_Value"]) for r in sorted(rows(conv_csv), key=lambda r: int(r["Start_Timestamp"]))
             if ROOF_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", "")
-            or "k_conv_halo" in r["Kernel_Name"] and "ILi1ELi128ELi8" in r["Kernel_Name"]][-roof_launches:]
+            or "k_conv_halo" in r["Kernel_Name"] and "ILi1ELi64ELi4ELb0" in r["Kernel_Name"]][-roof_launches:]
     cp = [float(r["Counter_Value"]) for r in rows(copy_csv) if "mul" in r["Kernel_Name"].lower()
           or "elementwise" in r["Kernel_Name"].lower()]
     scale = nbytes / (sum(cp) / len(cp))
@@ -374,14 +421,14 @@ def main():
     args = ap.parse_args()
 
     if args.digest_trace:
-        digest_trace(args.digest_trace, args.roof_reps + 3)
+        digest_trace(args.digest_trace, args.roof_reps)
         return 0
     if args.copy_calibration:
         copy_calibration()
         return 0
     if args.digest_pmc:
-        f = digest_pmc(args.digest_pmc[0], args.digest_pmc[2], "FETCH_SIZE", args.roof_reps + 3)
-        w = digest_pmc(args.digest_pmc[1], args.digest_pmc[3], "WRITE_SIZE", args.roof_reps + 3)
+        f = digest_pmc(args.digest_pmc[0], args.digest_pmc[2], "FETCH_SIZE", args.roof_reps)
+        w = digest_pmc(args.digest_pmc[1], args.digest_pmc[3], "WRITE_SIZE", args.roof_reps)
         print(json.dumps({"source_sha256_16": conv_source_hash(), "fetch_bytes_per_launch": round(f),
                           "write_bytes_per_launch": round(w), "bytes_per_launch": round(f + w)}))
         return 0
@@ -421,6 +468,10 @@ def main():
     gn_gbs = gn["bytes"] / (gn["avg_ms"] / 1000.0) / 1e9
     log("groupnorm 512^2x128 (32 groups): %.2f us, %.0f GB/s algorithmic (%.1f%% of HBM)" % (
         gn["avg_ms"] * 1000, gn_gbs, 100 * gn_gbs / HBM_PEAK_GBS))
+    att = bench_attention_roofline(max(5, args.roof_reps // 5))
+    att_tf = att["flops"] / (att["avg_ms"] / 1000.0) / 1e12
+    log("attention 16384 x 512: %.1f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (
+        att["avg_ms"] * 1000, att_tf, 100 * att_tf / MFMA_F16_PEAK_TFLOPS))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -491,6 +542,16 @@ def main():
             "unit": "GB/s",
             "frac": round(gn_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(gn["avg_ms"] * 1000, 3),
+        },
+        "roofline_attention": {
+            "kernel": "attention_f16 single pass (k_flash + k_flash_merge), 16384 tokens x 512",
+            "bound": "mfma",
+            "achieved": round(att_tf, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "avg_us": round(att["avg_ms"] * 1000, 3),
+            "algorithmic_flop": att["flops"],
         },
         "cpu_baseline": cpu,
         "context": "pages: 0.49-0.61 s per 1024^2 decode on an RTX PRO 4000 Blackwell "

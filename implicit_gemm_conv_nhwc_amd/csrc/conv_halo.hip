@@ -10,9 +10,10 @@
 //
 // Design (not the pages' 128x64 cooperative-matrix tiling):
 //  * a workgroup owns an output tile of 16 rows x 32 columns x BN
-//    channels: 8 wave64s with BN = 128 (one workgroup per CU), or 4 with
-//    BN = 64 (two per CU) when the 128-channel tiles would not fill the
-//    chip. Each wave computes 4 output rows x 32 columns x 64 channels as
+//    channels: 4 wave64s with BN = 64 (two workgroups per CU, so one's
+//    epilogue overlaps the other's MFMAs), or 8 with BN = 128 (one per CU)
+//    when the fused RMS_norm needs all 128 channels of a pixel in one tile.
+//    Each wave computes 4 output rows x 32 columns x 64 channels as
 //    4 x 2 tiles of v_mfma_f32_32x32x16_f16 (one output row is one 32-row
 //    MFMA operand);
 //  * the reduction runs in stages of 16 input channels. A stage brings into
@@ -330,13 +331,6 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return;
-    // 8 waves on 16x32x128 tiles (one workgroup per CU) when there are
-    // enough of them to fill the chip; otherwise 4 waves on 16x32x64 tiles
-    // (two workgroups per CU, twice the tiles)
-    const int Hout = (mode == kConv3x3Up2) ? 2 * a.H : a.H;
-    const int Wout = (mode == kConv3x3Up2) ? 2 * a.W : a.W;
-    const int64_t pix_tiles = (int64_t)((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW);
-    const bool bn128 = (a.N % 128) == 0 && pix_tiles * (a.N / 128) >= 256;
     if (a.ngamma) {
         // the fused RMS_norm needs every channel of a pixel in one tile
         if (mode == kConv3x3) {
@@ -348,13 +342,13 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
         }
         return;
     }
-    if (mode == kConv3x3) {
-        if (bn128) launch_t<kConv3x3, 128, 8>(a, s);
-        else launch_t<kConv3x3, 64, 4>(a, s);
-    } else {
-        if (bn128) launch_t<kConv3x3Up2, 128, 8>(a, s);
-        else launch_t<kConv3x3Up2, 64, 4>(a, s);
-    }
+    // 64-channel tiles: two workgroups share a CU, so one's epilogue (HBM
+    // writes) overlaps the other's MFMAs; measured faster than 128-channel
+    // tiles (one workgroup per CU) on every shape of the decoder
+    if (mode == kConv3x3)
+        launch_t<kConv3x3, 64, 4>(a, s);
+    else
+        launch_t<kConv3x3Up2, 64, 4>(a, s);
 }
 
 }  // namespace ig
