@@ -39,6 +39,7 @@ from ._lib import (  # noqa: F401
     nhwc_to_nchw,
     pack_conv_weights,
     rmsnorm_silu_f16,
+    rmsnorm_silu_guard_cast_f16,
     softmax_rows_f16,
     version,
     zero_rows_f16,

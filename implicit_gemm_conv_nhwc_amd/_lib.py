@@ -62,6 +62,8 @@ _gemm = _sig("gemm1x1", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, 
 _gemm_acc = _sig("gemm1x1_acc", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _c_float, _vp,
                                  _c_int, _vp])
 _rms = _sig("rmsnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_float, _vp, _vp])
+_rms_cast = _sig("rmsnorm_silu_guard_cast_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_float, _vp,
+                                                 _c_int, _vp, _vp])
 _cast = _sig("guard_cast", [_vp, _c_int, _c_int, _vp, _c_int, _vp, _vp])
 _comb = _sig("ig_combine", [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp])
 _smax = _sig("ig_softmax_rows_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp])
@@ -151,6 +153,11 @@ def gemm1x1_acc(a, M, K, lda, b, N, ldb, bias, oscale, c, ldc, stream=None):
 def rmsnorm_silu_f16(x, M, cp, c_real, bias, gamma, silu, eps, y, stream=None):
     return _check(_rms(_ptr(x), M, cp, c_real, _ptr(bias), _ptr(gamma), int(silu), float(eps), _ptr(y),
                        _stream(stream)))
+
+
+def rmsnorm_silu_guard_cast_f16(x, M, cp, c_real, bias, gamma, silu, eps, y, guard_log2, yg, stream=None):
+    return _check(_rms_cast(_ptr(x), M, cp, c_real, _ptr(bias), _ptr(gamma), silu, eps, _ptr(y), guard_log2,
+                            _ptr(yg), _stream(stream)))
 
 
 def guard_cast(x, M, C, bias, guard_log2, y, stream=None):

@@ -223,10 +223,11 @@ int gemm1x1_acc(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int
     return gemm_any(a, M, K, lda, b, N, ldb, bias, oscale, c, ldc, 0, 1, stream);
 }
 
-int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bias,
-                     const float *gamma, int silu, float eps, uint16_t *y, void *stream)
+static int rmsnorm_any(const float *x, int M, int cp, int c_real, const float *bias, const float *gamma, int silu,
+                       float eps, uint16_t *y, int guard_log2, uint16_t *yg, void *stream)
 {
     clear_error();
+    if (yg && (guard_log2 < 0 || guard_log2 > 14)) return fail(IG_EINVAL, "guard_log2=%d outside 0..14", guard_log2);
     if (M < 0) return fail(IG_EINVAL, "M=%d is negative", M);
     if (cp <= 0 || cp % 64 || cp > 1024) return fail(IG_EUNSUPPORTED, "cp=%d is not a multiple of 64 in 64..1024", cp);
     if (c_real <= 0 || c_real > cp) return fail(IG_EINVAL, "c_real=%d outside 1..cp", c_real);
@@ -236,10 +237,28 @@ int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bia
     int r;
     if ((r = check_ptr(x, "x")) || (r = check_ptr(gamma, "gamma")) || (r = check_ptr(y, "y"))) return r;
     if (bias && (r = check_ptr(bias, "bias"))) return r;
+    if (yg && (r = check_ptr(yg, "yg"))) return r;
     (void)hipGetLastError();
     launch_rmsnorm(x, M, cp, c_real, bias, gamma, silu, eps, reinterpret_cast<_Float16 *>(y),
-                   reinterpret_cast<hipStream_t>(stream));
+                   reinterpret_cast<hipStream_t>(stream), reinterpret_cast<_Float16 *>(yg), guard_log2);
     return check_launch("rmsnorm launch");
+}
+
+int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bias,
+                     const float *gamma, int silu, float eps, uint16_t *y, void *stream)
+{
+    return rmsnorm_any(x, M, cp, c_real, bias, gamma, silu, eps, y, 0, nullptr, stream);
+}
+
+int rmsnorm_silu_guard_cast_f16(const float *x, int M, int cp, int c_real, const float *bias,
+                                const float *gamma, int silu, float eps, uint16_t *y, int guard_log2,
+                                uint16_t *yg, void *stream)
+{
+    if (!yg) {
+        clear_error();
+        return fail(IG_EINVAL, "yg is NULL");
+    }
+    return rmsnorm_any(x, M, cp, c_real, bias, gamma, silu, eps, y, guard_log2, yg, stream);
 }
 
 size_t ig_groupnorm_workspace_bytes(int M, int cp, int groups)

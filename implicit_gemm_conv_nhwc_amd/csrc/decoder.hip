@@ -451,10 +451,13 @@ struct Run {
     void resnet(const ig_resnet_w &r, int H, int W, int cp)
     {
         const int M = H * W;
-        launch_rmsnorm(x, M, cp, r.c1.cin, nullptr, r.g1, 1, kEps, xn, s);
         if (r.has_sc) {
-            launch_guard_cast(x, M, cp, nullptr, g, xg, s);
+            // one read of the stream gives the norm and the shortcut's
+            // guarded input
+            launch_rmsnorm(x, M, cp, r.c1.cin, nullptr, r.g1, 1, kEps, xn, s, xg, g);
             conv(kGemm, xg, H, W, r.sc, r.sc.b, ldexpf(1.f, g), 0, x);
+        } else {
+            launch_rmsnorm(x, M, cp, r.c1.cin, nullptr, r.g1, 1, kEps, xn, s);
         }
         if (fusable(r.c1)) {
             // conv1's epilogue normalises (h + b1) itself; the f16 result

@@ -35,13 +35,16 @@ __device__ __forceinline__ float silu1(float y) { return y / (1.0f + __expf(-y))
 // ---------------------------------------------------------------------
 // RMS_norm: 16 lanes per pixel, each lane NCH float4 chunks (channels
 // 4*(g + 16k) .. +3), so a wave handles 4 pixels and every load
-// instruction reads 256 contiguous bytes per pixel.
+// instruction reads 256 contiguous bytes per pixel. With yg, the same read
+// also yields the guarded cast f16((x + b) * gscale) of the row (a resnet
+// whose shortcut takes the raw stream), saving that cast's own read.
 // ---------------------------------------------------------------------
 template <int NCH>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, int M, int cp,
                                                  float sqrt_c, const float *__restrict__ bias,
                                                  const float *__restrict__ gamma, int silu,
-                                                 float eps, _Float16 *__restrict__ y)
+                                                 float eps, _Float16 *__restrict__ y,
+                                                 _Float16 *__restrict__ yg, float gscale)
 {
     const int g = threadIdx.x & 15;
     const int64_t pix = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
@@ -60,6 +63,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, in
             v[k].z += b.z;
             v[k].w += b.w;
         }
+    }
+    if (yg) {
+        half4 *gr = reinterpret_cast<half4 *>(yg + pix * cp);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            gr[g + 16 * k] = to_half4(make_float4(v[k].x * gscale, v[k].y * gscale, v[k].z * gscale, v[k].w * gscale));
     }
     float ss = 0.f;
 #pragma unroll
@@ -93,7 +102,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, in
 __global__ __launch_bounds__(256) void k_rmsnorm_wide(const float *__restrict__ x, int M, int cp,
                                                       float sqrt_c, const float *__restrict__ bias,
                                                       const float *__restrict__ gamma, int silu,
-                                                      float eps, _Float16 *__restrict__ y)
+                                                      float eps, _Float16 *__restrict__ y,
+                                                      _Float16 *__restrict__ yg, float gscale)
 {
     const int g = threadIdx.x & 15;
     const int64_t pix = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
@@ -109,6 +119,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_wide(const float *__restrict__ 
             v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
         }
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        if (yg)
+            reinterpret_cast<half4 *>(yg + pix * cp)[c] =
+                to_half4(make_float4(v.x * gscale, v.y * gscale, v.z * gscale, v.w * gscale));
     }
     ss += __shfl_xor(ss, 8, 16);
     ss += __shfl_xor(ss, 4, 16);
@@ -353,16 +366,18 @@ inline unsigned blocks_for(int64_t n, int64_t per = 256, int64_t cap = 1 << 20)
 }  // namespace
 
 void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias,
-                    const float *gamma, int silu, float eps, _Float16 *y, hipStream_t s)
+                    const float *gamma, int silu, float eps, _Float16 *y, hipStream_t s, _Float16 *yg,
+                    int guard_log2)
 {
     if (M <= 0) return;
     const float sqrt_c = sqrtf((float)c_real);
+    const float gscale = ldexpf(1.0f, -guard_log2);
     const unsigned grid = (unsigned)(((int64_t)M * 16 + 255) / 256);
     switch (cp / 64) {
 #define IG_NORM_CASE(n)                                                                          \
     case n:                                                                                      \
         hipLaunchKernelGGL(k_rmsnorm<n>, dim3(grid), dim3(256), 0, s, x, M, cp, sqrt_c, bias,    \
-                           gamma, silu, eps, y);                                                 \
+                           gamma, silu, eps, y, yg, gscale);                                     \
         break;
         IG_NORM_CASE(1)
         IG_NORM_CASE(2)
@@ -375,7 +390,7 @@ void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias
 #undef IG_NORM_CASE
     default:
         hipLaunchKernelGGL(k_rmsnorm_wide, dim3(grid), dim3(256), 0, s, x, M, cp, sqrt_c, bias,
-                           gamma, silu, eps, y);
+                           gamma, silu, eps, y, yg, gscale);
     }
 }
 

@@ -101,8 +101,11 @@ void launch_flash(FlashArgs a, void *ws, hipStream_t s);
 // ---------------------------------------------------------------------
 // memory-bound kernels
 // ---------------------------------------------------------------------
+// RMS_norm (+ bias on read, + SiLU) -> f16 y; with yg, also the guarded
+// cast f16((x + bias) * 2^-guard_log2) of the same rows -> yg
 void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias,
-                    const float *gamma, int silu, float eps, _Float16 *y, hipStream_t s);
+                    const float *gamma, int silu, float eps, _Float16 *y, hipStream_t s,
+                    _Float16 *yg = nullptr, int guard_log2 = 0);
 // GroupNorm: workspace for the per-chunk statistics, support check, launch
 size_t gn_workspace_bytes(int M, int cp, int groups);
 bool gn_supported(int cp, int c_real, int groups);

@@ -156,6 +156,15 @@ int gemm1x1_acc(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int
 int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bias,
                      const float *gamma, int silu, float eps, uint16_t *y, void *stream);
 
+/* The same norm and, from the same read of x, the guarded cast of the raw
+ * stream ([QI] `Rec::resnet`: a resnet whose shortcut takes the stream
+ * normalises it for conv1 and casts it, guarded, for the 1x1 shortcut):
+ *   y as rmsnorm_silu_f16;  yg[p][c] = f16( (x[p][c] + bias[c]) * 2^-guard_log2 )
+ * yg: f16 [M][cp]; guard_log2 in 0..14. Errors as rmsnorm_silu_f16. */
+int rmsnorm_silu_guard_cast_f16(const float *x, int M, int cp, int c_real, const float *bias,
+                                const float *gamma, int silu, float eps, uint16_t *y, int guard_log2,
+                                uint16_t *yg, void *stream);
+
 /* GroupNorm into the next conv's f16 input -- the norm of FLUX-class
  * decoders ([VAE] `GroupNorm::apply`; page "cortiq-engine 0.8.72,
  * src/gpu_wgpu/s2v_vae.rs", GN_PART_SRC / GN_FIN_SRC / GN_APPLY_SRC, `gn`):

@@ -176,6 +176,36 @@ def test_guard_cast_bias_and_range(g):
         assert fin.all()  # 2^-8 keeps |x| < 65504 * 256 finite
 
 
+@pytest.mark.parametrize("c,cp,with_bias,g", [(256, 256, False, 8), (512, 512, False, 8), (288, 320, True, 4),
+                                             (1000, 1024, True, 14)])
+def test_rmsnorm_with_guarded_cast(c, cp, with_bias, g):
+    """The norm of a resnet with a shortcut and the shortcut's guarded cast
+    from one read of the stream: each output against the oracle's norm and
+    cast of the same rows (and bit for bit against the separate kernels)."""
+    M = 1000
+    x = synth.normal(14, c, (M, c), 1.0e8)  # std 1e4: the guard matters
+    gamma = synth.uniform(14, c + 1, (c,), 0.5, 1.5)
+    bias = synth.normal(14, c + 2, (c,), 0.02) if with_bias else None
+    xd = dev(pad_last(x, cp))
+    gd = padded_vec(gamma, cp)
+    bd = padded_vec(bias, cp) if bias is not None else None
+    y, yg = nan_f16((M, cp)), nan_f16((M, cp))
+    ig.rmsnorm_silu_guard_cast_f16(xd, M, cp, c, bd, gd, 1, 1e-12, y, g, yg)
+    y1, yg1 = nan_f16((M, cp)), nan_f16((M, cp))
+    ig.rmsnorm_silu_f16(xd, M, cp, c, bd, gd, 1, 1e-12, y1)
+    ig.guard_cast(xd, M, cp, bd, g, yg1)
+    assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(yg.view(torch.int16), yg1.view(torch.int16))
+    got, gotg = host(y), host(yg)
+    ref = O.f16(O.rmsnorm(x.T, gamma, bias=bias, silu=True)).T
+    _assert_f16_close(got[:, :c], ref)
+    assert np.all(got[:, c:] == 0)
+    refg = O.guard_cast(x.T, g, bias=bias).T
+    fin = np.isfinite(refg)
+    assert np.array_equal(np.isinf(gotg[:, :c]), np.isinf(refg))
+    _assert_f16_close(gotg[:, :c][fin], refg[fin])
+
+
 # ---------------------------------------------------------------------------
 # 3x3 convolution
 # ---------------------------------------------------------------------------
