@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     UpW,
     combine,
     conv3x3_nhwc,
+    conv3x3_guard_out_nhwc,
     conv3x3_norm_nhwc,
     conv3x3_out_nchw,
     conv3x3_up2_nhwc,

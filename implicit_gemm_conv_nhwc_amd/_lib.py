@@ -64,6 +64,8 @@ _gemm_acc = _sig("gemm1x1_acc", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_in
 _rms = _sig("rmsnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_float, _vp, _vp])
 _rms_cast = _sig("rmsnorm_silu_guard_cast_f16", [_vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_float, _vp,
                                                  _c_int, _vp, _vp])
+_conv_g = _sig("ig_conv3x3_guard_out_nhwc", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_float, _c_int,
+                                             _vp, _c_int, _c_int, _vp, _vp])
 _cast = _sig("guard_cast", [_vp, _c_int, _c_int, _vp, _c_int, _vp, _vp])
 _comb = _sig("ig_combine", [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp])
 _smax = _sig("ig_softmax_rows_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp])
@@ -158,6 +160,12 @@ def rmsnorm_silu_f16(x, M, cp, c_real, bias, gamma, silu, eps, y, stream=None):
 def rmsnorm_silu_guard_cast_f16(x, M, cp, c_real, bias, gamma, silu, eps, y, guard_log2, yg, stream=None):
     return _check(_rms_cast(_ptr(x), M, cp, c_real, _ptr(bias), _ptr(gamma), silu, eps, _ptr(y), guard_log2,
                             _ptr(yg), _stream(stream)))
+
+
+def conv3x3_guard_out_nhwc(x, H, W, cin_p, mode, w, cout_p, bias, oscale, accumulate, y, write_y, guard_log2, yg,
+                           stream=None):
+    return _check(_conv_g(_ptr(x), H, W, cin_p, mode, _ptr(w), cout_p, _ptr(bias), oscale, accumulate, _ptr(y),
+                          write_y, guard_log2, _ptr(yg), _stream(stream)))
 
 
 def guard_cast(x, M, C, bias, guard_log2, y, stream=None):

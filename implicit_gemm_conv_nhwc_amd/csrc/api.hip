@@ -171,6 +171,42 @@ int ig_conv_nhwc_ex(const uint16_t *x, int H, int W, int cin_p, int mode, const 
     return conv_any(x, H, W, cin_p, mode, w, cout_p, bias, oscale, accumulate, y, stream);
 }
 
+int ig_conv3x3_guard_out_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
+                              const float *bias, float oscale, int accumulate, float *y, int write_y, int guard_log2,
+                              uint16_t *yg, void *stream)
+{
+    clear_error();
+    if (mode != 1 && mode != 2) return fail(IG_EINVAL, "mode %d is not a 3x3 mode", mode);
+    if (guard_log2 < 0 || guard_log2 > 14) return fail(IG_EINVAL, "guard_log2=%d outside 0..14", guard_log2);
+    if ((accumulate || write_y) && !y) return fail(IG_EINVAL, "y is NULL but read or written");
+    bool empty;
+    int r = check_conv(x, H, W, cin_p, w, cout_p, bias, yg, mode, &empty);
+    if (r || empty) return r;
+    if (y && (r = check_ptr(y, "y"))) return r;
+    IgemmArgs a{};
+    a.a = reinterpret_cast<const _Float16 *>(x);
+    a.b = reinterpret_cast<const _Float16 *>(w);
+    a.bias = bias;
+    a.c = y;
+    a.M = H * W * (mode == 2 ? 4 : 1);
+    a.N = cout_p;
+    a.K = 9 * cin_p;
+    a.lda = cin_p;
+    a.ldb = a.K;
+    a.ldc = cout_p;
+    a.H = H;
+    a.W = W;
+    a.cin_p = cin_p;
+    a.oscale = oscale;
+    a.accumulate = accumulate ? 1 : 0;
+    a.write_out = write_y ? 1 : 0;
+    a.yg = reinterpret_cast<_Float16 *>(yg);
+    a.gscale = ldexpf(1.f, -guard_log2);
+    (void)hipGetLastError();
+    launch_conv_halo(mode == 1 ? kConv3x3 : kConv3x3Up2, a, reinterpret_cast<hipStream_t>(stream));
+    return check_launch("conv+cast launch");
+}
+
 int ig_conv3x3_norm_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
                          int c_real, const float *bias, float oscale, const float *gamma, int silu, float eps,
                          float *y, uint16_t *yn, void *stream)

@@ -52,6 +52,7 @@ namespace ig {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -250,7 +251,7 @@ void k_conv_halo(IgemmArgs p)
             }
         __syncthreads();
         constexpr int V4 = 4 * TW * BN / 4;  // 16-byte pieces staged per pass
-        if (!NORM || p.write_out) {
+        if ((!NORM && p.yg) || p.write_out) {
 #pragma unroll
             for (int v = tid; v < V4; v += NT) {
                 const int e = v * 4;
@@ -270,7 +271,18 @@ void k_conv_halo(IgemmArgs p)
                     }
                     // streaming store: the tile is written once and not
                     // read again by this kernel
-                    __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w}, reinterpret_cast<f32x4 *>(dst));
+                    if (p.write_out)
+                        __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w},
+                                                    reinterpret_cast<f32x4 *>(dst));
+                    if (!NORM && p.yg) {
+                        const float gs = p.gscale;
+                        half4v h;
+                        h[0] = (_Float16)(val.x * gs);
+                        h[1] = (_Float16)(val.y * gs);
+                        h[2] = (_Float16)(val.z * gs);
+                        h[3] = (_Float16)(val.w * gs);
+                        *reinterpret_cast<half4v *>(p.yg + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch) = h;
+                    }
                 }
             }
         }

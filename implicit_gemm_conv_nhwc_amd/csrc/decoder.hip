@@ -218,7 +218,8 @@ void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Row
         if (u.has_up) {
             const int fr = feed ? feed[s].n() : rows;
             upd(pl.max_xn, (int64_t)fr * W * cp);
-            upd(pl.max_xg, (int64_t)fr * W * cp);
+            // the last resnet's conv2 casts all its rows; else only the fed ones
+            upd(pl.max_xg, (int64_t)(u.n_res > 0 ? rows : fr) * W * cp);
             rows = 2 * fr;
             W *= 2;
             cp = u.up.cout_p;
@@ -319,7 +320,7 @@ struct Run {
     _Float16 *xn, *xg, *q16, *k16, *vt16, *P;
 
     void conv(int mode, const _Float16 *in, int H, int W, const ig_conv_w &cw, const float *bias,
-              float oscale, int acc, float *out)
+              float oscale, int acc, float *out, _Float16 *yg = nullptr)
     {
         IgemmArgs a{};
         a.a = in;
@@ -338,6 +339,12 @@ struct Run {
         a.oscale = oscale;
         a.accumulate = acc;
         a.out_f16 = 0;
+        if (yg) {
+            // the guarded cast of the result instead of the result
+            a.yg = yg;
+            a.gscale = ldexpf(1.f, -g);
+            a.write_out = 0;
+        }
         launch_igemm(mode, a, s);
     }
 
@@ -403,20 +410,27 @@ struct Run {
         for (int st = s0; st < s1; ++st) {
             const ig_up_w &u = d.ups[st];
             for (int k = 0; k < u.n_res; ++k) {
-                resnet(u.res[k], cur.n(), W, cp);
+                // a stage's last resnet before its up conv emits the
+                // guarded cast itself
+                const bool last = u.has_up && k == u.n_res - 1;
+                resnet(u.res[k], cur.n(), W, cp, last ? xg : nullptr);
                 cp = u.res[k].c2.cout_p;
             }
             if (u.has_up) {
                 const Rows f = feed ? feed[st] : cur;
                 const int64_t skip = (int64_t)(f.lo - cur.lo) * W;
-                launch_guard_cast(x + skip * cp, f.n() * W, cp, nullptr, g, xg, s);
+                const _Float16 *up_in = xg + skip * cp;
+                if (u.n_res == 0) {
+                    launch_guard_cast(x + skip * cp, f.n() * W, cp, nullptr, g, xg, s);
+                    up_in = xg;
+                }
                 if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout) {
                     // the last up conv's epilogue applies norm_out + SiLU; the
                     // f32 stream is not needed after it
-                    conv_norm(kConv3x3Up2, xg, f.n(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
+                    conv_norm(kConv3x3Up2, up_in, f.n(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
                     normed = true;
                 } else {
-                    conv(kConv3x3Up2, xg, f.n(), W, u.up, u.up.b, gs, 0, x);
+                    conv(kConv3x3Up2, up_in, f.n(), W, u.up, u.up.b, gs, 0, x);
                 }
                 cur = Rows{2 * f.lo, 2 * f.hi};
                 W *= 2;
@@ -447,8 +461,10 @@ struct Run {
         }
     }
 
-    // Rec::resnet with the combines folded into the epilogues
-    void resnet(const ig_resnet_w &r, int H, int W, int cp)
+    // Rec::resnet with the combines folded into the epilogues; with cast,
+    // conv2's epilogue emits the guarded f16 cast of the new stream into
+    // cast instead of the stream itself (the stage's up conv reads only that)
+    void resnet(const ig_resnet_w &r, int H, int W, int cp, _Float16 *cast = nullptr)
     {
         const int M = H * W;
         if (r.has_sc) {
@@ -464,11 +480,11 @@ struct Run {
             // goes to the h region (conv1 still reads xn)
             _Float16 *hn = reinterpret_cast<_Float16 *>(h);
             conv_norm(kConv3x3, xn, H, W, r.c1, r.c1.b, 1.f, r.g2, r.c1.cout, hn);
-            conv(kConv3x3, hn, H, W, r.c2, r.c2.b, 1.f, 1, x);
+            conv(kConv3x3, hn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast);
         } else {
             conv(kConv3x3, xn, H, W, r.c1, nullptr, 1.f, 0, h);
             launch_rmsnorm(h, M, r.c1.cout_p, r.c1.cout, r.c1.b, r.g2, 1, kEps, xn, s);
-            conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x);
+            conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast);
         }
     }
 

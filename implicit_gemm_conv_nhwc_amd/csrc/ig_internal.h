@@ -45,6 +45,11 @@ struct IgemmArgs {
     int norm_c, norm_silu;
     float norm_eps;
     int write_out = 1;
+    // 3x3 convs without the norm: the epilogue can also emit the guarded
+    // f16 copy f16(v * gscale) of the (accumulated) f32 result v into
+    // yg [M][ldc] -- the cast of the stream before an up conv
+    _Float16 *yg = nullptr;
+    float gscale = 1.f;
 };
 
 // Launch the MFMA implicit GEMM for `mode`; picks the tile shape. The 3x3

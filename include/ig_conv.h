@@ -156,6 +156,18 @@ int gemm1x1_acc(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int
 int rmsnorm_silu_f16(const float *x, int M, int cp, int c_real, const float *bias,
                      const float *gamma, int silu, float eps, uint16_t *y, void *stream);
 
+/* A 3x3 conv (mode 1) or up conv (mode 2) whose epilogue also emits the
+ * guarded f16 cast of its f32 result ([QI] `Rec::resnet` then
+ * `run_blocks`: a stage's last resnet adds conv2 into the stream, which is
+ * then cast, guarded, for the up conv):
+ *   v = oscale * conv(x, w) + bias (+ y[p][o] if accumulate)
+ *   y[p][o] = v (only if write_y);  yg[p][o] = f16( v * 2^-guard_log2 )
+ * Shapes as ig_conv_nhwc_ex; y: f32 [M][cout_p] (read if accumulate);
+ * yg: f16 [M][cout_p]. */
+int ig_conv3x3_guard_out_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
+                              const float *bias, float oscale, int accumulate, float *y, int write_y, int guard_log2,
+                              uint16_t *yg, void *stream);
+
 /* The same norm and, from the same read of x, the guarded cast of the raw
  * stream ([QI] `Rec::resnet`: a resnet whose shortcut takes the stream
  * normalises it for conv1 and casts it, guarded, for the 1x1 shortcut):

@@ -330,6 +330,44 @@ def test_conv_with_fused_norm(H, W, cin, cout, c_real, mode, silu, want_y):
         assert conv_err(gy, conv[:c_real])[2] <= 1e-4
 
 
+@pytest.mark.parametrize("H,W,cin,cout,mode,acc,write_y,g", [
+    (64, 64, 128, 128, 1, 1, 0, 8), (13, 29, 64, 256, 1, 1, 1, 8), (9, 13, 128, 64, 2, 0, 1, 4),
+    (40, 33, 192, 128, 1, 0, 0, 14), (128, 128, 512, 512, 1, 1, 0, 8)])
+def test_conv_with_guarded_cast_output(H, W, cin, cout, mode, acc, write_y, g):
+    """A 3x3 conv (or up conv) whose epilogue emits the guarded f16 cast of
+    its (accumulated) result: bit for bit the separate conv then guard_cast
+    (the same f32 value, the same scaling and rounding), and the f32 result
+    against the oracle's conv."""
+    seed = 500 + H + cout
+    x16 = synth.normal(18, seed, (H, W, cin), 1.0, np.float16)
+    w = synth.normal(18, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
+    b = synth.normal(18, seed + 2, (cout,), 0.02)
+    cin_p, cout_p = cpad(cin), cpad(cout)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    M = Ho * Wo
+    xd = dev(pad_last(x16.reshape(H * W, cin), cin_p))
+    pl = packed(w)
+    y0 = synth.normal(18, seed + 3, (M, cout_p), 1.0e6).astype(np.float32)  # a stream past f16's range
+    y = dev(y0)
+    yg = nan_f16((M, cout_p))
+    ig.conv3x3_guard_out_nhwc(xd, H, W, cin_p, mode, pl, cout_p, padded_vec(b, cout_p), 1.0, acc, y, write_y, g, yg)
+    yref = dev(y0)
+    ig.conv_nhwc_ex(xd, H, W, cin_p, mode, pl, cout_p, padded_vec(b, cout_p), 1.0, acc, yref)
+    ygref = nan_f16((M, cout_p))
+    ig.guard_cast(yref, M, cout_p, None, g, ygref)
+    torch.cuda.synchronize()
+    assert torch.equal(yg.view(torch.int16), ygref.view(torch.int16))
+    if write_y:
+        assert torch.equal(y, yref)
+    else:
+        assert torch.equal(y, dev(y0))  # the f32 result is not stored
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    conv = (O.conv2d_up2(xc, w) if mode == 2 else O.conv2d(xc, w)) + b[:, None, None]
+    want = conv + (nhwc_to_chw(y0[:, :cout].astype(np.float64), Ho, Wo) if acc else 0.0)
+    got = nhwc_to_chw(host(yref)[:, :cout].astype(np.float64), Ho, Wo)
+    assert np.max(np.abs(got - want)) <= 2e-3 * np.sqrt(np.mean(conv ** 2)) + 1e-7 * np.max(np.abs(want))
+
+
 def test_conv_fused_norm_needs_one_tile_per_pixel():
     with pytest.raises(ig.IgError) as e:
         z = dev(np.zeros((4, 64), np.float16))
