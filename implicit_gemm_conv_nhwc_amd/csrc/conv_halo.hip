@@ -22,16 +22,20 @@
 //    the 16-channel slice of all nine taps' weights (one contiguous block
 //    of the [cin_p/16][9][cout_p][16] plane). All nine taps read the same
 //    patch at shifted offsets, so every input byte is fetched once per tile;
-//  * stages are double-buffered in LDS and filled by direct-to-LDS loads
-//    (global/buffer_load ... lds): the next stage streams in while the
+//  * stages are double-buffered in LDS and filled by direct-to-LDS buffer
+//    loads (buffer_load ... lds): the next stage streams in while the
 //    current one feeds 72 MFMAs per wave, with no register staging and one
 //    barrier per stage. A wave issues its share of the next stage's loads a
-//    few at a time between its MFMA groups (patch loads first), so no wave
-//    waits on a burst of load issues before its first MFMA. Loads past the
-//    image return zero, which is the convolution's zero padding;
+//    few at a time between its first seven MFMA groups (patch loads first),
+//    so no wave waits on a burst of load issues before its first MFMA and
+//    the last loads have two groups' time to land. Loads past the image
+//    return zero, which is the convolution's zero padding;
 //  * for each tap column dx a wave loads the fragments of the patch rows it
 //    needs once and uses them for the three tap rows dy (output row r at
-//    tap row dy reads patch row r + dy; for the upsample, (r + dy + 1) / 2);
+//    tap row dy reads patch row r + dy; for the upsample, (r + dy + 1) / 2).
+//    Each tap group reads the next group's weight fragments (and, at the
+//    last dy, the next column's patch fragments) before its own MFMAs, so
+//    the LDS latency hides behind them;
 //  * LDS holds a pixel's (or an output channel's) 16 channels as two
 //    16-byte halves, the halves swapped on every other group of 8
 //    columns: a fragment read (32 lanes on consecutive columns, the other
@@ -63,6 +67,7 @@ constexpr int TH = 16;   // output rows per tile
 constexpr int TW = 32;   // output columns per tile
 constexpr int CK = 16;   // input channels per stage
 constexpr int FM = 4;    // output rows per wave
+constexpr int DG = 7;    // tap groups that issue the next stage's loads
 constexpr int kOOB = 0x7fffffff;
 
 template <int MODE>
@@ -135,9 +140,13 @@ void k_conv_halo(IgemmArgs p)
 
     const __amdgpu_buffer_rsrc_t a_src = make_rsrc(p.a, (uint32_t)H * W * cin_p * 2);
     // stage st of the blocked plane [cin_p/16][9][cout_p][16]
-    const int64_t b_stage = (int64_t)9 * cout_p * CK;
-    // weight unit (n, stored half) holds channel half stored ^ bit 3 of n
-    const _Float16 *b_tile = p.b + (int64_t)n0 * CK + (lane ^ ((lane >> 4) & 1)) * 8;
+    const int b_stage = 9 * cout_p * CK;
+    // weight unit (n, stored half) holds channel half stored ^ bit 3 of n.
+    // Both operands load through buffer resources (MUBUF): a FLAT-encoded
+    // LDS load would make the compiler drain every LDS read before each
+    // MFMA group.
+    const __amdgpu_buffer_rsrc_t b_src = make_rsrc(p.b, (uint32_t)(9 * cin_p) * cout_p * 2);
+    const int b_lane = ((int)n0 * CK + (lane ^ ((lane >> 4) & 1)) * 8) * 2;
 
     // this lane's patch source (stage 0 byte offset) for each patch load of
     // its wave: load index ii = wave + NW k covers units ii*64 .. ii*64+63
@@ -167,8 +176,9 @@ void k_conv_halo(IgemmArgs p)
                 const int jj = ii - A_INSTR;
                 const int tap = (jj * 64) / (2 * BN);
                 const int rem = jj * 64 - tap * (2 * BN);  // first (n, half) unit of this load
-                const _Float16 *src = b_tile + st * b_stage + (int64_t)tap * cout_p * CK + rem * 8;
-                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(base + A_PAD + jj * 64), 16, 0, 0);
+                const int soff = (st * b_stage + tap * cout_p * CK + rem * 8) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(b_src, (lds_void *)(base + A_PAD + jj * 64), 16, b_lane, soff,
+                                                         0, 0);
             }
         }
     };
@@ -189,36 +199,53 @@ void k_conv_halo(IgemmArgs p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // fragment loads: the patch rows tap column dx reads, and tap (dy, dx)'s
+    // weight fragments
+    auto load_a = [&](const u32x4 *sA, int dx, half8 *af) __attribute__((always_inline)) {
+        const int pc = G::pcol(fx, dx);
+        const int ph = fh ^ ((pc >> 3) & 1);
+#pragma unroll
+        for (int a = 0; a < AROWS; ++a) af[a] = __builtin_bit_cast(half8, sA[((ar0 + a) * PW + pc) * 2 + ph]);
+    };
+    auto load_b = [&](const u32x4 *sB, int tap, half8 *bf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bf[j] = __builtin_bit_cast(half8, sB[(tap * BN + wn * (BN / WN) + j * 32 + fx) * 2 + wh]);
+    };
+
     for (int st = 0; st < nst; ++st) {
         const int buf = st & 1;
         const u32x4 *sA = lds + buf * STAGE;
         const u32x4 *sB = sA + A_PAD;
+        // nine tap groups g = 3 dx + dy; each prefetches the next group's
+        // weight fragments (and, at the last dy of a column, the next
+        // column's patch fragments) before its MFMAs, so the LDS latency
+        // hides behind them
+        half8 af[2][AROWS], bf[2][FN];
+        load_a(sA, 0, af[0]);
+        load_b(sB, 0, bf[0]);
 #pragma unroll
-        for (int dx = 0; dx < 3; ++dx) {
-            half8 af[AROWS];
-            const int pc = G::pcol(fx, dx);
-            const int ph = fh ^ ((pc >> 3) & 1);
+        for (int g = 0; g < 9; ++g) {
+            const int dx = g / 3, dy = g % 3;
+            // the next stage's loads, spread over the first DG tap groups so
+            // the waves go straight to their MFMAs after the barrier and
+            // the last loads still have two groups' time to land
+            if (st + 1 < nst && g < DG)
+                issue(st + 1, buf ^ 1, (g * PER_WAVE + DG - 1) / DG, ((g + 1) * PER_WAVE + DG - 1) / DG);
+            if (g + 1 < 9) {
+                const int gn = g + 1;
+                load_b(sB, (gn % 3) * 3 + gn / 3, bf[gn & 1]);
+                if (dy == 2) load_a(sA, dx + 1, af[(dx + 1) & 1]);
+            }
+            // keep the prefetch ahead of this group's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            const half8 *a = af[dx & 1];
+            const half8 *b = bf[g & 1];
 #pragma unroll
-            for (int a = 0; a < AROWS; ++a)
-                af[a] = __builtin_bit_cast(half8, sA[((ar0 + a) * PW + pc) * 2 + ph]);
-#pragma unroll
-            for (int dy = 0; dy < 3; ++dy) {
-                const int tap = dy * 3 + dx;
-                // the next stage's loads, spread over the nine tap groups so
-                // the waves go straight to their MFMAs after the barrier
-                const int g = dx * 3 + dy;  // group order
-                if (st + 1 < nst) issue(st + 1, buf ^ 1, (g * PER_WAVE + 8) / 9, ((g + 1) * PER_WAVE + 8) / 9);
-                half8 bf[FN];
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bf[j] = __builtin_bit_cast(half8, sB[(tap * BN + wn * (BN / WN) + j * 32 + fx) * 2 + wh]);
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[G::arow(i, dy)], bf[j],
-                                                                           acc[i][j], 0, 0, 0);
-            }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[G::arow(i, dy)], b[j], acc[i][j], 0, 0, 0);
         }
         // the next stage has landed (own loads) and every wave is done with
         // this one (barrier)

@@ -6,114 +6,154 @@
 // GN_FIN_SRC / GN_APPLY_SRC and `gn`: bias on read, optional SiLU, f16 out).
 //
 // The pages reduce in two passes over memory (the sum, then the sum of
-// squared deviations). Here one pass suffices: each workgroup holds a chunk
-// of rows in registers, takes the chunk's per-group mean and then the
+// squared deviations). Here one pass suffices: a thread holds a batch of
+// rows of its channel quad in registers, takes the batch's mean and the
 // squared deviations from it (the two-pass formula, from registers), and
-// writes (count, mean, M2); a second kernel merges the chunks of a group
-// pairwise in f64 (Chan, Golub and LeVeque's update:
-// M2 = M2a + M2b + d^2 na nb / n, d = mean_b - mean_a), which is exact up
-// to rounding for any chunking; the apply kernel reads the stream once more.
-// HBM: two reads of the f32 stream and one f16 write.
+// folds them into running per-channel (count, mean, M2) with Chan, Golub
+// and LeVeque's update (M2 = M2a + M2b + d^2 na nb / n, d = mean_b -
+// mean_a), exact up to rounding for any split. Each of at most 1024
+// workgroups merges its threads' figures per group and writes one partial;
+// a second kernel merges a group's partials in f64 and turns the group
+// statistics into a per-channel scale and shift; the apply kernel reads the
+// stream once more. HBM: two reads of the f32 stream and one f16 write.
 #include "ig_internal.h"
 
 namespace ig {
 namespace {
 
-constexpr int RPT = 8;          // rows per thread in a stats chunk
+constexpr int RPT = 8;          // rows per thread in a batch
 constexpr int MAXT = 256;       // threads per stats workgroup (at most)
 constexpr int MAXG = 128;       // groups
+constexpr int MAXCHUNK = 1024;  // stats workgroups, i.e. partials per group
 
-__device__ __forceinline__ float silu1(float y) { return y / (1.0f + __expf(-y)); }
+__device__ __forceinline__ float silu1(float y) { return __fdividef(y, 1.0f + __expf(-y)); }
 
-// one workgroup per chunk of RL * RPT rows; thread (rl, q): channel quad q,
-// rows r0 + rl + RL k
-__global__ void k_gn_stats(const float *__restrict__ x, int M, int cp, int c_real, int cpg, int groups,
-                           const float *__restrict__ bias, float *__restrict__ part)
+// Chan, Golub and LeVeque's merge of (nb, mb, m2b) into (n, m, m2)
+__device__ __forceinline__ void chan_merge(float &n, float &m, float &m2, float nb, float mb, float m2b)
 {
-    __shared__ float ch_sum[MAXT * 4 / 1];  // per thread, reduced below
-    __shared__ float g_mean[MAXG];
+    const float nn = n + nb, wb = nb / nn, d = mb - m;
+    m += d * wb;
+    m2 += m2b + d * d * n * wb;
+    n = nn;
+}
+
+// Workgroup w walks the batches w, w + gridDim.x, ... of RL * RPT rows.
+// Thread (rl, q) holds channel quad q of rows rl + RL k of a batch in
+// registers, takes the batch's per-channel mean and squared deviations from
+// it, and merges them into its running per-channel (count, mean, M2). At
+// the end the workgroup merges its threads' per-channel figures into
+// per-group ones and writes them as chunk w of each group.
+__global__ __launch_bounds__(256) void k_gn_stats(const float *__restrict__ x, int M, int cp, int cpg, int groups,
+                                                  const float *__restrict__ bias, int64_t nbatch,
+                                                  float *__restrict__ part)
+{
+    __shared__ float s_mean[MAXT * 4], s_m2[MAXT * 4];  // [rl][cp]
+    __shared__ float s_n[MAXT];                         // [rl]
     const int nq = cp / 4;
     const int RL = blockDim.x / nq;
     const int t = threadIdx.x, q = t % nq, rl = t / nq;
     const int rows = RL * RPT;
-    const int64_t r0 = (int64_t)blockIdx.x * rows;
-    float4 v[RPT];
-    bool ok[RPT];
-    float4 b = {0.f, 0.f, 0.f, 0.f};
-    if (bias) b = reinterpret_cast<const float4 *>(bias)[q];
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-        const int64_t r = r0 + rl + (int64_t)RL * k;
-        ok[k] = r < M;
-        if (ok[k]) {
-            v[k] = reinterpret_cast<const float4 *>(x + r * cp)[q];
-            v[k].x += b.x;
-            v[k].y += b.y;
-            v[k].z += b.z;
-            v[k].w += b.w;
-        } else {
-            v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-    int nrows = M - (int)r0;
-    if (nrows > rows) nrows = rows;
-    // pass 1 (registers): per-channel sums -> per-group means
-    float4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-        s.x += v[k].x;
-        s.y += v[k].y;
-        s.z += v[k].z;
-        s.w += v[k].w;
-    }
-    float *cs = ch_sum;  // [RL][cp]
-    cs[rl * cp + 4 * q + 0] = s.x;
-    cs[rl * cp + 4 * q + 1] = s.y;
-    cs[rl * cp + 4 * q + 2] = s.z;
-    cs[rl * cp + 4 * q + 3] = s.w;
-    __syncthreads();
-    if (t < groups) {
-        float a = 0.f;
-        for (int c = t * cpg; c < (t + 1) * cpg; ++c)
-            for (int l = 0; l < RL; ++l) a += cs[l * cp + c];
-        g_mean[t] = a / (float)(nrows * cpg);
-    }
-    __syncthreads();
-    // pass 2 (registers): squared deviations from the chunk's group mean
-    float d2[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int c = 4 * q + e;
-        if (c >= c_real) continue;
-        const float m = g_mean[c / cpg];
+    const float4 b = bias ? reinterpret_cast<const float4 *>(bias)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float n = 0.f, mean[4] = {0.f, 0.f, 0.f, 0.f}, m2[4] = {0.f, 0.f, 0.f, 0.f};
+    // rows r0 + RL k of a batch grow with k: the valid ones are a prefix
+    // (rows past the end load row M - 1, unused: no branch around a load,
+    // so the compiler can keep the next batch's loads in flight)
+    auto load = [&](int64_t bt, float4 *v) __attribute__((always_inline)) {
+        const int64_t r0 = bt * rows + rl;
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            if (!ok[k]) continue;
-            const float val = e == 0 ? v[k].x : e == 1 ? v[k].y : e == 2 ? v[k].z : v[k].w;
-            const float d = val - m;
-            d2[e] += d * d;
+            const int64_t r = r0 + (int64_t)RL * k;
+            v[k] = reinterpret_cast<const float4 *>(x + (r < M ? r : (int64_t)M - 1) * cp)[q];
         }
+    };
+    // fold batch bt (held in v) into the running figures
+    auto fold = [&](int64_t bt, float4 *v) __attribute__((always_inline)) {
+        int64_t left = (int64_t)M - (bt * rows + rl);  // rows of this lane still in range
+        left = left < 0 ? 0 : (left > rows ? rows : left);
+        const int nb = ((int)left + RL - 1) / RL;
+        if (nb == 0) return;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            if (k < nb) {
+                v[k].x += b.x;
+                v[k].y += b.y;
+                v[k].z += b.z;
+                v[k].w += b.w;
+            }
+        }
+        float bm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            if (k < nb) {
+                bm[0] += v[k].x;
+                bm[1] += v[k].y;
+                bm[2] += v[k].z;
+                bm[3] += v[k].w;
+            }
+        }
+        const float inb = 1.f / (float)nb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bm[e] *= inb;
+        float bq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            if (k < nb) {
+                const float d0 = v[k].x - bm[0], d1 = v[k].y - bm[1], d2 = v[k].z - bm[2], d3 = v[k].w - bm[3];
+                bq[0] += d0 * d0;
+                bq[1] += d1 * d1;
+                bq[2] += d2 * d2;
+                bq[3] += d3 * d3;
+            }
+        }
+        const float nn = n + (float)nb, wb = (float)nb / nn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float d = bm[e] - mean[e];
+            mean[e] += d * wb;
+            m2[e] += bq[e] + d * d * n * wb;
+        }
+        n = nn;
+    };
+    // two register sets in turn: one batch's loads are in flight while the
+    // other is folded
+    float4 v[RPT], w[RPT];
+    const int64_t step = gridDim.x;
+    load(blockIdx.x, v);
+    for (int64_t bt = blockIdx.x; bt < nbatch; bt += 2 * step) {
+        load(bt + step, w);
+        fold(bt, v);
+        if (bt + step >= nbatch) break;
+        load(bt + 2 * step, v);
+        fold(bt + step, w);
     }
-    cs[rl * cp + 4 * q + 0] = d2[0];
-    cs[rl * cp + 4 * q + 1] = d2[1];
-    cs[rl * cp + 4 * q + 2] = d2[2];
-    cs[rl * cp + 4 * q + 3] = d2[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        s_mean[rl * cp + 4 * q + e] = mean[e];
+        s_m2[rl * cp + 4 * q + e] = m2[e];
+    }
+    if (q == 0) s_n[rl] = n;  // every quad of a row lane saw the same rows
     __syncthreads();
     if (t < groups) {
-        float a = 0.f;
-        for (int c = t * cpg; c < (t + 1) * cpg; ++c)
-            for (int l = 0; l < RL; ++l) a += cs[l * cp + c];
+        float gn = 0.f, gm = 0.f, gq = 0.f;
+        for (int l = 0; l < RL; ++l) {
+            const float nl = s_n[l];
+            if (nl <= 0.f) continue;
+            for (int c = t * cpg; c < (t + 1) * cpg; ++c) chan_merge(gn, gm, gq, nl, s_mean[l * cp + c], s_m2[l * cp + c]);
+        }
         float *o = part + ((int64_t)t * gridDim.x + blockIdx.x) * 3;  // [group][chunk][3]
-        o[0] = (float)(nrows * cpg);
-        o[1] = g_mean[t];
-        o[2] = a;
+        o[0] = gn;
+        o[1] = gm;
+        o[2] = gq;
     }
 }
 
-// one workgroup per group: merge its chunks' (n, mean, M2) in f64 and write
-// (mean, 1 / sqrt(var + eps))
-__global__ __launch_bounds__(256) void k_gn_final(const float *__restrict__ part, int nchunk, int groups,
-                                                  float eps, float *__restrict__ stat)
+// one workgroup per group: merge its chunks' (n, mean, M2) in f64, then
+// write the group's per-channel scale inv * gamma and shift
+// beta - mean * inv * gamma (workgroup 0 also zeroes the pad channels')
+__global__ __launch_bounds__(256) void k_gn_final(const float *__restrict__ part, int nchunk, int cp, int c_real,
+                                                  int cpg, float eps, const float *__restrict__ gamma,
+                                                  const float *__restrict__ beta, float *__restrict__ sc,
+                                                  float *__restrict__ sh)
 {
     __shared__ double sn[256], sm[256], s2[256];
     const int g = blockIdx.x, t = threadIdx.x;
@@ -143,47 +183,54 @@ __global__ __launch_bounds__(256) void k_gn_final(const float *__restrict__ part
         }
         __syncthreads();
     }
-    if (t == 0) {
-        const double var = sn[0] > 0.0 ? s2[0] / sn[0] : 0.0;
-        stat[2 * g] = (float)sm[0];
-        stat[2 * g + 1] = (float)(1.0 / sqrt(var + (double)eps));
+    const double var = sn[0] > 0.0 ? s2[0] / sn[0] : 0.0;
+    const float mean = (float)sm[0], inv = (float)(1.0 / sqrt(var + (double)eps));
+    for (int c = g * cpg + t; c < (g + 1) * cpg; c += 256) {
+        const float a = inv * gamma[c];
+        sc[c] = a;
+        sh[c] = beta[c] - mean * a;
     }
+    if (g == 0)
+        for (int c = c_real + t; c < cp; c += 256) {
+            sc[c] = 0.f;
+            sh[c] = 0.f;
+        }
 }
 
-// y = ((x + b) - mean) * inv * gamma + beta (+ SiLU), f16; pad channels 0.
-// Thread (rl, q) keeps channel quad q (its bias, gamma, beta and group
-// statistics in registers) and walks rows rl, rl + RL, ...
-__global__ __launch_bounds__(256) void k_gn_apply(const float *__restrict__ x, int M, int cp, int c_real, int cpg,
-                                                  const float *__restrict__ bias, const float *__restrict__ stat,
-                                                  const float *__restrict__ gamma, const float *__restrict__ beta,
-                                                  int silu, _Float16 *__restrict__ y)
+// y = (x + b) * scale + shift (+ SiLU), f16, with the per-channel scale
+// inv * gamma and shift beta - mean * inv * gamma (0 on pad channels).
+// Workgroup w covers rows w RL AU .. (w + 1) RL AU - 1; thread (rl, q)
+// issues the loads of its AU rows (channel quad q) first.
+constexpr int AU = 2;  // rows per thread in the apply kernel
+__global__ __launch_bounds__(256) void k_gn_apply(const float *__restrict__ x, int M, int cp,
+                                                  const float *__restrict__ bias, const float *__restrict__ scale,
+                                                  const float *__restrict__ shift, int silu, _Float16 *__restrict__ y)
 {
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int nq = cp / 4;
     const int RL = blockDim.x / nq;
     const int q = threadIdx.x % nq, rl = threadIdx.x / nq;
-    float b[4] = {0.f, 0.f, 0.f, 0.f}, sc[4], sh[4];
+    const int64_t r0 = (int64_t)blockIdx.x * RL * AU + rl;
+    f32x4 v[AU];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int c = 4 * q + e;
-        if (bias) b[e] = bias[c];
-        if (c < c_real) {
-            const int g = c / cpg;
-            // y = v * sc + sh with sc = inv * gamma, sh = beta - mean * inv * gamma
-            sc[e] = stat[2 * g + 1] * gamma[c];
-            sh[e] = beta[c] - stat[2 * g] * sc[e];
-        } else {
-            sc[e] = 0.f;
-            sh[e] = 0.f;
-        }
+    for (int k = 0; k < AU; ++k) {
+        const int64_t r = r0 + (int64_t)RL * k;
+        // the stream's last read here: a streaming (nontemporal) load (rows
+        // past the end load row M - 1 and are not written)
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + (r < M ? r : (int64_t)M - 1) * cp) + q);
     }
-    for (int64_t r = (int64_t)blockIdx.x * RL + rl; r < M; r += (int64_t)gridDim.x * RL) {
-        const float4 v = reinterpret_cast<const float4 *>(x + r * cp)[q];
-        const float vv[4] = {v.x, v.y, v.z, v.w};
+    const float4 b = bias ? reinterpret_cast<const float4 *>(bias)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 a4 = reinterpret_cast<const float4 *>(scale)[q], s4 = reinterpret_cast<const float4 *>(shift)[q];
+    const float bb[4] = {b.x, b.y, b.z, b.w}, sc[4] = {a4.x, a4.y, a4.z, a4.w}, sh[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int k = 0; k < AU; ++k) {
+        const int64_t r = r0 + (int64_t)RL * k;
+        if (r >= M) break;
         half4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float o = (vv[e] + b[e]) * sc[e] + sh[e];
+            float o = (v[k][e] + bb[e]) * sc[e] + sh[e];
             if (silu) o = silu1(o);
             h[e] = (_Float16)o;
         }
@@ -203,12 +250,13 @@ int stats_threads(int cp)
 int64_t gn_chunks(int M, int cp)
 {
     const int rows = (stats_threads(cp) / (cp / 4)) * RPT;
-    return ((int64_t)M + rows - 1) / rows;
+    const int64_t nbatch = ((int64_t)M + rows - 1) / rows;
+    return nbatch < MAXCHUNK ? nbatch : MAXCHUNK;
 }
 
 size_t gn_workspace_bytes(int M, int cp, int groups)
 {
-    return (size_t)gn_chunks(M, cp) * groups * 3 * sizeof(float) + (size_t)groups * 2 * sizeof(float) + 256;
+    return ((size_t)gn_chunks(M, cp) * groups * 3 + (size_t)cp * 2) * sizeof(float) + 256;
 }
 
 bool gn_supported(int cp, int c_real, int groups)
@@ -224,16 +272,20 @@ void launch_groupnorm(const float *x, int M, int cp, int c_real, int groups, con
     if (M <= 0) return;
     const int nt = stats_threads(cp);
     const int64_t nchunk = gn_chunks(M, cp);
+    const int rows = (nt / (cp / 4)) * RPT;
+    const int64_t nbatch = ((int64_t)M + rows - 1) / rows;
     float *part = reinterpret_cast<float *>(ws);
-    float *stat = part + nchunk * groups * 3;
+    // the per-channel table, 16-byte aligned for the apply kernel's vector
+    // loads (cp is a multiple of 4; the workspace holds 256 bytes of slack)
+    const uintptr_t tab = (reinterpret_cast<uintptr_t>(part + nchunk * groups * 3) + 15) & ~(uintptr_t)15;
+    float *scale = reinterpret_cast<float *>(tab), *shift = scale + cp;
     const int cpg = c_real / groups;
-    hipLaunchKernelGGL(k_gn_stats, dim3((unsigned)nchunk), dim3(nt), 0, s, x, M, cp, c_real, cpg, groups, bias, part);
-    hipLaunchKernelGGL(k_gn_final, dim3(groups), dim3(256), 0, s, part, (int)nchunk, groups, eps, stat);
+    hipLaunchKernelGGL(k_gn_stats, dim3((unsigned)nchunk), dim3(nt), 0, s, x, M, cp, cpg, groups, bias, nbatch, part);
+    hipLaunchKernelGGL(k_gn_final, dim3(groups), dim3(256), 0, s, part, (int)nchunk, cp, c_real, cpg, eps, gamma, beta,
+                       scale, shift);
     const int rl = nt / (cp / 4);
-    int64_t blocks = ((int64_t)M + rl - 1) / rl;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(k_gn_apply, dim3((unsigned)blocks), dim3(nt), 0, s, x, M, cp, c_real, cpg, bias, stat, gamma,
-                       beta, silu, y);
+    const int64_t blocks = ((int64_t)M + (int64_t)rl * AU - 1) / ((int64_t)rl * AU);
+    hipLaunchKernelGGL(k_gn_apply, dim3((unsigned)blocks), dim3(nt), 0, s, x, M, cp, bias, scale, shift, silu, y);
 }
 
 }  // namespace ig
