@@ -47,8 +47,11 @@ static int check_conv(const void *x, int H, int W, int cin_p, const void *w, int
     if (H < 0 || W < 0) return fail(IG_EINVAL, "negative image size %dx%d", H, W);
     if (cin_p <= 0 || cin_p % 64) return fail(IG_EUNSUPPORTED, "cin_p=%d is not a positive multiple of 64", cin_p);
     if (cout_p <= 0 || cout_p % 64) return fail(IG_EUNSUPPORTED, "cout_p=%d is not a positive multiple of 64", cout_p);
+    if (cin_p > kConvMaxChannels || cout_p > kConvMaxChannels)
+        return fail(IG_EUNSUPPORTED, "cin_p=%d / cout_p=%d exceed %d", cin_p, cout_p, kConvMaxChannels);
     const int64_t mout = (int64_t)H * W * (mode == 2 ? 4 : 1);
-    if ((int64_t)H * W * cin_p >= (1LL << 31) || mout * cout_p >= (1LL << 40) || mout >= (1LL << 31))
+    if ((int64_t)H * W * cin_p >= (1LL << 31) || mout * cout_p >= (1LL << 40) || mout >= (1LL << 31) ||
+        (mode != 0 && (int64_t)H * W * cin_p * 2 >= kConvInMaxBytes))
         return fail(IG_EUNSUPPORTED, "image %dx%d with %d/%d channels is too large", H, W, cin_p, cout_p);
     if (H == 0 || W == 0) {
         *empty = true;

@@ -68,7 +68,9 @@ constexpr int TW = 32;   // output columns per tile
 constexpr int CK = 16;   // input channels per stage
 constexpr int FM = 4;    // output rows per wave
 constexpr int DG = 7;    // tap groups that issue the next stage's loads
-constexpr int kOOB = 0x7fffffff;
+// patch offset of pixels outside the image: past every input (inputs stay
+// below kConvInMaxBytes), also after the stages' channel offsets are added
+constexpr int kOOB = (int)kConvInMaxBytes;
 
 template <int MODE>
 struct Geo {
@@ -84,10 +86,35 @@ struct Geo {
     __device__ static int pcol(int x, int dx) { return (MODE == kConv3x3) ? x + dx : ((x + dx + 1) >> 1); }
 };
 
+// Stage buffer size (16-byte units): the patch, padded to whole wave loads,
+// then the nine taps' weights. A workgroup may walk several tiles only when
+// its f32 output staging (4 rows x TW x BN) fits one stage buffer, the one
+// the next tile's first stage is not landing in.
+template <int MODE, int BN>
+constexpr int stage_units()
+{
+    return (Geo<MODE>::PH * Geo<MODE>::PW * 2 + 63) / 64 * 64 + 9 * BN * 2;
+}
+template <int MODE, int BN>
+constexpr bool can_walk()
+{
+    return 4 * TW * BN * 4 <= stage_units<MODE, BN>() * 16;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
+
+// A tile: its origin, and a lane's sources for the tile's stage loads: the
+// weight offset, and the patch offset (stage 0, bytes) of each patch load of
+// its wave (load index ii = wave + NW k covers units ii*64 .. ii*64+63).
+// (At namespace scope: a class local to the kernel template keeps hipcc's
+// host pass from emitting the kernel's launch stub.)
+struct Tile {
+    int y0, x0, n0, b_lane;
+    int8v aoff;
+};
 
 template <int MODE, int BN, int NW, bool NORM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
@@ -106,6 +133,7 @@ void k_conv_halo(IgemmArgs p)
     constexpr int PER_WAVE = (T_INSTR + NW - 1) / NW;
     constexpr int A_PER_WAVE = (A_INSTR + NW - 1) / NW;  // patch loads of the busiest wave
     constexpr int STAGE = A_PAD + B_UNITS;               // units per stage buffer
+    static_assert(STAGE == stage_units<MODE, BN>(), "stage layout");
     constexpr int FN = BN / (32 * WN);                   // 32-channel fragments per wave
     static_assert(B_UNITS % 64 == 0, "whole weight loads");
     static_assert(A_PER_WAVE <= 8, "patch offsets per lane");
@@ -117,7 +145,8 @@ void k_conv_halo(IgemmArgs p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+    // uniform (scalar branches); the mask tells the compiler wave < NW
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
     const int wm = wave / WN, wn = wave % WN;
     const int fx = lane & 31;  // tile column (A) / channel within a fragment (B)
     const int fh = lane >> 5;  // channel half of the stage: 8*fh .. 8*fh+7
@@ -128,15 +157,25 @@ void k_conv_halo(IgemmArgs p)
     const int tiles_x = (Wout + TW - 1) / TW;
     const int n_tiles = cout_p / BN;
 
-    // XCD-aware tile order (channel tiles fastest, then columns, then rows)
+    // Tile schedule (channel tiles fastest, then columns, then rows). With a
+    // grid that is a multiple of 8, XCD x (workgroups bid = x mod 8) takes
+    // the contiguous tile range [x T / 8, (x + 1) T / 8), so neighbouring
+    // tiles share halos and weights in its L2; its j-th workgroup walks
+    // tiles base + j, base + j + G / 8, ... (one tile when G = T).
+    const int T = ((Hout + TH - 1) / TH) * tiles_x * n_tiles;
     const int nblk = gridDim.x;
-    int bid = blockIdx.x;
-    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-    const int ntile = bid % n_tiles;
-    const int t2 = bid / n_tiles;
-    const int y0 = (t2 / tiles_x) * TH, x0 = (t2 % tiles_x) * TW, n0 = ntile * BN;
-    const int py0 = (MODE == kConv3x3) ? y0 - 1 : y0 / 2 - 1;
-    const int px0 = (MODE == kConv3x3) ? x0 - 1 : x0 / 2 - 1;
+    int t, t_end, t_step;
+    if ((nblk & 7) == 0) {
+        const int xcd = blockIdx.x & 7;
+        t = (int)((int64_t)xcd * T / 8) + (blockIdx.x >> 3);
+        t_end = (int)((int64_t)(xcd + 1) * T / 8);
+        t_step = nblk >> 3;
+    } else {
+        t = blockIdx.x;
+        t_end = T;
+        t_step = nblk;
+    }
+    if (t >= t_end) return;  // uniform: the whole workgroup leaves
 
     const __amdgpu_buffer_rsrc_t a_src = make_rsrc(p.a, (uint32_t)H * W * cin_p * 2);
     // stage st of the blocked plane [cin_p/16][9][cout_p][16]
@@ -146,58 +185,56 @@ void k_conv_halo(IgemmArgs p)
     // LDS load would make the compiler drain every LDS read before each
     // MFMA group.
     const __amdgpu_buffer_rsrc_t b_src = make_rsrc(p.b, (uint32_t)(9 * cin_p) * cout_p * 2);
-    const int b_lane = ((int)n0 * CK + (lane ^ ((lane >> 4) & 1)) * 8) * 2;
+    const int b_half = (lane ^ ((lane >> 4) & 1)) * 8 * 2;
 
-    // this lane's patch source (stage 0 byte offset) for each patch load of
-    // its wave: load index ii = wave + NW k covers units ii*64 .. ii*64+63
-    int8v aoff = {kOOB, kOOB, kOOB, kOOB, kOOB, kOOB, kOOB, kOOB};
+    auto make_tile = [&](int tt) __attribute__((always_inline)) {
+        Tile r;
+        const int ntile = tt % n_tiles;
+        const int t2 = tt / n_tiles;
+        r.y0 = (t2 / tiles_x) * TH;
+        r.x0 = (t2 % tiles_x) * TW;
+        r.n0 = ntile * BN;
+        r.b_lane = r.n0 * CK * 2 + b_half;
+        const int py0 = (MODE == kConv3x3) ? r.y0 - 1 : r.y0 / 2 - 1;
+        const int px0 = (MODE == kConv3x3) ? r.x0 - 1 : r.x0 / 2 - 1;
+        r.aoff = int8v{kOOB, kOOB, kOOB, kOOB, kOOB, kOOB, kOOB, kOOB};
 #pragma unroll
-    for (int k = 0; k < A_PER_WAVE; ++k) {
-        const int u = (wave + NW * k) * 64 + lane;
-        const int pix = u >> 1;
-        const int pr = pix / PW, pc = pix - (pix / PW) * PW;
-        const int half = (u & 1) ^ ((pc >> 3) & 1);  // stored half -> channel half
-        const int sy = py0 + pr, sx = px0 + pc;
-        const bool ok = (u < A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
-        aoff[k] = ok ? ((sy * W + sx) * cin_p + half * 8) * 2 : kOOB;
-    }
+        for (int k = 0; k < A_PER_WAVE; ++k) {
+            const int u = (wave + NW * k) * 64 + lane;
+            const int pix = u >> 1;
+            const int pr = pix / PW, pc = pix - (pix / PW) * PW;
+            const int half = (u & 1) ^ ((pc >> 3) & 1);  // stored half -> channel half
+            const int sy = py0 + pr, sx = px0 + pc;
+            const bool ok = (u < A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
+            r.aoff[k] = ok ? ((sy * W + sx) * cin_p + half * 8) * 2 : kOOB;
+        }
+        return r;
+    };
 
-    // issue the direct-to-LDS loads of stage st into buffer buf
+    // issue the direct-to-LDS loads of stage st of tile tl into buffer buf:
     // loads k in [k0, k1) of this wave (patch loads come first)
-    auto issue = [&](int st, int buf, int k0, int k1) __attribute__((always_inline)) {
+    auto issue = [&](const Tile &tl, int st, int buf, int k0, int k1) __attribute__((always_inline)) {
         u32x4 *base = lds + buf * STAGE;
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
             const int ii = wave + NW * k;
             if (ii < A_INSTR) {
-                const int off = aoff[k] == kOOB ? kOOB : aoff[k] + st * CK * 2;
+                const int off = tl.aoff[k] + st * CK * 2;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(a_src, (lds_void *)(base + ii * 64), 16, off, 0, 0, 0);
             } else if (ii < T_INSTR) {
                 const int jj = ii - A_INSTR;
                 const int tap = (jj * 64) / (2 * BN);
                 const int rem = jj * 64 - tap * (2 * BN);  // first (n, half) unit of this load
                 const int soff = (st * b_stage + tap * cout_p * CK + rem * 8) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(b_src, (lds_void *)(base + A_PAD + jj * 64), 16, b_lane, soff,
-                                                         0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(b_src, (lds_void *)(base + A_PAD + jj * 64), 16, tl.b_lane,
+                                                         soff, 0, 0);
             }
         }
     };
 
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
     const int ar0 = G::row0(wm);
     const int nst = cin_p / CK;
     const int wh = fh ^ ((fx >> 3) & 1);  // stored half of this lane's weight fragment
-
-    issue(0, 0, 0, PER_WAVE);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
 
     // fragment loads: the patch rows tap column dx reads, and tap (dy, dx)'s
     // weight fragments
@@ -213,45 +250,70 @@ void k_conv_halo(IgemmArgs p)
             bf[j] = __builtin_bit_cast(half8, sB[(tap * BN + wn * (BN / WN) + j * 32 + fx) * 2 + wh]);
     };
 
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        const u32x4 *sA = lds + buf * STAGE;
-        const u32x4 *sB = sA + A_PAD;
-        // nine tap groups g = 3 dx + dy; each prefetches the next group's
-        // weight fragments (and, at the last dy of a column, the next
-        // column's patch fragments) before its MFMAs, so the LDS latency
-        // hides behind them
-        half8 af[2][AROWS], bf[2][FN];
-        load_a(sA, 0, af[0]);
-        load_b(sB, 0, bf[0]);
+    Tile cur = make_tile(t);
+    issue(cur, 0, 0, 0, PER_WAVE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    int gs = 0;  // stages run so far: stage gs sits in buffer gs & 1
+    for (; t < t_end; t += t_step) {
+        const bool has_next = can_walk<MODE, BN>() && t + t_step < t_end;
+        const Tile nxt = make_tile(has_next ? t + t_step : t);
+
+        f32x16 acc[FM][FN];
 #pragma unroll
-        for (int g = 0; g < 9; ++g) {
-            const int dx = g / 3, dy = g % 3;
-            // the next stage's loads, spread over the first DG tap groups so
-            // the waves go straight to their MFMAs after the barrier and
-            // the last loads still have two groups' time to land
-            if (st + 1 < nst && g < DG)
-                issue(st + 1, buf ^ 1, (g * PER_WAVE + DG - 1) / DG, ((g + 1) * PER_WAVE + DG - 1) / DG);
-            if (g + 1 < 9) {
-                const int gn = g + 1;
-                load_b(sB, (gn % 3) * 3 + gn / 3, bf[gn & 1]);
-                if (dy == 2) load_a(sA, dx + 1, af[(dx + 1) & 1]);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+        for (int st = 0; st < nst; ++st, ++gs) {
+            const int buf = gs & 1;
+            const u32x4 *sA = lds + buf * STAGE;
+            const u32x4 *sB = sA + A_PAD;
+            // the loads issued during this stage: the tile's next stage, or
+            // after its last stage the next tile's first
+            const bool last = st + 1 == nst;
+            const bool do_issue = !last || has_next;
+            const Tile &src = last ? nxt : cur;
+            const int sst = last ? 0 : st + 1;
+            // nine tap groups g = 3 dx + dy; each prefetches the next group's
+            // weight fragments (and, at the last dy of a column, the next
+            // column's patch fragments) before its MFMAs, so the LDS latency
+            // hides behind them
+            half8 af[2][AROWS], bf[2][FN];
+            load_a(sA, 0, af[0]);
+            load_b(sB, 0, bf[0]);
+#pragma unroll
+            for (int g = 0; g < 9; ++g) {
+                const int dx = g / 3, dy = g % 3;
+                // the next stage's loads, spread over the first DG tap groups so
+                // the waves go straight to their MFMAs after the barrier and
+                // the last loads still have two groups' time to land
+                if (do_issue && g < DG)
+                    issue(src, sst, buf ^ 1, (g * PER_WAVE + DG - 1) / DG, ((g + 1) * PER_WAVE + DG - 1) / DG);
+                if (g + 1 < 9) {
+                    const int gn = g + 1;
+                    load_b(sB, (gn % 3) * 3 + gn / 3, bf[gn & 1]);
+                    if (dy == 2) load_a(sA, dx + 1, af[(dx + 1) & 1]);
+                }
+                // keep the prefetch ahead of this group's MFMAs
+                __builtin_amdgcn_sched_barrier(0);
+                const half8 *a = af[dx & 1];
+                const half8 *b = bf[g & 1];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[G::arow(i, dy)], b[j], acc[i][j], 0, 0, 0);
             }
-            // keep the prefetch ahead of this group's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-            const half8 *a = af[dx & 1];
-            const half8 *b = bf[g & 1];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[G::arow(i, dy)], b[j], acc[i][j], 0, 0, 0);
+            // the next stage has landed (own loads) and every wave is done with
+            // this one (barrier)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
         }
-        // the next stage has landed (own loads) and every wave is done with
-        // this one (barrier)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
+        const int y0 = cur.y0, x0 = cur.x0, n0 = cur.n0;
 
     // epilogue through LDS: accumulator element (i, j, r) of lane l is tile
     // pixel (4 wm + i, 8 (r / 4) + 4 (l / 32) + r % 4), channel
@@ -260,9 +322,12 @@ void k_conv_halo(IgemmArgs p)
     // f32; then every thread writes 16 contiguous bytes, so each tile row
     // leaves as one run of TW * BN * 4 bytes (contiguous when BN is the
     // output row width).
+    // With a next tile its first stage is landing in the other buffer:
+    // stage in the last stage's buffer only (the launcher keeps tiles too
+    // wide for one buffer to one tile per workgroup).
     const float osc = p.oscale;
     const bool accum = p.accumulate != 0;
-    float *stg = reinterpret_cast<float *>(lds);
+    float *stg = reinterpret_cast<float *>(lds + (has_next ? ((gs - 1) & 1) * STAGE : 0));
     float bv[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) bv[j] = p.bias ? p.bias[n0 + wn * (BN / WN) + j * 32 + fx] : 0.f;
@@ -354,6 +419,23 @@ void k_conv_halo(IgemmArgs p)
         }
         __syncthreads();
     }
+    cur = nxt;
+    }
+}
+
+// workgroups resident at once: the compute units times the workgroups one
+// holds (queried once per device)
+int resident_slots(int per_cu)
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev] * per_cu;
 }
 
 template <int MODE, int BN, int NW, bool NORM = false>
@@ -361,7 +443,15 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
 {
     const int Hout = (MODE == kConv3x3Up2) ? 2 * a.H : a.H;
     const int Wout = (MODE == kConv3x3Up2) ? 2 * a.W : a.W;
-    const int grid = ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW) * (a.N / BN);
+    const int tiles = ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW) * (a.N / BN);
+    // where a workgroup can walk several tiles: as many workgroups as are
+    // resident at once (8 waves per compute unit), a multiple of 8 for the
+    // XCD schedule; else one tile each
+    int grid = tiles;
+    if (can_walk<MODE, BN>()) {
+        const int slots = resident_slots(8 / NW) & ~7;
+        if (slots > 0 && slots < tiles) grid = slots;
+    }
     hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW, NORM>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 

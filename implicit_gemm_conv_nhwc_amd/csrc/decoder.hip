@@ -93,6 +93,8 @@ int check_conv_w(const ig_conv_w &c, const char *name, int k)
     if (c.cin <= 0 || c.cout <= 0 || c.cin > c.cin_p || c.cout > c.cout_p)
         return fail(IG_EINVAL, "%s: bad channel counts %d/%d -> %d/%d", name, c.cin, c.cin_p, c.cout, c.cout_p);
     if (c.cin_p % 64 || c.cout_p % 64) return fail(IG_EUNSUPPORTED, "%s: padded widths must be multiples of 64", name);
+    if (c.cin_p > kConvMaxChannels || c.cout_p > kConvMaxChannels)
+        return fail(IG_EUNSUPPORTED, "%s: padded widths above %d", name, kConvMaxChannels);
     return IG_OK;
 }
 
@@ -279,6 +281,10 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
             size_blocks(*d, pl.s, d->n_up, input.n(), w0 << lv, feed, true, wd.cp_in[pl.s], pl.max_xb, pl);
         }
     }
+    // every 3x3 conv reads its f16 input from xn or xg
+    if ((pl.max_xn > pl.max_xg ? pl.max_xn : pl.max_xg) * 2 >= kConvInMaxBytes)
+        return fail(IG_EUNSUPPORTED, "a conv input of this frame passes %lld bytes; decode it in bands",
+                    (long long)kConvInMaxBytes);
     // layout
     size_t o = 0;
     auto take = [&](size_t bytes) {

@@ -23,6 +23,13 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // implicit GEMM (MFMA f16 -> f32)
 // ---------------------------------------------------------------------
 enum GemmMode { kGemm = 0, kConv3x3 = 1, kConv3x3Up2 = 2 };
+// The 3x3 conv kernels address their f16 input with 32-bit byte offsets
+// and mark out-of-image patch pixels with an offset past every input: the
+// input must stay below this many bytes.
+constexpr int64_t kConvInMaxBytes = 0x7fff0000;
+// widest padded channel count a conv takes (its weight plane stays below
+// 2 GB and a stage's channel offset below 64 KB)
+constexpr int kConvMaxChannels = 8192;
 
 struct IgemmArgs {
     const _Float16 *a;  // kGemm: A [M][lda]; convs: NHWC image [H*W][cin_p]
