@@ -84,6 +84,10 @@ int ig_pack_conv_weights(const uint16_t *w, int cout, int cin, int k, int cout_p
  *          (cout_p: multiple of 64)
  *   bias:  f32 [cout_p] or NULL
  *   y:     f32 NHWC [H*W][cout_p]
+ * Limits (IG_EUNSUPPORTED past them), for every 3x3 entry point: the f16
+ * input below 0x7fff0000 bytes (the kernels address it with 32-bit byte
+ * offsets) and cin_p, cout_p <= 8192. The decoders check the same for
+ * every conv input of their plan (a larger frame decodes in bands).
  * --------------------------------------------------------------------- */
 int conv3x3_nhwc(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout_p,
                  const float *bias, float oscale, float *y, void *stream);

@@ -85,6 +85,13 @@ def test_validation_rejects_before_enqueueing(ig):
     assert lib.conv3x3_nhwc(ctypes.c_void_p((1 << 20) + 8), 4, 4, 64, fake, 64, None, f1, fake, None) == -1
     assert lib.conv3x3_up2_nhwc(fake, -1, 4, 64, fake, 64, None, f1, fake, None) == -1
     assert lib.ig_conv_nhwc_ex(fake, 4, 4, 64, 5, fake, 64, None, f1, 0, fake, None) == -1
+    # the 3x3 kernels address their f16 input with 32-bit byte offsets: an
+    # input of 2^31 - 2^16 bytes or more is refused (a 1x1 GEMM of the same
+    # size is not); channel counts above 8192 too
+    assert lib.conv3x3_nhwc(fake, 2048, 8192, 64, fake, 64, None, f1, fake, None) == -2
+    assert lib.conv3x3_up2_nhwc(fake, 2048, 8192, 64, fake, 64, None, f1, fake, None) == -2
+    assert lib.conv3x3_nhwc(fake, 4, 4, 8256, fake, 64, None, f1, fake, None) == -2
+    assert lib.conv3x3_nhwc(fake, 4, 4, 64, fake, 8256, None, f1, fake, None) == -2
     # empty inputs are valid and enqueue nothing
     assert lib.conv3x3_nhwc(None, 0, 4, 64, None, 64, None, f1, None, None) == 0
     # GEMM
@@ -140,6 +147,12 @@ def test_decoder_descriptor_validation(ig):
     d.conv_out = conv(64, 3, 3)
     n = L._ws_bytes(ctypes.byref(d), 8, 8, 0)
     assert n > 0, ig.last_error()
+    # a frame whose conv inputs pass the 3x3 kernels' 2 GB offset range
+    # (64 channels f16 at 4096 x 4096 = 2 GB) is refused in one pass...
+    assert L._ws_bytes(ctypes.byref(d), 2048, 2048, 128) == 0
+    assert "bands" in ig.last_error()
+    # ...and planned in bands of 64 output rows
+    assert ig.lib.ig_decoder_bands_workspace_bytes(ctypes.byref(d), 2048, 2048, 128, 64, 0) > 0, ig.last_error()
     # too small a workspace: rejected, nothing enqueued
     assert ig.lib.decoder_forward(ctypes.byref(d), fake, 8, 8, 8, 0, fake, n - 1, fake, None) == -3
     assert ig.lib.decoder_forward(ctypes.byref(d), fake, 8, 8, 15, 0, fake, n, fake, None) == -1
