@@ -24,7 +24,9 @@
 //    the blocked weight plane into registers;
 //  * a patch pixel's 32 channels are 4 units of 16 bytes, unit u stored at
 //    u ^ ((pixel >> 2) & 3), so the 16 lanes reading one unit of 16
-//    consecutive pixels touch 16 distinct bank groups.
+//    consecutive pixels touch 16 distinct bank groups;
+//  * each XCD works on a contiguous band of tiles (workgroups are dealt to
+//    the XCDs round robin), so neighbouring tiles' halo rows hit its L2.
 #include "ig_internal.h"
 
 namespace ig {
@@ -62,8 +64,14 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;  // pixel column in a group; K quarter / output row block
 
+    // workgroups are dealt round robin to the 8 XCDs: remap so each XCD
+    // takes a contiguous band of tiles, whose shared halo rows then come
+    // from its own L2
     const int tiles_x = (W + OW - 1) / OW;
-    const int y0 = (blockIdx.x / tiles_x) * OH, x0 = (blockIdx.x % tiles_x) * OW;
+    const int nblk = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int y0 = (bid / tiles_x) * OH, x0 = (bid % tiles_x) * OW;
     const __amdgpu_buffer_rsrc_t src = make_rsrc(x, (uint32_t)H * W * cin_p * 2);
 
     // this lane's source offset (stage 0) for each of its wave's patch loads
