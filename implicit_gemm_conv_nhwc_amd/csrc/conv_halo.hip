@@ -142,6 +142,9 @@ void k_conv_halo(IgemmArgs p)
     static_assert(4 * TW * BN * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
 
     __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
+    // the fused norm's gamma, read from LDS in the epilogue (a tile spans
+    // all N = BN channels, so n0 = 0)
+    __shared__ __attribute__((aligned(16))) float gam[NORM ? BN : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -250,6 +253,7 @@ void k_conv_halo(IgemmArgs p)
             bf[j] = __builtin_bit_cast(half8, sB[(tap * BN + wn * (BN / WN) + j * 32 + fx) * 2 + wh]);
     };
 
+    if (NORM && tid < BN) gam[tid] = p.ngamma[tid];  // visible after the first barrier
     Tile cur = make_tile(t);
     issue(cur, 0, 0, 0, PER_WAVE);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -398,7 +402,7 @@ void k_conv_halo(IgemmArgs p)
             const float inv = sqrtf((float)p.norm_c) / fmaxf(sqrtf(ss), p.norm_eps);
             const int oy = y0 + FM * wr + q, ox = x0 + px;
             if (oy < Hout && ox < Wout) {
-                const float4 *g4 = reinterpret_cast<const float4 *>(p.ngamma + cb);
+                const float4 *g4 = reinterpret_cast<const float4 *>(gam + cb);
                 _Float16 *dst = p.ny + ((int64_t)oy * Wout + ox) * BN + cb;
 #pragma unroll
                 for (int k = 0; k < 8; k += 2) {
