@@ -253,6 +253,38 @@ def test_conv3x3_up2_isolated(H, W, cin, cout):
     assert ratio <= CONV_TOL and ratio <= 1e-4
 
 
+@pytest.mark.parametrize("H,W,cin,cout,mode", [(300, 530, 64, 192, 1), (160, 270, 128, 128, 2),
+                                               (272, 512, 128, 128, 1)])
+def test_conv3x3_tile_walk_sampled(H, W, cin, cout, mode):
+    """More 16x32x64 output tiles than the chip holds workgroups, so each
+    workgroup walks several (the next tile's first stage loading under the
+    current tile's last stage and epilogue), with ragged image edges and a
+    tile count that splits unevenly over the 8 XCDs: every output written,
+    the border pixels, one pixel of every tile and seeded picks against the
+    oracle."""
+    seed = 500 + H + mode
+    x16 = synth.normal(14, seed, (H, W, cin), 1.0, np.float16)
+    w = synth.normal(14, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
+    b = synth.normal(14, seed + 2, (cout,), 0.02)
+    cin_p, cout_p = cpad(cin), cpad(cout)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    assert ((Ho + 15) // 16) * ((Wo + 31) // 32) * (cout_p // 64) > 512
+    y = nan_f32((Ho * Wo, cout_p))
+    ig.conv_nhwc_ex(dev(pad_last(x16.reshape(H * W, cin), cin_p)), H, W, cin_p, mode, packed(w), cout_p,
+                    padded_vec(b, cout_p), 1.0, 0, y)
+    got = host(y)
+    assert not np.isnan(got).any(), "a tile was not written"
+    assert np.all(got[:, cout:] == 0)
+    corners = np.array([r * Wo + c for r in range(0, Ho, 16) for c in range(0, Wo, 32)], np.int64)
+    pix = np.unique(np.concatenate([sample_pixels(Ho, Wo, 512, seed=seed), corners, corners + 15 * Wo + 31]))
+    pix = pix[pix < Ho * Wo]
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    ref = O.conv2d_at(xc, w, pix, b, up2=(mode == 2))
+    err, rms, ratio = conv_err(got[pix, :cout], ref)
+    print("tile walk %dx%d %d->%d mode %d (%d px): ratio %.2e" % (H, W, cin, cout, mode, len(pix), ratio))
+    assert ratio <= CONV_TOL and ratio <= 1e-4
+
+
 @pytest.mark.parametrize("H,W,cin,cout", [(11, 23, 256, 256), (1, 1, 64, 64), (32, 32, 512, 256)])
 def test_conv1x1_isolated(H, W, cin, cout):
     got, ref = _conv_isolated(H, W, cin, cout, 0, seed=200 + H)
