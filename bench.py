@@ -373,6 +373,35 @@ def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
     return avg * scale
 
 
+def digest_counters(path, roof_launches, n_xcd=8, n_simd=1024):
+    """Averages of every counter over the roofline conv's last
+    `roof_launches` dispatches, and what they imply: the clock
+    (GRBM_GUI_ACTIVE counts per XCD) and the MFMA pipes' busy share
+    (SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs)."""
+    import csv
+
+    rows = [r for r in csv.DictReader(open(path))
+            if "k_conv_halo" in r["Kernel_Name"] and ("ILi1ELi64ELi4ELb0" in r["Kernel_Name"]
+                                                     or ROOF_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", ""))]
+    by = {}
+    for r in rows:
+        by.setdefault(r["Counter_Name"], []).append((int(r["Start_Timestamp"]), float(r["Counter_Value"]),
+                                                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, v in sorted(by.items()):
+        v = sorted(v)[-roof_launches:]
+        out[name] = sum(x[1] for x in v) / len(v)
+        dur_ns = sum(x[2] for x in v) / len(v)
+        print("%-28s %16.1f   (n=%d, dispatch %.1f us)" % (name, out[name], len(v), dur_ns / 1e3))
+    if "GRBM_GUI_ACTIVE" in out:
+        cyc = out["GRBM_GUI_ACTIVE"] / n_xcd
+        print("clock: %.0f cycles per XCD over %.1f us = %.2f GHz" % (cyc, dur_ns / 1e3, cyc / dur_ns))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in out:
+            busy = out["SQ_VALU_MFMA_BUSY_CYCLES"] / n_simd
+            print("MFMA busy: %.0f cycles per SIMD = %.1f%% of the dispatch" % (busy, 100 * busy / cyc))
+    return out
+
+
 def digest_trace(path, roof_launches):
     """Per-kernel totals of a rocprofv3 kernel trace, plus the average of the
     roofline region's launches of the dominant kernel (its last
@@ -418,7 +447,12 @@ def main():
     ap.add_argument("--digest-trace", default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--digest-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
+    ap.add_argument("--digest-counters", default=None, metavar="COUNTER_CSV")
     args = ap.parse_args()
+
+    if args.digest_counters:
+        digest_counters(args.digest_counters, args.roof_reps)
+        return 0
 
     if args.digest_trace:
         digest_trace(args.digest_trace, args.roof_reps)
