@@ -382,7 +382,7 @@ void k_conv_halo(IgemmArgs p)
                 }
             }
         }
-        if (NORM) {
+        if constexpr (NORM) {
             // the staged 4 x TW pixels' RMS_norm: TPP consecutive lanes per
             // pixel, 32 channels each (the tile holds every channel: BN = N)
             constexpr int TPP = NT / (4 * TW);

@@ -35,7 +35,8 @@ __device__ __forceinline__ float silu1(float y) { return y / (1.0f + __expf(-y))
 // ---------------------------------------------------------------------
 // RMS_norm: 16 lanes per pixel, each lane NCH float4 chunks (channels
 // 4*(g + 16k) .. +3), so a wave handles 4 pixels and every load
-// instruction reads 256 contiguous bytes per pixel. With yg, the same read
+// instruction reads 256 contiguous bytes per pixel; the row's bias and
+// gamma come from LDS, staged once per workgroup. With yg, the same read
 // also yields the guarded cast f16((x + b) * gscale) of the row (a resnet
 // whose shortcut takes the raw stream), saving that cast's own read.
 // ---------------------------------------------------------------------
@@ -46,18 +47,26 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, in
                                                  float eps, _Float16 *__restrict__ y,
                                                  _Float16 *__restrict__ yg, float gscale)
 {
+    // the row's bias and gamma, staged once per workgroup: each lane then
+    // reads its chunks from LDS instead of issuing 2 NCH vector loads
+    __shared__ float4 s_b[16 * NCH], s_g[16 * NCH];
+    for (int i = threadIdx.x; i < 16 * NCH; i += 256) {
+        s_b[i] = bias ? reinterpret_cast<const float4 *>(bias)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s_g[i] = reinterpret_cast<const float4 *>(gamma)[i];
+    }
     const int g = threadIdx.x & 15;
     const int64_t pix = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-    if (pix >= M) return;  // the 16 lanes of a pixel leave together
-    const float4 *xr = reinterpret_cast<const float4 *>(x + pix * cp);
+    const bool live = pix < M;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + (live ? pix : 0) * cp);
     float4 v[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) v[k] = xr[g + 16 * k];
+    __syncthreads();
+    if (!live) return;  // the 16 lanes of a pixel leave together
     if (bias) {
-        const float4 *b4 = reinterpret_cast<const float4 *>(bias);
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const float4 b = b4[g + 16 * k];
+            const float4 b = s_b[g + 16 * k];
             v[k].x += b.x;
             v[k].y += b.y;
             v[k].z += b.z;
@@ -78,11 +87,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, in
     ss += __shfl_xor(ss, 2, 16);
     ss += __shfl_xor(ss, 1, 16);
     const float inv = sqrt_c / fmaxf(sqrtf(ss), eps);
-    const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
     half4 *yr = reinterpret_cast<half4 *>(y + pix * cp);
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const float4 gm = g4[g + 16 * k];
+        const float4 gm = s_g[g + 16 * k];
         float4 o;
         o.x = v[k].x * inv * gm.x;
         o.y = v[k].y * inv * gm.y;
