@@ -19,6 +19,7 @@ namespace {
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ half4 to_half4(float4 v)
 {
@@ -169,7 +170,10 @@ __global__ __launch_bounds__(256) void k_guard_cast(const float *__restrict__ x,
     half4 *y4 = reinterpret_cast<half4 *>(y);
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * 256) {
-        float4 v = x4[i];
+        // the stream's last read before the conv that takes the cast (the
+        // up conv writes a new stream): a streaming (nontemporal) load
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x4 + i));
+        float4 v = make_float4(t[0], t[1], t[2], t[3]);
         if (bias) {
             const float4 b = b4[i % C4];
             v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;

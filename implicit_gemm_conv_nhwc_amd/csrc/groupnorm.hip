@@ -220,8 +220,15 @@ __global__ __launch_bounds__(256) void k_gn_apply(const float *__restrict__ x, i
         // past the end load row M - 1 and are not written)
         v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + (r < M ? r : (int64_t)M - 1) * cp) + q);
     }
-    const float4 b = bias ? reinterpret_cast<const float4 *>(bias)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 a4 = reinterpret_cast<const float4 *>(scale)[q], s4 = reinterpret_cast<const float4 *>(shift)[q];
+    // the per-channel bias, scale and shift, staged once per workgroup
+    __shared__ float4 s_b[MAXT], s_a[MAXT], s_s[MAXT];
+    for (int i = threadIdx.x; i < nq; i += blockDim.x) {
+        s_b[i] = bias ? reinterpret_cast<const float4 *>(bias)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s_a[i] = reinterpret_cast<const float4 *>(scale)[i];
+        s_s[i] = reinterpret_cast<const float4 *>(shift)[i];
+    }
+    __syncthreads();
+    const float4 b = s_b[q], a4 = s_a[q], s4 = s_s[q];
     const float bb[4] = {b.x, b.y, b.z, b.w}, sc[4] = {a4.x, a4.y, a4.z, a4.w}, sh[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
     for (int k = 0; k < AU; ++k) {
