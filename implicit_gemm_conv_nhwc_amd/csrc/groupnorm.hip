@@ -122,9 +122,8 @@ __global__ __launch_bounds__(256) void k_gn_stats(const float *__restrict__ x, i
     for (int64_t bt = blockIdx.x; bt < nbatch; bt += 2 * step) {
         load(bt + step, w);
         fold(bt, v);
-        if (bt + step >= nbatch) break;
         load(bt + 2 * step, v);
-        fold(bt + step, w);
+        fold(bt + step, w);  // (a batch past the end folds nothing)
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
