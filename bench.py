@@ -374,32 +374,42 @@ def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
 
 
 def digest_counters(path, roof_launches, n_xcd=8, n_simd=1024):
-    """Averages of every counter over the roofline conv's last
-    `roof_launches` dispatches, and what they imply: the clock
-    (GRBM_GUI_ACTIVE counts per XCD) and the MFMA pipes' busy share
-    (SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs)."""
+    """Averages of every counter over the conv roofline's last
+    `roof_launches` dispatches and the attention roofline's last 10, and
+    what they imply: the clock (GRBM_GUI_ACTIVE counts per XCD) and the MFMA
+    pipes' busy share (SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs)."""
     import csv
 
-    rows = [r for r in csv.DictReader(open(path))
-            if "k_conv_halo" in r["Kernel_Name"] and ("ILi1ELi64ELi4ELb0" in r["Kernel_Name"]
-                                                     or ROOF_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", ""))]
-    by = {}
-    for r in rows:
-        by.setdefault(r["Counter_Name"], []).append((int(r["Start_Timestamp"]), float(r["Counter_Value"]),
-                                                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    out = {}
-    for name, v in sorted(by.items()):
-        v = sorted(v)[-roof_launches:]
-        out[name] = sum(x[1] for x in v) / len(v)
-        dur_ns = sum(x[2] for x in v) / len(v)
-        print("%-28s %16.1f   (n=%d, dispatch %.1f us)" % (name, out[name], len(v), dur_ns / 1e3))
-    if "GRBM_GUI_ACTIVE" in out:
-        cyc = out["GRBM_GUI_ACTIVE"] / n_xcd
-        print("clock: %.0f cycles per XCD over %.1f us = %.2f GHz" % (cyc, dur_ns / 1e3, cyc / dur_ns))
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in out:
-            busy = out["SQ_VALU_MFMA_BUSY_CYCLES"] / n_simd
-            print("MFMA busy: %.0f cycles per SIMD = %.1f%% of the dispatch" % (busy, 100 * busy / cyc))
-    return out
+    rows = list(csv.DictReader(open(path)))
+    kernels = [("conv3x3 512^2x128 (%s)" % ROOF_KERNEL,
+                lambda n: "k_conv_halo" in n and ("ILi1ELi64ELi4ELb0" in n or ROOF_KERNEL.replace(" ", "") in n.replace(" ", "")),
+                roof_launches),
+               ("attention 16384 x 512 (k_flash)", lambda n: "k_flash(" in n or "k_flashEN" in n, 10)]
+    res = {}
+    for title, match, last in kernels:
+        by = {}
+        for r in rows:
+            if match(r["Kernel_Name"]):
+                by.setdefault(r["Counter_Name"], []).append((int(r["Start_Timestamp"]), float(r["Counter_Value"]),
+                                                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        if not by:
+            continue
+        print("%s:" % title)
+        out = {}
+        dur_ns = 1.0
+        for name, v in sorted(by.items()):
+            v = sorted(v)[-last:]
+            out[name] = sum(x[1] for x in v) / len(v)
+            dur_ns = sum(x[2] for x in v) / len(v)
+            print("  %-28s %16.1f   (n=%d, dispatch %.1f us)" % (name, out[name], len(v), dur_ns / 1e3))
+        if "GRBM_GUI_ACTIVE" in out:
+            cyc = out["GRBM_GUI_ACTIVE"] / n_xcd
+            print("  clock: %.0f cycles per XCD over %.1f us = %.2f GHz" % (cyc, dur_ns / 1e3, cyc / dur_ns))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in out:
+                busy = out["SQ_VALU_MFMA_BUSY_CYCLES"] / n_simd
+                print("  MFMA busy: %.0f cycles per SIMD = %.1f%% of the dispatch" % (busy, 100 * busy / cyc))
+        res[title] = out
+    return res
 
 
 def digest_trace(path, roof_launches):
