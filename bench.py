@@ -373,6 +373,30 @@ def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
     return avg * scale
 
 
+def digest_pmc_stream(fetch_csv, write_csv, copyf_csv, copyw_csv, roof_launches, nbytes=1 << 30):
+    """HBM bytes per launch of the RMS_norm and guarded-cast rooflines (the
+    last `roof_launches` dispatches of each), scaled like the conv's."""
+    import csv
+
+    def scale(copy_csv, counter):
+        cp = [float(r["Counter_Value"]) for r in csv.DictReader(open(copy_csv)) if r["Counter_Name"] == counter
+              and ("mul" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower())]
+        return nbytes / (sum(cp) / len(cp))
+
+    def avg(path, counter, match):
+        v = [float(r["Counter_Value"]) for r in sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+             if r["Counter_Name"] == counter and match(r["Kernel_Name"])][-roof_launches:]
+        return sum(v) / len(v) if v else float("nan")
+
+    fs, ws = scale(copyf_csv, "FETCH_SIZE"), scale(copyw_csv, "WRITE_SIZE")
+    for title, match, algo in (("rmsnorm 512^2x128 (k_rmsnorm<2>)", lambda n: "k_rmsnorm" in n and "ILi2E" in n, 262144 * 128 * 6),
+                               ("guard_cast 512^2x128 (k_guard_cast)", lambda n: "k_guard_cast" in n, 262144 * 128 * 6)):
+        f = avg(fetch_csv, "FETCH_SIZE", match) * fs
+        w = avg(write_csv, "WRITE_SIZE", match) * ws
+        print("%s: read %.1f MB, written %.1f MB, total %.1f MB per launch (algorithmic %.1f MB)" % (
+            title, f / 1e6, w / 1e6, (f + w) / 1e6, algo / 1e6))
+
+
 def digest_counters(path, roof_launches, n_xcd=8, n_simd=1024):
     """Averages of every counter over the conv roofline's last
     `roof_launches` dispatches and the attention roofline's last 10, and
@@ -473,6 +497,7 @@ def main():
     if args.digest_pmc:
         f = digest_pmc(args.digest_pmc[0], args.digest_pmc[2], "FETCH_SIZE", args.roof_reps)
         w = digest_pmc(args.digest_pmc[1], args.digest_pmc[3], "WRITE_SIZE", args.roof_reps)
+        digest_pmc_stream(*args.digest_pmc, args.roof_reps)
         print(json.dumps({"source_sha256_16": conv_source_hash(), "fetch_bytes_per_launch": round(f),
                           "write_bytes_per_launch": round(w), "bytes_per_launch": round(f + w)}))
         return 0
