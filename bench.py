@@ -409,11 +409,18 @@ def digest_counters(path, roof_launches, n_xcd=8, n_simd=1024):
                 lambda n: "k_conv_halo" in n and ("ILi1ELi64ELi4ELb0" in n or ROOF_KERNEL.replace(" ", "") in n.replace(" ", "")),
                 roof_launches),
                ("attention 16384 x 512 (k_flash)", lambda n: "k_flash(" in n or "k_flashEN" in n, 10)]
+    # the decode's upsampling convs (k_conv_halo<2, 64, 4, false>), one entry per grid
+    up = lambda n: "k_conv_halo" in n and ("ILi2ELi64ELi4ELb0" in n or "<2, 64, 4, false>" in n)
+    for g in sorted({r["Grid_Size"] for r in rows if up(r["Kernel_Name"])}, key=int):
+        kernels.append(("decode up conv k_conv_halo<2, 64, 4, false>, grid %s" % g,
+                        (lambda g: lambda n, r=None: up(n))(g), 10, g))
     res = {}
-    for title, match, last in kernels:
+    for entry in kernels:
+        title, match, last = entry[:3]
+        grid = entry[3] if len(entry) > 3 else None
         by = {}
         for r in rows:
-            if match(r["Kernel_Name"]):
+            if match(r["Kernel_Name"]) and (grid is None or r["Grid_Size"] == grid):
                 by.setdefault(r["Counter_Name"], []).append((int(r["Start_Timestamp"]), float(r["Counter_Value"]),
                                                              int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
         if not by:
