@@ -92,7 +92,8 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // uniform (scalar branches); the mask tells the compiler wave < 8
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
     const int wm = wave / WN, wn = wave % WN;
     const int fx = lane & 31, fh = lane >> 5;
 
@@ -160,22 +161,27 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
         const int buf = st & 1;
         const u32x4 *sA = lds + buf * STAGE;
         const u32x4 *sB = sA + BM * UPR;
+        // each K step reads the next step's fragments before its MFMAs, so
+        // the LDS latency hides behind them
+        half8 af[2][FM], bf[2][FN];
+        auto frags = [&](int ks, half8 *a, half8 *b) __attribute__((always_inline)) {
+            const int unit = (2 * ks + fh) ^ swz;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = __builtin_bit_cast(half8, sA[(wm * TM + 32 * i + fx) * UPR + unit]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = __builtin_bit_cast(half8, sB[(wn * TN + 32 * j + fx) * UPR + unit]);
+        };
+        frags(0, af[0], bf[0]);
 #pragma unroll
         for (int ks = 0; ks < KST / 16; ++ks) {
             if (st + 1 < nst) issue(st + 1, buf ^ 1, ks * PER_WAVE / 4, (ks + 1) * PER_WAVE / 4);
-            const int unit = (2 * ks + fh) ^ swz;
-            half8 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = __builtin_bit_cast(half8, sA[(wm * TM + 32 * i + fx) * UPR + unit]);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = __builtin_bit_cast(half8, sB[(wn * TN + 32 * j + fx) * UPR + unit]);
+            if (ks + 1 < KST / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
