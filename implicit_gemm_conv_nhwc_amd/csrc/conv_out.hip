@@ -39,6 +39,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int NT = 256;                     // 4 waves
 constexpr int OH = 8, OW = 32;              // output tile
+constexpr int RPW = OH / 4;                 // output rows per wave
 constexpr int PH = OH + 2, PW = OW + 2;     // input patch
 constexpr int CS = 32;                      // input channels per stage
 constexpr int UPP = CS * 2 / 16;            // 16-byte units per patch pixel
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
         }
     };
 
-    constexpr int NG = 2 * OW / 16;  // groups of 16 pixels per wave
+    constexpr int NG = RPW * OW / 16;  // groups of 16 pixels per wave
     f32x4 acc[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -127,8 +128,8 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
             const int dy = t / 3, dx = t % 3;
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                // group g of this wave: output row 2 wave + g / (OW / 16), columns 16 (g % (OW / 16)) ..
-                const int pr = 2 * wave + g / (OW / 16) + dy, pc = 16 * (g % (OW / 16)) + col + dx;
+                // group g of this wave: output row RPW wave + g / (OW / 16), columns 16 (g % (OW / 16)) ..
+                const int pr = RPW * wave + g / (OW / 16) + dy, pc = 16 * (g % (OW / 16)) + col + dx;
                 const int pix = pr * PW + pc;
                 const half8 xf = __builtin_bit_cast(half8, sA[pix * UPP + (grp ^ ((pix >> 2) & 3))]);
                 acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wt[t], xf, acc[g], 0, 0, 0);
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
     // rows r0 .. r1 - 1 are stored, output planes HWo apart
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        const int oy = y0 + 2 * wave + g / (OW / 16), ox = x0 + 16 * (g % (OW / 16)) + col;
+        const int oy = y0 + RPW * wave + g / (OW / 16), ox = x0 + 16 * (g % (OW / 16)) + col;
         if (oy < r0 || oy >= r1 || ox >= W) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
