@@ -14,7 +14,7 @@
 // mean_a), exact up to rounding for any split. Each of at most 1024
 // workgroups merges its threads' figures per group and writes one partial;
 // a second kernel merges a group's partials in f64 and turns the group
-// statistics into a per-channel scale and shift; the apply kernel reads the
+// statistics into a per-channel offset and scale; the apply kernel reads the
 // stream once more. HBM: two reads of the f32 stream and one f16 write.
 #include "ig_internal.h"
 
@@ -152,11 +152,12 @@ __global__ __launch_bounds__(256) void k_gn_stats(const float *__restrict__ x, i
 }
 
 // one workgroup per group: merge its chunks' (n, mean, M2) in f64, then
-// write the group's per-channel scale inv * gamma and shift
-// beta - mean * inv * gamma (workgroup 0 also zeroes the pad channels')
+// write the group's per-channel offset mean - b (in f64, rounded once),
+// scale inv * gamma and beta (workgroup 0 also zeroes the pad channels')
 __global__ __launch_bounds__(256) void k_gn_final(const float *__restrict__ part, int nchunk, int cp, int c_real,
-                                                  int cpg, float eps, const float *__restrict__ gamma,
-                                                  const float *__restrict__ beta, float *__restrict__ sc,
+                                                  int cpg, float eps, const float *__restrict__ bias,
+                                                  const float *__restrict__ gamma, const float *__restrict__ beta,
+                                                  float *__restrict__ off, float *__restrict__ sc,
                                                   float *__restrict__ sh)
 {
     __shared__ double sn[256], sm[256], s2[256];
@@ -188,26 +189,29 @@ __global__ __launch_bounds__(256) void k_gn_final(const float *__restrict__ part
         __syncthreads();
     }
     const double var = sn[0] > 0.0 ? s2[0] / sn[0] : 0.0;
-    const float mean = (float)sm[0], inv = (float)(1.0 / sqrt(var + (double)eps));
+    const float inv = (float)(1.0 / sqrt(var + (double)eps));
     for (int c = g * cpg + t; c < (g + 1) * cpg; c += 256) {
-        const float a = inv * gamma[c];
-        sc[c] = a;
-        sh[c] = beta[c] - mean * a;
+        // the statistics are of v = x + b: (v - mean) = x - (mean - b)
+        off[c] = (float)(sm[0] - (bias ? (double)bias[c] : 0.0));
+        sc[c] = inv * gamma[c];
+        sh[c] = beta[c];
     }
     if (g == 0)
         for (int c = c_real + t; c < cp; c += 256) {
+            off[c] = 0.f;
             sc[c] = 0.f;
             sh[c] = 0.f;
         }
 }
 
-// y = (x + b) * scale + shift (+ SiLU), f16, with the per-channel scale
-// inv * gamma and shift beta - mean * inv * gamma (0 on pad channels).
+// y = (x - off) * scale + beta (+ SiLU), f16, with the per-channel offset
+// mean - b and scale inv * gamma: subtracting the mean first keeps the f32
+// rounding to the mean's own (0 on pad channels).
 // Workgroup w covers rows w RL AU .. (w + 1) RL AU - 1; thread (rl, q)
 // issues the loads of its AU rows (channel quad q) first.
 constexpr int AU = 2;  // rows per thread in the apply kernel
 __global__ __launch_bounds__(256) void k_gn_apply(const float *__restrict__ x, int M, int cp,
-                                                  const float *__restrict__ bias, const float *__restrict__ scale,
+                                                  const float *__restrict__ offset, const float *__restrict__ scale,
                                                   const float *__restrict__ shift, int silu, _Float16 *__restrict__ y)
 {
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -223,10 +227,10 @@ __global__ __launch_bounds__(256) void k_gn_apply(const float *__restrict__ x, i
         // past the end load row M - 1 and are not written)
         v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + (r < M ? r : (int64_t)M - 1) * cp) + q);
     }
-    // the per-channel bias, scale and shift, staged once per workgroup
+    // the per-channel offset, scale and shift, staged once per workgroup
     __shared__ float4 s_b[MAXT], s_a[MAXT], s_s[MAXT];
     for (int i = threadIdx.x; i < nq; i += blockDim.x) {
-        s_b[i] = bias ? reinterpret_cast<const float4 *>(bias)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s_b[i] = reinterpret_cast<const float4 *>(offset)[i];
         s_a[i] = reinterpret_cast<const float4 *>(scale)[i];
         s_s[i] = reinterpret_cast<const float4 *>(shift)[i];
     }
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(256) void k_gn_apply(const float *__restrict__ x, i
         half4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float o = (v[k][e] + bb[e]) * sc[e] + sh[e];
+            float o = (v[k][e] - bb[e]) * sc[e] + sh[e];
             if (silu) o = silu1(o);
             h[e] = (_Float16)o;
         }
@@ -266,7 +270,7 @@ int64_t gn_chunks(int M, int cp)
 
 size_t gn_workspace_bytes(int M, int cp, int groups)
 {
-    return ((size_t)gn_chunks(M, cp) * groups * 3 + (size_t)cp * 2) * sizeof(float) + 256;
+    return ((size_t)gn_chunks(M, cp) * groups * 3 + (size_t)cp * 3) * sizeof(float) + 256;
 }
 
 bool gn_supported(int cp, int c_real, int groups)
@@ -288,14 +292,14 @@ void launch_groupnorm(const float *x, int M, int cp, int c_real, int groups, con
     // the per-channel table, 16-byte aligned for the apply kernel's vector
     // loads (cp is a multiple of 4; the workspace holds 256 bytes of slack)
     const uintptr_t tab = (reinterpret_cast<uintptr_t>(part + nchunk * groups * 3) + 15) & ~(uintptr_t)15;
-    float *scale = reinterpret_cast<float *>(tab), *shift = scale + cp;
+    float *offset = reinterpret_cast<float *>(tab), *scale = offset + cp, *shift = scale + cp;
     const int cpg = c_real / groups;
     hipLaunchKernelGGL(k_gn_stats, dim3((unsigned)nchunk), dim3(nt), 0, s, x, M, cp, cpg, groups, bias, nbatch, part);
-    hipLaunchKernelGGL(k_gn_final, dim3(groups), dim3(256), 0, s, part, (int)nchunk, cp, c_real, cpg, eps, gamma, beta,
-                       scale, shift);
+    hipLaunchKernelGGL(k_gn_final, dim3(groups), dim3(256), 0, s, part, (int)nchunk, cp, c_real, cpg, eps, bias, gamma,
+                       beta, offset, scale, shift);
     const int rl = nt / (cp / 4);
     const int64_t blocks = ((int64_t)M + (int64_t)rl * AU - 1) / ((int64_t)rl * AU);
-    hipLaunchKernelGGL(k_gn_apply, dim3((unsigned)blocks), dim3(nt), 0, s, x, M, cp, bias, scale, shift, silu, y);
+    hipLaunchKernelGGL(k_gn_apply, dim3((unsigned)blocks), dim3(nt), 0, s, x, M, cp, offset, scale, shift, silu, y);
 }
 
 }  // namespace ig

@@ -138,6 +138,40 @@ def test_groupnorm(H, W, c, cp, groups, with_bias, silu):
     assert np.all((u <= 1) | (d <= 1e-5)) and exact >= 0.999
 
 
+def test_groupnorm_many_batches_per_workgroup():
+    """A frame large enough that each of the statistics kernel's 1024
+    workgroups folds many batches (with the next batch's loads in flight),
+    a row count that leaves a ragged last batch, and a mean far from zero
+    (the running merge must not lose the variance to cancellation).
+
+    Tolerance: an f32 evaluation of (v - mean) * inv * gamma + beta carries
+    the f32 rounding of the mean, up to 2^-24 |mean|, times inv * |gamma|;
+    near zero that exceeds 1 f16 ulp, so each element must be within 1 ulp
+    or within 1e-5 + 2^-21 |mean| inv |gamma| (8x that rounding), and 97%
+    exact (98.3% measured at mean 100, std 1)."""
+    H, W, c, groups = 701, 1499, 64, 16
+    M = H * W
+    x = (synth.normal(18, 77, (M, c), 1.0) + 100.0).astype(np.float32)
+    gamma = synth.uniform(18, 78, (c,), 0.5, 1.5)
+    beta = synth.normal(18, 79, (c,), 0.1)
+    nbytes = ig.groupnorm_workspace_bytes(M, c, groups)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = nan_f16((M, c))
+    ig.groupnorm_silu_f16(dev(x), M, c, c, groups, None, dev(gamma), dev(beta), 1, 1e-6, ws, nbytes, y)
+    got = host(y)
+    ref = O.group_norm(x.T, groups, gamma, beta, silu=True).T
+    xg = x.astype(np.float64).reshape(M, groups, c // groups)
+    mean = xg.mean(axis=(0, 2))
+    inv = 1.0 / np.sqrt(xg.var(axis=(0, 2)) + 1e-6)
+    bound = 1e-5 + 2.0 ** -21 * np.repeat(np.abs(mean) * inv, c // groups)[None, :] * np.abs(gamma)[None, :]
+    u = f16_ulps(got, ref.astype(np.float16))
+    d = np.abs(got.astype(np.float64) - ref)
+    exact = float(np.mean(u == 0))
+    print("groupnorm %dx%d c=%d g=%d (mean 100): max ulp %d, exact %.5f, max d/bound %.3f" % (
+        H, W, c, groups, u.max(), exact, float(np.max(np.where(u <= 1, 0.0, d / bound)))))
+    assert np.all((u <= 1) | (d <= bound)) and exact >= 0.97
+
+
 def test_groupnorm_workspace_too_small():
     M, cp = 64, 128
     y = nan_f16((M, cp))
