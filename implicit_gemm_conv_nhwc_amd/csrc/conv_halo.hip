@@ -11,11 +11,12 @@
 // Design (not the pages' 128x64 cooperative-matrix tiling):
 //  * a workgroup owns an output tile of 16 rows x 32 columns x BN
 //    channels: 4 wave64s with BN = 64 (two workgroups per CU, so one's
-//    epilogue overlaps the other's MFMAs), or 8 with BN = 128 (one per CU)
-//    when the fused RMS_norm needs all 128 channels of a pixel in one tile.
-//    Each wave computes 4 output rows x 32 columns x 64 channels as
-//    4 x 2 tiles of v_mfma_f32_32x32x16_f16 (one output row is one 32-row
-//    MFMA operand);
+//    epilogue overlaps the other's MFMAs), each wave 4 output rows x 32
+//    columns x 64 channels; for a plain conv with no more tiles than CUs, 8
+//    waves with BN = 64 (4 rows x 32 channels each, two waves per SIMD);
+//    8 waves with BN = 128 when the fused RMS_norm needs all 128 channels
+//    of a pixel in one tile. A wave's block is 4 x FN tiles of
+//    v_mfma_f32_32x32x16_f16 (one output row is one 32-row MFMA operand);
 //  * the reduction runs in stages of 16 input channels. A stage brings into
 //    LDS the input patch the tile needs -- (16+2) x (32+2) pixels, or
 //    (8+2) x (16+2) half-resolution pixels for the folded upsample -- and
@@ -475,13 +476,21 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
         }
         return;
     }
-    // 64-channel tiles: two workgroups share a CU, so one's epilogue (HBM
-    // writes) overlaps the other's MFMAs; measured faster than 128-channel
-    // tiles (one workgroup per CU) on every shape of the decoder
-    if (mode == kConv3x3)
-        launch_t<kConv3x3, 64, 4>(a, s);
-    else
+    // 64-channel tiles (128-channel tiles measured slower on every shape of
+    // the decoder), on 4 waves with two workgroups per CU, so one's epilogue
+    // overlaps the other's MFMAs. With no more tiles than CUs (one
+    // workgroup per CU anyway) the plain conv splits a tile over 8 waves
+    // (4 rows x 32 channels each: two waves per SIMD instead of one).
+    if (mode == kConv3x3) {
+        const int tiles = ((a.H + TH - 1) / TH) * ((a.W + TW - 1) / TW) * (a.N / 64);
+        const int cus = resident_slots(1);
+        if (cus > 0 && tiles <= cus)
+            launch_t<kConv3x3, 64, 8>(a, s);
+        else
+            launch_t<kConv3x3, 64, 4>(a, s);
+    } else {
         launch_t<kConv3x3Up2, 64, 4>(a, s);
+    }
 }
 
 }  // namespace ig
