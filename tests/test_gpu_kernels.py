@@ -396,6 +396,37 @@ def test_conv_with_fused_norm(H, W, cin, cout, c_real, mode, silu, want_y):
         assert conv_err(gy, conv[:c_real])[2] <= 1e-4
 
 
+def test_conv_with_fused_norm_tile_walk_sampled():
+    """The fused-norm conv on 64 channels with more tiles than the chip holds
+    workgroups (each walks several; its f32 tile is staged in the last
+    stage's buffer while the next tile's first stage loads into the other):
+    every pixel written, the borders, one pixel of every tile and seeded
+    picks against the oracle's norm of the oracle's convolution, to the
+    bar of the full-image test."""
+    H, W, cin, cout = 400, 700, 64, 64
+    seed = 900
+    x16 = synth.normal(17, seed, (H, W, cin), 1.0, np.float16)
+    w = synth.normal(17, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
+    b = synth.normal(17, seed + 2, (cout,), 0.02)
+    gamma = synth.uniform(17, seed + 3, (cout,), 0.5, 1.5)
+    assert ((H + 15) // 16) * ((W + 31) // 32) > 512
+    yn = nan_f16((H * W, cout))
+    ig.conv3x3_norm_nhwc(dev(x16.reshape(H * W, cin)), H, W, cin, 1, packed(w), cout, cout, dev(b), 1.0,
+                         dev(gamma), 1, 1e-12, None, yn)
+    got = host(yn)
+    assert not np.isnan(got.astype(np.float32)).any(), "a tile was not written"
+    corners = np.array([r * W + c for r in range(0, H, 16) for c in range(0, W, 32)], np.int64)
+    pix = np.unique(np.concatenate([sample_pixels(H, W, 512, seed=seed), corners]))
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    conv = O.conv2d_at(xc, w, pix, b)  # [npix, cout]
+    ref = O.rmsnorm(conv.T, gamma, silu=True).T
+    u = f16_ulps(got[pix], ref.astype(np.float16))
+    d = np.abs(got[pix].astype(np.float64) - ref)
+    exact = float(np.mean(u == 0))
+    print("conv+norm tile walk %dx%d (%d px): max ulp %d, exact %.5f" % (H, W, len(pix), u.max(), exact))
+    assert np.all((u <= 1) | (d <= 1e-5)) and exact >= 0.995
+
+
 @pytest.mark.parametrize("H,W,cin,cout,mode,acc,write_y,g", [
     (64, 64, 128, 128, 1, 1, 0, 8), (13, 29, 64, 256, 1, 1, 1, 8), (9, 13, 128, 64, 2, 0, 1, 4),
     (40, 33, 192, 128, 1, 0, 0, 14), (128, 128, 512, 512, 1, 1, 0, 8)])
