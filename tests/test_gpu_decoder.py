@@ -64,6 +64,19 @@ def test_config4_decode_256(full_decoder):
     assert _report("config4 256^2", got, ref) >= PSNR_MIN
 
 
+def test_full_decoder_non_square_ragged(full_decoder):
+    """The full-width decoder on a 20x28 latent (a 160x224 frame): ragged
+    tiles at every level, 560 attention tokens (a partial key block), the
+    single-pass attention, against the oracle's decode."""
+    w, dd = full_decoder
+    z = synth.decoder_latent(20, 28, config=4)
+    got = _run(dd, z, q_chunk=0)
+    assert got.shape == (3, 160, 224)
+    ref = O.decode(w, z, guard_log2=8, q_chunk=None)
+    assert np.all(np.isfinite(got))
+    assert _report("full decoder 20x28", got, ref) >= PSNR_MIN
+
+
 def test_config4_decode_256_single_pass_attention(full_decoder):
     w, dd = full_decoder
     z = synth.decoder_latent(32, 32, config=4)
