@@ -504,8 +504,29 @@ struct Run {
         const _Float16 *wk = reinterpret_cast<const _Float16 *>(a.k.w);
         const _Float16 *wv = reinterpret_cast<const _Float16 *>(a.v.w);
         const _Float16 *wp = reinterpret_cast<const _Float16 *>(a.proj.w);
-        gemm(xn, mp, C, C, wq, C, C, a.q.b, 1.f, q16, C, 1, 0);
-        gemm(xn, mp, C, C, wk, C, C, a.k.b, 1.f, k16, C, 1, 0);
+        // Q and K share xn: one launch covers both when the widths allow
+        Gemm2Args qk{};
+        qk.a = xn;
+        qk.b = wq;
+        qk.c = q16;
+        qk.bias = a.q.b;
+        qk.b2 = wk;
+        qk.c2 = k16;
+        qk.bias2 = a.k.b;
+        qk.nsplit = C;
+        qk.M = mp;
+        qk.N = 2 * C;
+        qk.K = C;
+        qk.lda = C;
+        qk.ldb = C;
+        qk.ldc = C;
+        qk.oscale = 1.f;
+        if (gemm2_supported(qk)) {
+            launch_gemm2(kEpiF16, qk, s);
+        } else {
+            gemm(xn, mp, C, C, wq, C, C, a.q.b, 1.f, q16, C, 1, 0);
+            gemm(xn, mp, C, C, wk, C, C, a.k.b, 1.f, k16, C, 1, 0);
+        }
         // V^T [C][mp] = Wv . xn^T; V's bias comes after P.V (P's rows sum to 1)
         gemm(wv, C, C, C, xn, mp, C, nullptr, 1.f, vt16, mp, 1, 0);
         if (pl.flash) {

@@ -106,10 +106,18 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
     const int g = bid / per_group, first = g * GROUP;
     const int gsz = (tiles_m - first) < GROUP ? (tiles_m - first) : GROUP;
     const int local = bid - g * per_group;
-    const int m0 = (first + local % gsz) * BM, n0 = (local / gsz) * BN;
+    const int m0 = (first + local % gsz) * BM;
+    int n0 = (local / gsz) * BN;
+    // a pair of products: the tile's half of the columns picks its B, C, bias
+    const bool second = p.nsplit > 0 && n0 >= p.nsplit;
+    const _Float16 *bmat = second ? p.b2 : p.b;
+    void *cmat = second ? p.c2 : p.c;
+    const float *bvec = second ? p.bias2 : p.bias;
+    const int nb = p.nsplit > 0 ? (second ? N - p.nsplit : p.nsplit) : N;  // B rows of this half
+    if (second) n0 -= p.nsplit;
 
     const __amdgpu_buffer_rsrc_t a_src = make_rsrc(p.a, (uint32_t)((uint64_t)M * p.lda * 2));
-    const __amdgpu_buffer_rsrc_t b_src = make_rsrc(p.b, (uint32_t)((uint64_t)N * p.ldb * 2));
+    const __amdgpu_buffer_rsrc_t b_src = make_rsrc(bmat, (uint32_t)((uint64_t)nb * p.ldb * 2));
 
     // this lane's source offset for each of its wave's loads: load
     // ii = wave + 8k fills LDS units ii*64 .. ii*64+63, i.e. rows 8ii..8ii+7
@@ -232,16 +240,16 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = (n + e < p.valid) ? __expf(osc * v[e] - rs[0]) * rs[1] : 0.f;
                     half4v h = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
-                    *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(p.c) + (int64_t)m * p.ldc + n) = h;
+                    *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(cmat) + (int64_t)m * p.ldc + n) = h;
                     continue;
                 }
                 v *= osc;
-                if (p.bias) v += *reinterpret_cast<const f32x4 *>(p.bias + n);
+                if (bvec) v += *reinterpret_cast<const f32x4 *>(bvec + n);
                 if (EPI == kEpiF16) {
                     half4v h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                    *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(p.c) + (int64_t)m * p.ldc + n) = h;
+                    *reinterpret_cast<half4v *>(reinterpret_cast<_Float16 *>(cmat) + (int64_t)m * p.ldc + n) = h;
                 } else {
-                    f32x4 *dst = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + (int64_t)m * p.ldc + n);
+                    f32x4 *dst = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(cmat) + (int64_t)m * p.ldc + n);
                     if (p.accumulate) v += *dst;
                     *dst = v;
                 }
@@ -295,15 +303,24 @@ bool gemm2_supported(const Gemm2Args &a)
     auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
     if (a.M <= 0 || a.N <= 0 || a.K <= 0) return false;
     if (a.K % KST || a.N % 64 || a.lda % 8 || a.ldb % 8 || a.ldc % 4) return false;
-    if (a.lda < a.K || a.ldb < a.K || a.ldc < a.N) return false;
     if (!al16(a.a) || !al16(a.b) || !al16(a.c) || (a.bias && !al16(a.bias))) return false;
+    if ((uint64_t)a.M * a.lda * 2 >= kOOB) return false;
+    if (a.nsplit > 0) {
+        // two products: both halves tile by 256 columns, so no tile straddles
+        const int n2 = a.N - a.nsplit;
+        if (a.nsplit % 256 || n2 <= 0 || n2 % 256) return false;
+        if (!al16(a.b2) || !al16(a.c2) || (a.bias2 && !al16(a.bias2))) return false;
+        if (a.lda < a.K || a.ldb < a.K || a.ldc < (a.nsplit > n2 ? a.nsplit : n2)) return false;
+        return (uint64_t)a.nsplit * a.ldb * 2 < kOOB && (uint64_t)n2 * a.ldb * 2 < kOOB;
+    }
+    if (a.lda < a.K || a.ldb < a.K || a.ldc < a.N) return false;
     // the buffer resources span M*lda and N*ldb halves; offsets stay below kOOB
-    if ((uint64_t)a.M * a.lda * 2 >= kOOB || (uint64_t)a.N * a.ldb * 2 >= kOOB) return false;
-    return true;
+    return (uint64_t)a.N * a.ldb * 2 < kOOB;
 }
 
 void launch_gemm2(int epi, const Gemm2Args &a, hipStream_t s)
 {
+    if (a.nsplit > 0 && epi != kEpiF32 && epi != kEpiF16) return;
     switch (epi) {
     case kEpiF32: launch_e<kEpiF32>(a, s); break;
     case kEpiF16: launch_e<kEpiF16>(a, s); break;

@@ -83,6 +83,13 @@ struct Gemm2Args {
     int valid;             // kEpiStats, kEpiProb: columns >= valid are masked
     int accumulate;        // kEpiF32: C += result
     float oscale;
+    // a pair of products sharing A in one launch (kEpiF32, kEpiF16): with
+    // nsplit > 0, columns [nsplit, N) use b2 [N - nsplit][ldb], c2 and bias2
+    // (column n - nsplit); nsplit must be a multiple of 256
+    const _Float16 *b2 = nullptr;
+    void *c2 = nullptr;
+    const float *bias2 = nullptr;
+    int nsplit = 0;
 };
 
 // true when the shapes, strides and alignment fit k_gemm2 (K % 64 == 0,
