@@ -89,17 +89,28 @@ struct Geo {
 
 // Stage buffer size (16-byte units): the patch, padded to whole wave loads,
 // then the nine taps' weights. A workgroup may walk several tiles only when
-// its f32 output staging (4 rows x TW x BN) fits one stage buffer, the one
-// the next tile's first stage is not landing in.
+// its f32 output staging (4 rows x TW pixels, a pixel's BN channels at a
+// pitch of SP floats) fits one stage buffer, the one the next tile's first
+// stage is not landing in.
 template <int MODE, int BN>
 constexpr int stage_units()
 {
     return (Geo<MODE>::PH * Geo<MODE>::PW * 2 + 63) / 64 * 64 + 9 * BN * 2;
 }
-template <int MODE, int BN>
+// Staging pitch: the fused norm reads a pixel's channels 32 per lane; at
+// 128 channels (4 lanes per pixel) 8 floats of padding per pixel spread those
+// reads over the LDS banks. The plain epilogue reads the rows linearly and
+// needs none; the 64-channel norm keeps the plain pitch (padding it costs
+// that instantiation register spills).
+template <int BN, bool NORM>
+constexpr int stage_pitch()
+{
+    return (NORM && BN == 128) ? BN + 8 : BN;
+}
+template <int MODE, int BN, bool NORM>
 constexpr bool can_walk()
 {
-    return 4 * TW * BN * 4 <= stage_units<MODE, BN>() * 16;
+    return 4 * TW * stage_pitch<BN, NORM>() * 4 <= stage_units<MODE, BN>() * 16;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -140,7 +151,8 @@ void k_conv_halo(IgemmArgs p)
     static_assert(A_PER_WAVE <= 8, "patch offsets per lane");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     // the output tile leaves through LDS, 4 tile rows per pass
-    static_assert(4 * TW * BN * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
+    constexpr int SP = stage_pitch<BN, NORM>();
+    static_assert(4 * TW * SP * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
 
     __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
     // the fused norm's gamma, read from LDS in the epilogue (a tile spans
@@ -262,7 +274,7 @@ void k_conv_halo(IgemmArgs p)
 
     int gs = 0;  // stages run so far: stage gs sits in buffer gs & 1
     for (; t < t_end; t += t_step) {
-        const bool has_next = can_walk<MODE, BN>() && t + t_step < t_end;
+        const bool has_next = can_walk<MODE, BN, NORM>() && t + t_step < t_end;
         const Tile nxt = make_tile(has_next ? t + t_step : t);
 
         f32x16 acc[FM][FN];
@@ -324,7 +336,7 @@ void k_conv_halo(IgemmArgs p)
     // pixel (4 wm + i, 8 (r / 4) + 4 (l / 32) + r % 4), channel
     // wn BN/2 + 32 j + l % 32. Pass q stages tile rows {q, 4 + q, 8 + q,
     // 12 + q} (wave row i = q of the four wave row groups) as [4][TW][BN]
-    // f32; then every thread writes 16 contiguous bytes, so each tile row
+    // f32 (pixel pitch SP); then every thread writes 16 contiguous bytes, so each tile row
     // leaves as one run of TW * BN * 4 bytes (contiguous when BN is the
     // output row width).
     // With a next tile its first stage is landing in the other buffer:
@@ -344,7 +356,7 @@ void k_conv_halo(IgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int px = (r >> 2) * 8 + fh * 4 + (r & 3);
-                stg[(wm * TW + px) * BN + wn * (BN / WN) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
+                stg[(wm * TW + px) * SP + wn * (BN / WN) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
             }
         __syncthreads();
         constexpr int V4 = 4 * TW * BN / 4;  // 16-byte pieces staged per pass
@@ -357,7 +369,8 @@ void k_conv_halo(IgemmArgs p)
                 const int ch = e % BN;
                 const int oy = y0 + FM * wr + q, ox = x0 + px;
                 if (oy < Hout && ox < Wout) {
-                    float4 val = reinterpret_cast<const float4 *>(stg)[v];
+                    float4 val = (SP == BN) ? reinterpret_cast<const float4 *>(stg)[v]
+                                            : *reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + ch);
                     float *dst = out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch;
                     if (accum) {
                         const float4 o = *reinterpret_cast<const float4 *>(dst);
@@ -388,14 +401,19 @@ void k_conv_halo(IgemmArgs p)
             // pixel, 32 channels each (the tile holds every channel: BN = N)
             constexpr int TPP = NT / (4 * TW);
             static_assert(BN / TPP == 32, "32 channels per lane");
-            const int pi = tid / TPP, cb = (tid % TPP) * 32;
+            const int pi = tid / TPP, q4 = tid % TPP, cb = q4 * 32;
+            // lanes 2 and 3 of a pixel take their 32 channels starting at the
+            // fifth float4: with the padded pitch, a read then touches at most
+            // two lanes per bank group (8 when every lane starts at its first);
+            // with 2 lanes per pixel rot is 0
+            const int rot = (q4 >> 1) * 4;
             const int wr = pi / TW, px = pi % TW;
-            const float4 *sv = reinterpret_cast<const float4 *>(stg + (wr * TW + px) * BN + cb);
-            float4 v[8];
+            const float4 *sv = reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + cb);
+            float4 v[8];  // v[k] holds channels cb + 4 ((k + rot) & 7) .. + 3
             float ss = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                v[k] = sv[k];
+                v[k] = sv[(k + rot) & 7];
                 ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
             }
 #pragma unroll
@@ -405,20 +423,25 @@ void k_conv_halo(IgemmArgs p)
             if (oy < Hout && ox < Wout) {
                 const float4 *g4 = reinterpret_cast<const float4 *>(gam + cb);
                 _Float16 *dst = p.ny + ((int64_t)oy * Wout + ox) * BN + cb;
+                // SiLU as y * rcp(1 + exp(-y)) with the hardware reciprocal
+                // (~1 ulp): the epilogue has no partner workgroup to hide
+                // behind, and a full-precision divide is about ten
+                // instructions. Without SiLU the factor is rcp(1) = 1 exactly.
+                const bool silu = p.norm_silu != 0;
 #pragma unroll
                 for (int k = 0; k < 8; k += 2) {
+                    const int u = (k + rot) & 7;  // even: 8 channels, 16-byte aligned
                     float o[8] = {v[k].x, v[k].y, v[k].z, v[k].w, v[k + 1].x, v[k + 1].y, v[k + 1].z, v[k + 1].w};
-                    const float4 ga = g4[k], gb = g4[k + 1];
+                    const float4 ga = g4[u], gb = g4[u + 1];
                     const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
                     half8 h;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        float y = o[e] * inv * gm[e];
-                        // fast divide: the epilogue is on the critical path
-                        if (p.norm_silu) y = __fdividef(y, 1.0f + __expf(-y));
-                        h[e] = (_Float16)y;
+                        const float y = o[e] * inv * gm[e];
+                        const float ex = silu ? __expf(-y) : 0.f;
+                        h[e] = (_Float16)(y * __builtin_amdgcn_rcpf(1.0f + ex));
                     }
-                    *reinterpret_cast<half8 *>(dst + 4 * k) = h;
+                    *reinterpret_cast<half8 *>(dst + 4 * u) = h;
                 }
             }
         }
@@ -453,7 +476,7 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
     // resident at once (8 waves per compute unit), a multiple of 8 for the
     // XCD schedule; else one tile each
     int grid = tiles;
-    if (can_walk<MODE, BN>()) {
+    if (can_walk<MODE, BN, NORM>()) {
         const int slots = resident_slots(8 / NW) & ~7;
         if (slots > 0 && slots < tiles) grid = slots;
     }
