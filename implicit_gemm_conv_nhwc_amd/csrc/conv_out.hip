@@ -21,7 +21,7 @@
 //    patch of the stage's channels streams into double-buffered LDS by
 //    direct-to-LDS loads (zero outside the image); the stage's weights (9
 //    taps, the lane's output channel, 8 of the 32 channels) are read from
-//    the blocked weight plane into registers;
+//    the blocked weight plane into registers one stage ahead;
 //  * a patch pixel's 32 channels are 4 units of 16 bytes, unit u stored at
 //    u ^ ((pixel >> 2) & 3), so the 16 lanes reading one unit of 16
 //    consecutive pixels touch 16 distinct bank groups;
@@ -106,14 +106,11 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
     // + 7 of the stage; zero for o >= cout
     const int o = col;
     const int nst = cin_p / CS;
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nst) issue(st + 1, buf ^ 1);
-        half8 wt[9];
-        // blocked plane [cin_p/16][9][cout_p][16]: channel 32 st + 8 grp + e
+    // the stage's weights: blocked plane [cin_p/16][9][cout_p][16], channel
+    // 32 st + 8 grp + e. They are read one stage ahead, before the next
+    // stage's patch loads: loads complete in order, so a wait for weights
+    // read after those would wait for the patch too
+    auto load_w = [&](int st, half8 *wt) __attribute__((always_inline)) {
         const int c16 = 2 * st + (grp >> 1), ci = 8 * (grp & 1);
 #pragma unroll
         for (int t = 0; t < 9; ++t) {
@@ -121,6 +118,18 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
                 wt[t] = *reinterpret_cast<const half8 *>(plane + ((int64_t)(c16 * 9 + t) * cout_p + o) * 16 + ci);
             else
                 wt[t] = half8{};
+        }
+    };
+    half8 wt[9], wn[9];
+    load_w(0, wt);
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nst) {
+            load_w(st + 1, wn);
+            issue(st + 1, buf ^ 1);
         }
         const u32x4 *sA = lds + buf * STAGE;
 #pragma unroll
@@ -137,9 +146,14 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 9; ++t) wt[t] = wn[t];
     }
     // lane (grp, col) holds output channels 4 grp + r of pixel column col;
     // rows r0 .. r1 - 1 are stored, output planes HWo apart
+    float bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bv[r] = (bias && 4 * grp + r < cout) ? bias[4 * grp + r] : 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int oy = y0 + RPW * wave + g / (OW / 16), ox = x0 + 16 * (g % (OW / 16)) + col;
@@ -147,7 +161,7 @@ __global__ __launch_bounds__(NT) void k_conv_out(const _Float16 *__restrict__ x,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ch = 4 * grp + r;
-            if (ch < cout) out[ch * HWo + (int64_t)oy * W + ox] = acc[g][r] + (bias ? bias[ch] : 0.f);
+            if (ch < cout) out[ch * HWo + (int64_t)oy * W + ox] = acc[g][r] + bv[r];
         }
     }
 }
