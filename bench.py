@@ -471,6 +471,24 @@ def digest_trace(path, roof_launches):
         avg = sum(x[2] for x in last) / len(last)
         print("roofline region: last %d dispatches of %s (grid %s): avg %.2f us" % (
             len(last), ROOF_KERNEL, last[-1][3], avg))
+    # the last decode alone: from its latent cast (k_latent) to its output
+    # conv (k_conv_out), by kernel and grid
+    starts = [i for i, x in enumerate(seq) if "k_latent" in x[1]]
+    if starts:
+        dec = seq[starts[-1]:]
+        ends = [i for i, x in enumerate(dec) if "k_conv_out" in x[1]]
+        dec = dec[:ends[0] + 1] if ends else dec
+        per = {}
+        for _, name, t, grid in dec:
+            short = name if len(name) < 70 else name[:67] + "..."
+            e = per.setdefault((short, grid), [0, 0.0])
+            e[0] += 1
+            e[1] += t
+        busy = sum(v[1] for v in per.values())
+        print("\nlast decode: %d dispatches, %.1f us of kernel time" % (len(dec), busy))
+        print("kernel | grid (threads) | calls | total us | share")
+        for (name, grid), (n, t) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+            print("%s | %s | %d | %.1f | %.1f%%" % (name, grid, n, t, 100 * t / busy))
 
 
 # ---------------------------------------------------------------------------
