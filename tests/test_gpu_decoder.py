@@ -48,6 +48,20 @@ def test_small_decoder(h0, w0, q_chunk):
     assert _report("small %dx%d" % (h0, w0), got, ref) >= PSNR_MIN
 
 
+def test_decoder_256_wide_attention_pairs_q_and_k():
+    """A decoder 256 channels wide at the latent: the attention's Q and K
+    then come from one GEMM launch over both weight planes (each half one
+    256-column tile), here on a ragged 6x10 latent (60 tokens)."""
+    spec = synth.DecoderSpec(zc=4, c_in=256, stages=(256, 128, 64), n_res=1, out_c=3)
+    w = synth.decoder_weights(spec, seed_config=4)
+    z = synth.decoder_latent(6, 10, zc=spec.zc)
+    got = _run(ig.DeviceDecoder(w), z)
+    ref = O.decode(w, z, guard_log2=8)
+    assert got.shape == ref.shape == (3, 48, 80)
+    assert np.all(np.isfinite(got))
+    assert _report("256-wide 6x10", got, ref) >= PSNR_MIN
+
+
 @pytest.fixture(scope="module")
 def full_decoder():
     spec = synth.decoder_spec()
