@@ -89,9 +89,9 @@ struct Geo {
 
 // Stage buffer size (16-byte units): the patch, padded to whole wave loads,
 // then the nine taps' weights. A workgroup may walk several tiles only when
-// its f32 output staging (4 rows x TW pixels, a pixel's BN channels at a
-// pitch of SP floats) fits one stage buffer, the one the next tile's first
-// stage is not landing in.
+// its f32 output staging (RS rows x TW pixels per pass, a pixel's BN
+// channels at a pitch of SP floats) fits one stage buffer, the one the next
+// tile's first stage is not landing in.
 template <int MODE, int BN>
 constexpr int stage_units()
 {
@@ -107,10 +107,18 @@ constexpr int stage_pitch()
 {
     return (NORM && BN == 128) ? BN + 8 : BN;
 }
+// Tile rows staged per epilogue pass: 4 (one per wave row group), or 2 for
+// the 128-channel fused norm, whose 4-row staging would not fit one stage
+// buffer and so could not walk tiles
+template <int BN, bool NORM>
+constexpr int stage_rows()
+{
+    return (NORM && BN == 128) ? 2 : 4;
+}
 template <int MODE, int BN, bool NORM>
 constexpr bool can_walk()
 {
-    return 4 * TW * stage_pitch<BN, NORM>() * 4 <= stage_units<MODE, BN>() * 16;
+    return stage_rows<BN, NORM>() * TW * stage_pitch<BN, NORM>() * 4 <= stage_units<MODE, BN>() * 16;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -152,7 +160,8 @@ void k_conv_halo(IgemmArgs p)
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     // the output tile leaves through LDS, 4 tile rows per pass
     constexpr int SP = stage_pitch<BN, NORM>();
-    static_assert(4 * TW * SP * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
+    constexpr int RS = stage_rows<BN, NORM>();  // rows staged per pass
+    static_assert(RS * TW * SP * 4 <= 2 * STAGE * 16, "output staging fits the stage buffers");
 
     __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
     // the fused norm's gamma, read from LDS in the epilogue (a tile spans
@@ -352,22 +361,27 @@ void k_conv_halo(IgemmArgs p)
 #pragma unroll
     for (int q = 0; q < FM; ++q) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+    for (int h = 0; h < 4 / RS; ++h) {
+        // pass (q, h): wave row groups h RS .. h RS + RS - 1 stage their row q
+        if (wm / RS == h) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int px = (r >> 2) * 8 + fh * 4 + (r & 3);
-                stg[(wm * TW + px) * SP + wn * (BN / WN) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
-            }
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int px = (r >> 2) * 8 + fh * 4 + (r & 3);
+                    stg[((wm % RS) * TW + px) * SP + wn * (BN / WN) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
+                }
+        }
         __syncthreads();
-        constexpr int V4 = 4 * TW * BN / 4;  // 16-byte pieces staged per pass
+        constexpr int V4 = RS * TW * BN / 4;  // 16-byte pieces staged per pass
         if ((!NORM && p.yg) || p.write_out) {
 #pragma unroll
             for (int v = tid; v < V4; v += NT) {
                 const int e = v * 4;
-                const int wr = e / (TW * BN);  // wave row group: tile row FM * wr + q
+                const int wr = e / (TW * BN);  // staged row: tile row FM (h RS + wr) + q
                 const int px = (e / BN) % TW;
                 const int ch = e % BN;
-                const int oy = y0 + FM * wr + q, ox = x0 + px;
+                const int oy = y0 + FM * (h * RS + wr) + q, ox = x0 + px;
                 if (oy < Hout && ox < Wout) {
                     float4 val = (SP == BN) ? reinterpret_cast<const float4 *>(stg)[v]
                                             : *reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + ch);
@@ -397,29 +411,32 @@ void k_conv_halo(IgemmArgs p)
             }
         }
         if constexpr (NORM) {
-            // the staged 4 x TW pixels' RMS_norm: TPP consecutive lanes per
-            // pixel, 32 channels each (the tile holds every channel: BN = N)
-            constexpr int TPP = NT / (4 * TW);
-            static_assert(BN / TPP == 32, "32 channels per lane");
-            const int pi = tid / TPP, q4 = tid % TPP, cb = q4 * 32;
+            // the staged RS x TW pixels' RMS_norm: TPP consecutive lanes per
+            // pixel, CPL channels each (the tile holds every channel: BN = N)
+            constexpr int TPP = NT / (RS * TW);
+            constexpr int CPL = BN / TPP;
+            constexpr int NV = CPL / 4;  // float4 per lane
+            static_assert(CPL == 32 || CPL == 16, "16 or 32 channels per lane");
+            const int pi = tid / TPP, q4 = tid % TPP, cb = q4 * CPL;
             // lanes 2 and 3 of a pixel take their 32 channels starting at the
             // fifth float4: with the padded pitch, a read then touches at most
             // two lanes per bank group (8 when every lane starts at its first);
-            // with 2 lanes per pixel rot is 0
-            const int rot = (q4 >> 1) * 4;
+            // with 2 lanes per pixel rot is 0; with 16 channels per lane
+            // there is no rotation
+            const int rot = (CPL == 32) ? (q4 >> 1) * 4 : 0;
             const int wr = pi / TW, px = pi % TW;
             const float4 *sv = reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + cb);
-            float4 v[8];  // v[k] holds channels cb + 4 ((k + rot) & 7) .. + 3
+            float4 v[NV];  // v[k] holds channels cb + 4 ((k + rot) % NV) .. + 3
             float ss = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                v[k] = sv[(k + rot) & 7];
+            for (int k = 0; k < NV; ++k) {
+                v[k] = sv[(k + rot) & (NV - 1)];
                 ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
             }
 #pragma unroll
             for (int off = TPP / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, TPP);
             const float inv = sqrtf((float)p.norm_c) / fmaxf(sqrtf(ss), p.norm_eps);
-            const int oy = y0 + FM * wr + q, ox = x0 + px;
+            const int oy = y0 + FM * (h * RS + wr) + q, ox = x0 + px;
             if (oy < Hout && ox < Wout) {
                 const float4 *g4 = reinterpret_cast<const float4 *>(gam + cb);
                 _Float16 *dst = p.ny + ((int64_t)oy * Wout + ox) * BN + cb;
@@ -429,8 +446,8 @@ void k_conv_halo(IgemmArgs p)
                 // instructions. Without SiLU the factor is rcp(1) = 1 exactly.
                 const bool silu = p.norm_silu != 0;
 #pragma unroll
-                for (int k = 0; k < 8; k += 2) {
-                    const int u = (k + rot) & 7;  // even: 8 channels, 16-byte aligned
+                for (int k = 0; k < NV; k += 2) {
+                    const int u = (k + rot) & (NV - 1);  // even: 8 channels, 16-byte aligned
                     float o[8] = {v[k].x, v[k].y, v[k].z, v[k].w, v[k + 1].x, v[k + 1].y, v[k + 1].z, v[k + 1].w};
                     const float4 ga = g4[u], gb = g4[u + 1];
                     const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
@@ -446,6 +463,7 @@ void k_conv_halo(IgemmArgs p)
             }
         }
         __syncthreads();
+    }
     }
     cur = nxt;
     }

@@ -396,34 +396,39 @@ def test_conv_with_fused_norm(H, W, cin, cout, c_real, mode, silu, want_y):
         assert conv_err(gy, conv[:c_real])[2] <= 1e-4
 
 
-def test_conv_with_fused_norm_tile_walk_sampled():
-    """The fused-norm conv on 64 channels with more tiles than the chip holds
-    workgroups (each walks several; its f32 tile is staged in the last
-    stage's buffer while the next tile's first stage loads into the other):
-    every pixel written, the borders, one pixel of every tile and seeded
-    picks against the oracle's norm of the oracle's convolution, to the
-    bar of the full-image test."""
-    H, W, cin, cout = 400, 700, 64, 64
-    seed = 900
+@pytest.mark.parametrize("H,W,cin,cout,mode", [
+    (400, 700, 64, 64, 1), (300, 530, 128, 128, 1), (150, 260, 128, 128, 2)])
+def test_conv_with_fused_norm_tile_walk_sampled(H, W, cin, cout, mode):
+    """The fused-norm conv with more tiles than the chip holds workgroups
+    (each walks several; its f32 rows are staged in the last stage's buffer
+    while the next tile's first stage loads into the other; at 128 channels
+    two rows per staging pass), on ragged frames: every pixel written, the
+    borders, one pixel of every tile and seeded picks against the oracle's
+    norm of the oracle's convolution, to the bar of the full-image test."""
+    seed = 900 + cout + mode
     x16 = synth.normal(17, seed, (H, W, cin), 1.0, np.float16)
     w = synth.normal(17, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
     b = synth.normal(17, seed + 2, (cout,), 0.02)
     gamma = synth.uniform(17, seed + 3, (cout,), 0.5, 1.5)
-    assert ((H + 15) // 16) * ((W + 31) // 32) > 512
-    yn = nan_f16((H * W, cout))
-    ig.conv3x3_norm_nhwc(dev(x16.reshape(H * W, cin)), H, W, cin, 1, packed(w), cout, cout, dev(b), 1.0,
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    osc = 256.0 if mode == 2 else 1.0
+    assert ((Ho + 15) // 16) * ((Wo + 31) // 32) > (512 if cout == 64 else 256)
+    yn = nan_f16((Ho * Wo, cout))
+    ig.conv3x3_norm_nhwc(dev(x16.reshape(H * W, cin)), H, W, cin, mode, packed(w), cout, cout, dev(b), osc,
                          dev(gamma), 1, 1e-12, None, yn)
     got = host(yn)
     assert not np.isnan(got.astype(np.float32)).any(), "a tile was not written"
-    corners = np.array([r * W + c for r in range(0, H, 16) for c in range(0, W, 32)], np.int64)
-    pix = np.unique(np.concatenate([sample_pixels(H, W, 512, seed=seed), corners]))
+    corners = np.array([r * Wo + c for r in range(0, Ho, 16) for c in range(0, Wo, 32)], np.int64)
+    edges = np.array([(Ho - 1) * Wo + c for c in range(Wo)] + [r * Wo + Wo - 1 for r in range(Ho)], np.int64)
+    pix = np.unique(np.concatenate([sample_pixels(Ho, Wo, 512, seed=seed), corners, edges]))
     xc = nhwc_to_chw(x16.astype(np.float64), H, W)
-    conv = O.conv2d_at(xc, w, pix, b)  # [npix, cout]
+    conv = osc * O.conv2d_at(xc, w, pix, up2=(mode == 2)) + b[None, :]  # [npix, cout]
     ref = O.rmsnorm(conv.T, gamma, silu=True).T
     u = f16_ulps(got[pix], ref.astype(np.float16))
     d = np.abs(got[pix].astype(np.float64) - ref)
     exact = float(np.mean(u == 0))
-    print("conv+norm tile walk %dx%d (%d px): max ulp %d, exact %.5f" % (H, W, len(pix), u.max(), exact))
+    print("conv+norm tile walk %dx%d %d->%d mode %d (%d px): max ulp %d, exact %.5f" % (
+        H, W, cin, cout, mode, len(pix), u.max(), exact))
     assert np.all((u <= 1) | (d <= 1e-5)) and exact >= 0.995
 
 
