@@ -21,7 +21,7 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libigconv.so")
 ARCH = os.environ.get("IG_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "igemm.hip", "gemm2.hip", "conv_halo.hip", "conv_out.hip", "attn_flash.hip", "groupnorm.hip", "elementwise.hip", "decoder.hip"]
+SOURCES = ["api.hip", "igemm.hip", "gemm2.hip", "conv_halo.hip", "conv_ws.hip", "conv_out.hip", "attn_flash.hip", "groupnorm.hip", "elementwise.hip", "decoder.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

@@ -506,6 +506,10 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return;
+    if (conv_ws_supported(mode, a)) {
+        launch_conv_ws(mode, a, s);
+        return;
+    }
     if (a.ngamma) {
         // the fused RMS_norm needs every channel of a pixel in one tile
         if (mode == kConv3x3) {

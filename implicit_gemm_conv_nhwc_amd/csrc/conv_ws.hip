@@ -1,0 +1,574 @@
+// The 3x3 convolutions (plain and nearest-2x upsampled) at 128 input and
+// 128 output channels with the weights held in registers for the whole
+// launch, for gfx950.
+//
+// Page "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs", module doc: every
+// 3x3 conv an implicit GEMM with the nearest-2x upsample folded into the
+// gather, f16 inputs, f32 accumulation; `Rec::conv_s` (raw f32 times
+// oscale); `qconv` (K ordered (tap, channel)). Page "cortiq-engine 0.7.6,
+// src/vae.rs", `Conv2d::apply` and `upsample2x` for the definition.
+//
+// Why a second conv kernel: a 128 -> 128 conv has 295 KB of weights, which
+// fit in the register files of one compute unit (512 KB). Held there, a
+// workgroup never reloads them per tile, and the only operand that streams
+// through LDS is the input patch.
+//
+//  * one workgroup per compute unit: 4 wave64s, one per SIMD; wave w owns
+//    output channels 32w .. 32w + 31 and keeps their 72 weight fragments
+//    (16 input channels x 9 taps each, the A operand of
+//    v_mfma_f32_32x32x16_f16) -- 64 in AGPRs, 8 in VGPRs -- for the whole
+//    launch; the MFMAs are inline asm so the fragments are read where they
+//    live instead of being copied before every use;
+//  * a tile is 4 output rows x 32 columns x all 128 channels; the B operand
+//    is one output row's 32 pixels x 16 channels of the input patch, so
+//    lane l's accumulators hold pixel l % 32 and 16 of the wave's channels;
+//  * the reduction runs in 4 stages of 32 input channels. A stage's
+//    (4+2) x 34-pixel patch (half resolution for the folded upsample,
+//    4 x 18) streams into LDS with direct-to-LDS buffer loads, 64 bytes per
+//    pixel; four stage buffers, filled three stages ahead, so a patch has
+//    two stages (~2 us) to arrive. Each fragment read from LDS feeds every
+//    (output row, tap row) pair that uses it;
+//  * the finished tile (oscale, bias applied) is staged in LDS and leaves
+//    during the next tile's stages, one row per stage: its stores (and,
+//    when accumulating, the loads of the stream it adds to, issued a stage
+//    ahead) overlap the next tile's MFMAs instead of following them. The
+//    same pass can emit the guarded f16 cast of the result or, since a tile
+//    holds every channel of a pixel, the pixel's RMS_norm (+ SiLU) as f16;
+//  * every global access of the stage loop is a buffer instruction, and
+//    each stage issues its drain's stores and loads before its patch loads:
+//    the wait at a stage's start ("all but the last stage's patch loads")
+//    then holds whatever the epilogue writes;
+//  * workgroups walk the tiles persistently; workgroup b runs on XCD b % 8
+//    and each XCD takes a contiguous range of tile rows (shared halos stay
+//    in its L2).
+#include "ig_internal.h"
+
+namespace ig {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TH = 4;        // output rows per tile
+constexpr int TW = 32;       // output columns per tile (one MFMA operand)
+constexpr int CK = 32;       // input channels per stage (two MFMA K-steps)
+constexpr int NW = 4;        // waves per workgroup, one per SIMD
+constexpr int NT = 64 * NW;  // threads per workgroup
+constexpr int BN = 128;      // output channels: 32 per wave
+constexpr int NST = 4;       // stages: 128 input channels
+constexpr int NBUF = 4;      // patch buffers (stage s lands in buffer s)
+constexpr int SP = BN + 4;   // staged floats per pixel (spreads the LDS banks)
+constexpr int NWF = 8;       // weight fragments kept in VGPRs (the rest in AGPRs)
+constexpr uint32_t kOOB = 0x7fff0000u;  // a buffer offset past every resource here
+
+template <int MODE>
+struct WGeo {
+    static constexpr int PH = (MODE == kConv3x3) ? TH + 2 : TH / 2 + 2;
+    static constexpr int PW = (MODE == kConv3x3) ? TW + 2 : TW / 2 + 2;
+    static constexpr int A_UNITS = PH * PW * 4;                  // 16-byte units (pixel, channel quarter)
+    static constexpr int A_INSTR = (A_UNITS + 63) / 64;          // wave loads that carry data
+    static constexpr int APW = (A_INSTR + NW - 1) / NW;          // loads per wave per stage (all waves)
+    static constexpr int A_PAD = APW * NW * 64;                  // units per patch buffer
+    // patch row read by output row r at tap row dy (patch origin: one row
+    // above the tile, at half resolution for the upsample)
+    __device__ static constexpr int arow(int r, int dy) { return (MODE == kConv3x3) ? r + dy : (r + dy + 1) >> 1; }
+    // patch column read by tile column x at tap column dx
+    __device__ static int pcol(int x, int dx) { return (MODE == kConv3x3) ? x + dx : ((x + dx + 1) >> 1); }
+};
+
+template <int MODE>
+constexpr int ws_lds_bytes()
+{
+    return NBUF * WGeo<MODE>::A_PAD * 16 + TH * TW * SP * 4 + 2 * BN * 4;
+}
+
+// a raw buffer descriptor in SGPRs (stride 0, num_records bytes)
+__device__ __forceinline__ i32x4 srd(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// A 16-byte-per-lane direct-to-LDS buffer load as asm: the kernel orders
+// these loads itself (the wait at each stage's start), so the compiler must
+// not see them -- as builtins, every LDS read after one would wait for it.
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds_addr, uint32_t voff)
+{
+    unsigned saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+// 16-byte buffer load into registers, also hidden from the compiler's wait
+// tracking (the stage-start wait covers it)
+__device__ __forceinline__ f32x4 ld16(i32x4 rsrc, uint32_t voff)
+{
+    f32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voff), "s"(rsrc) : "memory");
+    return v;
+}
+
+// 16-byte buffer store (a wait state after it: its data registers may be
+// rewritten by the next instruction)
+__device__ __forceinline__ void st16(i32x4 rsrc, uint32_t voff, f32x4 v, bool nt)
+{
+    if (nt)
+        asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt\n\ts_nop 0" ::"v"(v), "v"(voff), "s"(rsrc) : "memory");
+    else
+        asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 0" ::"v"(v), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// 8-byte buffer store (four f16)
+__device__ __forceinline__ void st8(i32x4 rsrc, uint32_t voff, half4v v)
+{
+    asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 0" ::"v"(v), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// A workgroup barrier after this wave's LDS operations have completed. No
+// wait for vector memory: the stage loop orders its loads itself (the
+// fence of __syncthreads would drain the prefetched stages).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The MFMAs: acc += W.B with the weight fragment in an AGPR ("a") or a
+// VGPR ("v"); the first of a tile's chain starts from zero (no SrcC read);
+// a chain's MFMAs read their predecessor's result as SrcC in the same
+// registers (no wait states needed); the last pads 16 wait states so the
+// epilogue's VALU may read the result. Volatile: two MFMAs with the same
+// operands (the upsample's rows 1 and 2 at tap row 0 read the same patch
+// row) must both run -- merged, the compiler would copy the result with a
+// VALU move that does not wait for the MFMA.
+template <bool AG>
+__device__ __forceinline__ void mma(f32x16 &acc, const half8 &w, const half8 &b, int kind)
+{
+    if (kind == 0) {
+        if (AG) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "a"(w), "v"(b));
+        else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(w), "v"(b));
+    } else if (kind == 1) {
+        if (AG) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "a"(w), "v"(b));
+        else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(w), "v"(b));
+    } else {
+        if (AG) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(acc) : "a"(w), "v"(b));
+        else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(acc) : "v"(w), "v"(b));
+    }
+}
+
+struct WTile {
+    int y0, x0;
+    uint32_t aoff[4];  // per patch load of this lane: source byte offset at stage 0 (kOOB: zeros)
+};
+
+// Sum over the 16 lanes of a DPP row (xor 1, xor 2 within quads, then the
+// mirrored half and the mirrored row): every lane gets the row's sum.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+    return v;
+}
+
+// The epilogue's outputs, fixed per instantiation so that every stage
+// issues the same number of memory operations (the stage wait counts them):
+// ACC adds the f32 output's current values (the residual stream), WOUT
+// stores the f32 result, YG stores its guarded f16 cast, NORM stores the
+// pixel's f16 RMS_norm (+ SiLU).
+template <int MODE, bool NORM, bool ACC, bool WOUT, bool YG>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_conv_ws(IgemmArgs p)
+{
+    using G = WGeo<MODE>;
+    constexpr int PH = G::PH, PW = G::PW;
+    constexpr int A_INSTR = G::A_INSTR, A_PAD = G::A_PAD, APW = G::APW;
+    static_assert(APW <= 4, "patch loads per lane");
+    static_assert(NST == TH, "one staged row drained per stage");
+    static_assert(NBUF == NST, "stage s lands in buffer s");
+    static_assert(!(NORM && (ACC || YG)), "the fused norm writes neither a sum nor a cast");
+    // memory operations per stage besides the patch loads
+    constexpr int NDL = ACC ? 4 : 0;                                   // stream loads
+    constexpr int NDS = (WOUT ? 4 : 0) + (YG ? 4 : 0) + (NORM ? 2 : 0);  // stores
+    // At a stage's start the stage's patch (issued three stages earlier)
+    // and the stream values of the row it drains (two stages earlier) must
+    // have landed; after those loads each stage issues its stores, the next
+    // stream loads and its patch loads, and at most this many operations
+    // issued later may still be in flight.
+    constexpr int WAITN = 2 * APW + NDS + NDL;
+    static_assert(WAITN < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) u32x4 lds[ws_lds_bytes<MODE>() / 16];
+    float *stg = reinterpret_cast<float *>(lds + NBUF * A_PAD);  // [TH][TW][SP]
+    float *sbias = stg + TH * TW * SP;                           // [BN]
+    float *sgam = sbias + BN;                                    // [BN]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
+    const int fx = lane & 31;  // tile column of this lane's B fragments and accumulators
+    const int fh = lane >> 5;  // channel half (of a K-step's 16) in the fragments
+
+    const int H = p.H, W = p.W, cin_p = p.cin_p;
+    const int Hout = (MODE == kConv3x3Up2) ? 2 * H : H;
+    const int Wout = (MODE == kConv3x3Up2) ? 2 * W : W;
+    const int tiles_x = (Wout + TW - 1) / TW;
+    const int T = ((Hout + TH - 1) / TH) * tiles_x;
+
+    // tile schedule: XCD x (workgroups b = x mod 8) takes the contiguous
+    // range [x T / 8, (x + 1) T / 8); its j-th workgroup walks tiles
+    // base + j, base + j + G / 8, ...
+    const int nblk = gridDim.x;
+    int t, t_end, t_step;
+    if ((nblk & 7) == 0) {
+        const int xcd = blockIdx.x & 7;
+        t = (int)((int64_t)xcd * T / 8) + (blockIdx.x >> 3);
+        t_end = (int)((int64_t)(xcd + 1) * T / 8);
+        t_step = nblk >> 3;
+    } else {
+        t = blockIdx.x;
+        t_end = T;
+        t_step = nblk;
+    }
+    if (t >= t_end) return;  // uniform: the whole workgroup leaves
+
+    const i32x4 a_src = srd(p.a, (uint32_t)H * W * cin_p * 2);
+    const unsigned lds_base = (unsigned)(uintptr_t)lds;
+
+    // a tile's patch sources; tt < 0: no tile (every load reads zeros)
+    auto make_tile = [&](int tt) __attribute__((always_inline)) {
+        WTile r;
+        const int tv = tt < 0 ? 0 : tt;
+        r.y0 = (tv / tiles_x) * TH;
+        r.x0 = (tv % tiles_x) * TW;
+        const int py0 = (MODE == kConv3x3) ? r.y0 - 1 : r.y0 / 2 - 1;
+        const int px0 = (MODE == kConv3x3) ? r.x0 - 1 : r.x0 / 2 - 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = (wave + NW * k) * 64 + lane;
+            const int pix = u >> 2;
+            const int pr = pix / PW, pc = pix - (pix / PW) * PW;
+            const int q = (u & 3) ^ ((pc >> 2) & 3);  // stored quarter -> channel quarter
+            const int sy = py0 + pr, sx = px0 + pc;
+            const bool ok = (tt >= 0) & (k < APW) & (u < G::A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
+            r.aoff[k] = ok ? (uint32_t)(((sy * W + sx) * cin_p + q * 8) * 2) : kOOB;
+        }
+        return r;
+    };
+    // this wave's APW patch loads of stage st of tile tl into buffer buf
+    // (loads past the patch read zeros into the buffer's padding)
+    auto issue = [&](const WTile &tl, int st, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < APW; ++k) {
+            const int ii = wave + NW * k;
+            const uint32_t off = tl.aoff[k] == kOOB ? kOOB : tl.aoff[k] + st * CK * 2;
+            dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, ii < A_INSTR ? off : kOOB);
+        }
+    };
+
+    // the wave's weights: fragment f = (2 s + ks) 9 + tap = output channel
+    // 32 wave + fx, input channels 16 (2 s + ks) + 8 fh .. + 7 of the
+    // [cin_p/16][9][cout_p][16] plane
+    half8 wr[NST * 2 * 9];
+    {
+        const half8 *wp = reinterpret_cast<const half8 *>(p.b) + (32 * wave + fx) * 2 + fh;
+#pragma unroll
+        for (int f = 0; f < NST * 2 * 9; ++f) wr[f] = wp[f * BN * 2];
+    }
+    if (tid < BN) {
+        sbias[tid] = p.bias ? p.bias[tid] : 0.f;
+        sgam[tid] = NORM ? p.ngamma[tid] : 0.f;
+    }
+
+    const float osc = p.oscale;
+
+    // The drain. A staged row is 32 pixels x 32 float4. f32 passes: in
+    // pass k thread tid takes float4 tid + 256 k (pixel 8 k + tid / 32,
+    // channels 4 (tid % 32) .. + 3), so each store writes one contiguous
+    // run. The norm's passes: in pass h thread tid takes pixel
+    // 16 h + tid / 16, channels 8 (tid % 16) .. + 7, a pixel per DPP row.
+    const int dpx = tid >> 5, dc = (tid & 31) * 4;
+    const int npx = tid >> 4, nc = (tid & 15) * 8;
+    int sy0 = 0, sx0 = 0;       // the staged tile
+    bool staged = false;
+    // stream values of the next two drained rows: even rows in xa, odd in xb
+    f32x4 xa[4] = {}, xb[4] = {};
+    // byte offset of (row r of a tile at y0, pixel x0 + px, channel c) in an
+    // output of esz-byte elements with row pitch ld, relative to row y0;
+    // kOOB outside the output or when !live
+    auto doff = [&](bool live, int y0, int x0, int r, int px, int c, int ld, int esz) __attribute__((always_inline)) {
+        const int oy = y0 + r, ox = x0 + px;
+        return (live && oy < Hout && ox < Wout) ? (uint32_t)(((r * Wout + ox) * ld + c) * esz) : kOOB;
+    };
+    // descriptors over the output rows from tile row y0 on (offsets inside a
+    // tile stay below 4 rows; past the last row they fall outside)
+    auto out_srd = [&](const void *base, int y0, int ld, int esz) __attribute__((always_inline)) {
+        const int64_t rem = (int64_t)(Hout - y0) * Wout * ld * esz;
+        return srd(reinterpret_cast<const char *>(base) + (int64_t)y0 * Wout * ld * esz,
+                   (uint32_t)(rem < (int64_t)kOOB ? rem : (int64_t)kOOB));
+    };
+    // stream loads of row r of the tile at (y0, x0) into x (xa or xb: the
+    // callers pick the array by the row's parity with a plain branch, which
+    // keeps both in registers)
+    auto load_row = [&](f32x4 (&x)[4], bool live, int y0, int x0, int r) __attribute__((always_inline)) {
+        if constexpr (ACC) {
+            const i32x4 rs = out_srd(p.c, y0, p.ldc, 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = ld16(rs, doff(live, y0, x0, r, 8 * k + dpx, dc, p.ldc, 4));
+        }
+    };
+    auto drain_load = [&](bool live, int y0, int x0, int r) __attribute__((always_inline)) {
+        if (r & 1) load_row(xb, live, y0, x0, r);
+        else load_row(xa, live, y0, x0, r);
+    };
+    // the outputs of row r of the staged tile (stores only when live); x:
+    // the row's stream values
+    auto store_row = [&](const f32x4 (&x)[4], bool live, int r) __attribute__((always_inline)) {
+        if constexpr (WOUT || YG) {
+            f32x4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[k] = *reinterpret_cast<const f32x4 *>(stg + (r * TW + 8 * k + dpx) * SP + dc);
+                if constexpr (ACC) v[k] += x[k];
+            }
+            if constexpr (WOUT) {
+                const i32x4 rs = out_srd(p.c, sy0, p.ldc, 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) st16(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 4), v[k], true);
+            }
+            if constexpr (YG) {
+                const i32x4 rs = out_srd(p.yg, sy0, p.ldc, 2);
+                const float gs = p.gscale;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    half4v h;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[e] = (_Float16)(v[k][e] * gs);
+                    st8(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 2), h);
+                }
+            }
+        }
+        if constexpr (NORM) {
+            const bool silu = p.norm_silu != 0;
+            const f32x4 ga = *reinterpret_cast<const f32x4 *>(sgam + nc);
+            const f32x4 gb = *reinterpret_cast<const f32x4 *>(sgam + nc + 4);
+            const float rc = sqrtf((float)p.norm_c);
+            const i32x4 rs = out_srd(p.ny, sy0, BN, 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float *sv = stg + (r * TW + 16 * h + npx) * SP + nc;
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(sv);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(sv + 4);
+                float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] +
+                           b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+                ss = row16_sum(ss);
+                const float inv = rc / fmaxf(sqrtf(ss), p.norm_eps);
+                half8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float y = (e < 4 ? a[e] * ga[e] : b[e - 4] * gb[e - 4]) * inv;
+                    // SiLU as y * rcp(1 + exp(-y)) (hardware reciprocal, ~1 ulp)
+                    const float ex = silu ? __expf(-y) : 0.f;
+                    o[e] = (_Float16)(y * __builtin_amdgcn_rcpf(1.0f + ex));
+                }
+                st16(rs, doff(live, sy0, sx0, r, 16 * h + npx, nc, BN, 2), __builtin_bit_cast(f32x4, o), false);
+            }
+        }
+    };
+    auto drain_store = [&](bool live, int r) __attribute__((always_inline)) {
+        if (r & 1) store_row(xb, live, r);
+        else store_row(xa, live, r);
+    };
+    // all but the last WAITN memory operations have landed (and, after the
+    // barrier, every wave's); the stream values are ready from here on
+    auto stage_wait = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(%8)"
+                     : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]), "+v"(xb[2]),
+                       "+v"(xb[3])
+                     : "n"(WAITN)
+                     : "memory");
+        lds_barrier();
+    };
+
+    WTile cur = make_tile(t);
+    WTile nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
+    // the three stages before the first: placeholder stores and stream
+    // loads (outside every output; the loads go straight to the unused
+    // staging area, so no register waits for them) and this tile's first
+    // three patches, so the first stages wait exactly as the later ones
+    const i32x4 none = srd(p.a, 0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        drain_store(false, 0);
+#pragma unroll
+        for (int k = 0; k < NDL; ++k) dma16(none, lds_base + (NBUF * A_PAD + (wave * NDL + k) * 64) * 16, kOOB);
+        issue(cur, j, j);
+    }
+
+    for (;;) {
+        f32x16 acc[TH];
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            stage_wait();
+            drain_store(staged, st);
+            // stream values two rows ahead: the staged tile's rows 2, 3, then
+            // this tile's rows 0, 1
+            if (st + 2 < NST) drain_load(staged, sy0, sx0, st + 2);
+            else drain_load(true, cur.y0, cur.x0, st + 2 - NST);
+            // patches three stages ahead: this tile's last stage, then the
+            // next tile's first three (zeros when there is none)
+            if (st == 0) issue(cur, NST - 1, NST - 1);
+            else issue(nxt, st - 1, st - 1);
+
+            const u32x4 *sA = lds + st * A_PAD;
+            // six fragment groups (K-step ks, tap column dx): each group's
+            // PH patch-row fragments are read before the previous group's
+            // MFMAs run
+            half8 bf[2][PH];
+            auto load_group = [&](int g, half8 *b) __attribute__((always_inline)) {
+                const int ks = g / 3, dx = g % 3;
+                const int pc = G::pcol(fx, dx);
+                const int sq = (2 * ks + fh) ^ ((pc >> 2) & 3);
+                const half8 *sa = reinterpret_cast<const half8 *>(sA) + pc * 4 + sq;
+#pragma unroll
+                for (int pr = 0; pr < PH; ++pr) b[pr] = sa[pr * PW * 4];
+            };
+            load_group(0, bf[0]);
+#pragma unroll
+            for (int g = 0; g < 6; ++g) {
+                if (g + 1 < 6) load_group(g + 1, bf[(g + 1) & 1]);
+                const int ks = g / 3, dx = g % 3;
+                const half8 *b = bf[g & 1];
+#pragma unroll
+                for (int pr = 0; pr < PH; ++pr)
+#pragma unroll
+                    for (int dy = 0; dy < 3; ++dy)
+#pragma unroll
+                        for (int r = 0; r < TH; ++r)
+                            if (G::arow(r, dy) == pr) {
+                                const int f = (2 * st + ks) * 9 + dy * 3 + dx;
+                                // the first and last MFMA of each accumulator's chain
+                                const bool first = st == 0 && ks == 0 && dx == 0 && dy == 0;
+                                const bool lastm = st == NST - 1 && ks == 1 && dx == 2 && dy == 2;
+                                const int kind = first ? 0 : (lastm ? 2 : 1);
+                                if (f < NST * 18 - NWF) mma<true>(acc[r], wr[f], b[pr], kind);
+                                else mma<false>(acc[r], wr[f], b[pr], kind);
+                            }
+            }
+        }
+        // every wave is done with the staged rows before they are replaced
+        lds_barrier();
+        // stage the tile (oscale, bias): lane l holds pixel fx, channels
+        // 32 wave + 8 k + 4 fh .. + 3
+#pragma unroll
+        for (int r = 0; r < TH; ++r)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int ch = 32 * wave + 8 * k + 4 * fh;
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sbias + ch);
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = osc * acc[r][4 * k + e] + b4[e];
+                *reinterpret_cast<f32x4 *>(stg + (r * TW + fx) * SP + ch) = v;
+            }
+        sy0 = cur.y0;
+        sx0 = cur.x0;
+        staged = true;
+        t += t_step;
+        if (t >= t_end) break;
+        cur = nxt;
+        nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
+    }
+    // the last tile's rows (the stream values of rows 0 and 1 are loading)
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]),
+                 "+v"(xb[2]), "+v"(xb[3]) :: "memory");
+    lds_barrier();
+    drain_store(true, 0);
+    drain_store(true, 1);
+    drain_load(true, sy0, sx0, 2);
+    drain_load(true, sy0, sx0, 3);
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]),
+                 "+v"(xb[2]), "+v"(xb[3]) :: "memory");
+    drain_store(true, 2);
+    drain_store(true, 3);
+}
+
+int cu_count()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int MODE, bool NORM, bool ACC, bool WOUT, bool YG>
+void launch_ws_t(const IgemmArgs &a, hipStream_t s)
+{
+    const int Hout = (MODE == kConv3x3Up2) ? 2 * a.H : a.H;
+    const int Wout = (MODE == kConv3x3Up2) ? 2 * a.W : a.W;
+    const int tiles = ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW);
+    int grid = cu_count() & ~7;
+    if (grid <= 0 || grid > tiles) grid = tiles;
+    hipLaunchKernelGGL((k_conv_ws<MODE, NORM, ACC, WOUT, YG>), dim3(grid), dim3(NT), 0, s, a);
+}
+
+template <int MODE>
+void launch_ws_mode(const IgemmArgs &a, hipStream_t s)
+{
+    const bool w = a.write_out != 0;
+    if (a.ngamma) {
+        if (w) launch_ws_t<MODE, true, false, true, false>(a, s);
+        else launch_ws_t<MODE, true, false, false, false>(a, s);
+        return;
+    }
+    const bool acc = a.accumulate != 0, g = a.yg != nullptr;
+    if (acc) {
+        if (w && g) launch_ws_t<MODE, false, true, true, true>(a, s);
+        else if (w) launch_ws_t<MODE, false, true, true, false>(a, s);
+        else if (g) launch_ws_t<MODE, false, true, false, true>(a, s);
+    } else {
+        if (w && g) launch_ws_t<MODE, false, false, true, true>(a, s);
+        else if (w) launch_ws_t<MODE, false, false, true, false>(a, s);
+        else if (g) launch_ws_t<MODE, false, false, false, true>(a, s);
+    }
+}
+
+}  // namespace
+
+bool conv_ws_supported(int mode, const IgemmArgs &a)
+{
+    if (mode != kConv3x3 && mode != kConv3x3Up2) return false;
+    if (a.cin_p != 128 || a.N != 128 || a.ldc != 128) return false;
+    if (a.ngamma && a.accumulate) return false;
+    const int64_t Hout = (mode == kConv3x3Up2) ? 2LL * a.H : a.H;
+    const int64_t Wout = (mode == kConv3x3Up2) ? 2LL * a.W : a.W;
+    (void)Hout;
+    // a tile's output rows addressed with 32-bit offsets. The choice
+    // depends on the channels and the width only, never on the frame's
+    // height: a banded decode must run the same kernel as the whole frame
+    // (the fused norm's sum order differs between the two conv kernels)
+    return (int64_t)TH * Wout * BN * 4 < (int64_t)kOOB;
+}
+
+void launch_conv_ws(int mode, const IgemmArgs &a, hipStream_t s)
+{
+    if (a.M <= 0) return;
+    if (mode == kConv3x3) launch_ws_mode<kConv3x3>(a, s);
+    else launch_ws_mode<kConv3x3Up2>(a, s);
+}
+
+}  // namespace ig

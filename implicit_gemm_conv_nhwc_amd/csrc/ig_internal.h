@@ -63,8 +63,14 @@ struct IgemmArgs {
 // modes go to the patch-reusing convolution kernel.
 void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s);
 // The 3x3 convolutions (kConv3x3, kConv3x3Up2) with per-tile input patches.
-// With a.ngamma set, N must be 64 or 128 and accumulate 0.
+// With a.ngamma set, N must be 64 or 128 and accumulate 0. Shapes that
+// conv_ws_supported accepts go to launch_conv_ws.
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s);
+// The 3x3 convolutions at cin_p = N = ldc = 128 with the weights held in
+// registers; true when the shape fits (it depends on the channels and the
+// output width, not the height, so bands and whole frames agree).
+bool conv_ws_supported(int mode, const IgemmArgs &a);
+void launch_conv_ws(int mode, const IgemmArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------------
 // plain NT GEMM C = oscale * A.B^T with the attention's softmax epilogues

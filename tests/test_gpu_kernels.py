@@ -470,6 +470,55 @@ def test_conv_with_guarded_cast_output(H, W, cin, cout, mode, acc, write_y, g):
     assert np.max(np.abs(got - want)) <= 2e-3 * np.sqrt(np.mean(conv ** 2)) + 1e-7 * np.max(np.abs(want))
 
 
+@pytest.mark.parametrize("H,W,mode,acc,write_y,g", [
+    (258, 300, 1, 0, 1, 8), (258, 300, 1, 1, 1, 8), (259, 301, 1, 1, 0, 8),
+    (130, 150, 2, 0, 1, 8), (131, 149, 2, 1, 0, 4)])
+def test_conv_weights_in_registers_sampled(H, W, mode, acc, write_y, g):
+    """128 -> 128 convs on frames large enough for the kernel that keeps the
+    weights in registers (4-row tiles walked by one workgroup per CU, each
+    tile's result staged in LDS and written out during the next tile's
+    stages), ragged at the bottom and right: every pixel written; the f32
+    result, plain or accumulated into a stream, at the borders, at a pixel
+    of every tile and at seeded picks against the oracle; and the guarded
+    f16 cast emitted by the same epilogue bit for bit the separate cast of
+    the f32 result."""
+    seed = 1100 + H + mode
+    c = 128
+    x16 = synth.normal(19, seed, (H, W, c), 1.0, np.float16)
+    w = synth.normal(19, seed + 1, (c, c, 3, 3), 1.0 / (9 * c), np.float16)
+    b = synth.normal(19, seed + 2, (c,), 0.02)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    M = Ho * Wo
+    assert ((Ho + 3) // 4) * ((Wo + 31) // 32) >= 512
+    osc = 256.0 if mode == 2 else 1.0
+    xd = dev(x16.reshape(H * W, c))
+    pl = packed(w)
+    y0 = synth.normal(19, seed + 3, (M, c), 100.0).astype(np.float32)
+    yref = dev(y0) if acc else nan_f32((M, c))
+    ig.conv_nhwc_ex(xd, H, W, c, mode, pl, c, dev(b), osc, acc, yref)
+    ygref = nan_f16((M, c))
+    ig.guard_cast(yref, M, c, None, g, ygref)
+    y = dev(y0)
+    yg = nan_f16((M, c))
+    ig.conv3x3_guard_out_nhwc(xd, H, W, c, mode, pl, c, dev(b), osc, acc, y, write_y, g, yg)
+    torch.cuda.synchronize()
+    assert torch.equal(yg.view(torch.int16), ygref.view(torch.int16))
+    assert torch.equal(y, yref) if write_y else torch.equal(y, dev(y0))
+    got = host(yref)
+    assert not np.isnan(got).any(), "a tile was not written"
+    corners = np.array([r * Wo + cc for r in range(0, Ho, 4) for cc in range(0, Wo, 32)], np.int64)
+    edges = np.array([(Ho - 1) * Wo + cc for cc in range(Wo)] + [r * Wo + Wo - 1 for r in range(Ho)], np.int64)
+    pix = np.unique(np.concatenate([sample_pixels(Ho, Wo, 512, seed=seed), corners, corners + 3 * Wo + 31, edges]))
+    pix = pix[pix < M]
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    conv = osc * O.conv2d_at(xc, w, pix, up2=(mode == 2)) + b[None, :]
+    want = conv + (y0[pix].astype(np.float64) if acc else 0.0)
+    err = float(np.max(np.abs(got[pix] - want)))
+    rms = float(np.sqrt(np.mean(conv * conv)))
+    print("weights in registers %dx%d mode %d acc %d (%d px): max|d| %.3e rms %.3e" % (H, W, mode, acc, len(pix), err, rms))
+    assert err <= 1e-4 * rms + 1e-7 * float(np.max(np.abs(want)))
+
+
 def test_conv_fused_norm_needs_one_tile_per_pixel():
     with pytest.raises(ig.IgError) as e:
         z = dev(np.zeros((4, 64), np.float16))
