@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     attention_f16,
     attention_workspace_bytes,
     groupnorm_silu_f16,
+    groupnorm_silu_f16_noalloc,
     groupnorm_workspace_bytes,
     guard_cast,
     last_error,

@@ -79,6 +79,8 @@ _gn_ws.argtypes = [_c_int, _c_int, _c_int]
 _gn_ws.restype = ctypes.c_size_t
 _gn = _sig("groupnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _c_float, _vp,
                                   ctypes.c_size_t, _vp, _vp])
+_gn_na = _sig("groupnorm_silu_f16_noalloc", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _c_float,
+                                           _vp, _vp])
 _attn_ws = _sig("ig_attention_workspace_bytes", [_c_int, _c_int], ctypes.c_size_t)
 _attn = _sig("attention_f16", [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, ctypes.c_size_t, _vp, _vp])
 _conv_out = _sig("ig_conv3x3_out_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp])
@@ -201,6 +203,11 @@ def groupnorm_workspace_bytes(M, cp, groups):
 def groupnorm_silu_f16(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, ws, ws_bytes, y, stream=None):
     return _check(_gn(_ptr(x), M, cp, c_real, groups, _ptr(bias), _ptr(gamma), _ptr(beta), silu, eps, _ptr(ws),
                       ws_bytes, _ptr(y), _stream(stream)))
+
+
+def groupnorm_silu_f16_noalloc(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, y, stream=None):
+    return _check(_gn_na(_ptr(x), M, cp, c_real, groups, _ptr(bias), _ptr(gamma), _ptr(beta), silu, eps, _ptr(y),
+                         _stream(stream)))
 
 
 def conv3x3_out_nchw(x, H, W, cin_p, w, cout, cout_p, bias, out, stream=None):

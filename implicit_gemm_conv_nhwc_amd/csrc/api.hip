@@ -129,6 +129,26 @@ static int gemm_any(const uint16_t *a, int M, int K, int lda, const uint16_t *b,
     return check_launch("gemm launch");
 }
 
+// GroupNorm's checks shared by both entry points; IG_OK, or the status
+int groupnorm_check(const float *x, int M, int cp, int c_real, int groups, const float *bias, const float *gamma,
+                    const float *beta, float eps, uint16_t *y)
+{
+    if (M < 0) return fail(IG_EINVAL, "M=%d is negative", M);
+    if (cp <= 0 || c_real <= 0 || c_real > cp || groups <= 0) return fail(IG_EINVAL, "bad channels cp=%d c_real=%d groups=%d", cp, c_real, groups);
+    if (!gn_supported(cp, c_real, groups))
+        return fail(IG_EUNSUPPORTED, "GroupNorm needs cp %% 4 == 0 (<= 1024) and 1..128 groups dividing c_real");
+    if (!(eps > 0.f)) return fail(IG_EINVAL, "eps must be positive");
+    if ((int64_t)M * cp >= (1LL << 40)) return fail(IG_EUNSUPPORTED, "too many elements");
+    if (M == 0) return IG_OK;
+    int r;
+    if ((r = check_ptr(x, "x")) || (r = check_ptr(gamma, "gamma")) || (r = check_ptr(beta, "beta")) ||
+        (r = check_ptr(y, "y", false)))
+        return r;
+    if (bias && (r = check_ptr(bias, "bias"))) return r;
+    return IG_OK;
+}
+
+
 }  // namespace ig
 
 using namespace ig;
@@ -306,23 +326,31 @@ size_t ig_groupnorm_workspace_bytes(int M, int cp, int groups)
     return gn_workspace_bytes(M, cp, groups);
 }
 
+int groupnorm_silu_f16_noalloc(const float *x, int M, int cp, int c_real, int groups, const float *bias,
+                               const float *gamma, const float *beta, int silu, float eps, uint16_t *y, void *stream)
+{
+    clear_error();
+    int r = groupnorm_check(x, M, cp, c_real, groups, bias, gamma, beta, eps, y);
+    if (r || M == 0) return r;
+    const size_t need = gn_workspace_bytes(M, cp, groups);
+    if (need > gn_scratch_bytes())
+        return fail(IG_EUNSUPPORTED, "GroupNorm needs %zu bytes of scratch, the built-in array holds %zu", need,
+                    gn_scratch_bytes());
+    void *ws = gn_scratch_ptr();
+    if (!ws) return fail(IG_EHIP, "the GroupNorm scratch array's device address is not available");
+    (void)hipGetLastError();
+    launch_groupnorm(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, ws, reinterpret_cast<_Float16 *>(y),
+                     reinterpret_cast<hipStream_t>(stream));
+    return check_launch("groupnorm launch");
+}
+
 int groupnorm_silu_f16(const float *x, int M, int cp, int c_real, int groups, const float *bias,
                        const float *gamma, const float *beta, int silu, float eps, void *ws, size_t ws_bytes,
                        uint16_t *y, void *stream)
 {
     clear_error();
-    if (M < 0) return fail(IG_EINVAL, "M=%d is negative", M);
-    if (cp <= 0 || c_real <= 0 || c_real > cp || groups <= 0) return fail(IG_EINVAL, "bad channels cp=%d c_real=%d groups=%d", cp, c_real, groups);
-    if (!gn_supported(cp, c_real, groups))
-        return fail(IG_EUNSUPPORTED, "GroupNorm needs cp %% 4 == 0 (<= 1024) and 1..128 groups dividing c_real");
-    if (!(eps > 0.f)) return fail(IG_EINVAL, "eps must be positive");
-    if ((int64_t)M * cp >= (1LL << 40)) return fail(IG_EUNSUPPORTED, "too many elements");
-    if (M == 0) return IG_OK;
-    int r;
-    if ((r = check_ptr(x, "x")) || (r = check_ptr(gamma, "gamma")) || (r = check_ptr(beta, "beta")) ||
-        (r = check_ptr(y, "y", false)))
-        return r;
-    if (bias && (r = check_ptr(bias, "bias"))) return r;
+    int r = groupnorm_check(x, M, cp, c_real, groups, bias, gamma, beta, eps, y);
+    if (r || M == 0) return r;
     if (!ws || ws_bytes < gn_workspace_bytes(M, cp, groups))
         return fail(IG_EWORKSPACE, "GroupNorm workspace of %zu bytes, %zu needed", ws_bytes,
                     gn_workspace_bytes(M, cp, groups));

@@ -16,6 +16,8 @@
 // a second kernel merges a group's partials in f64 and turns the group
 // statistics into a per-channel offset and scale; the apply kernel reads the
 // stream once more. HBM: two reads of the f32 stream and one f16 write.
+#include <mutex>
+
 #include "ig_internal.h"
 
 namespace ig {
@@ -273,6 +275,33 @@ int64_t gn_chunks(int M, int cp)
 size_t gn_workspace_bytes(int M, int cp, int groups)
 {
     return ((size_t)gn_chunks(M, cp) * groups * 3 + (size_t)cp * 3) * sizeof(float) + 256;
+}
+
+// The allocation-free entry point's workspace: a file-scope device array
+// sized for every supported call (at most MAXCHUNK partials per group, MAXG
+// groups, 4 MAXT channels), one copy per GPU for the life of the process.
+// Host code never passes its name to a kernel (on the host it only stands
+// for the symbol): the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+constexpr size_t kGnScratchBytes = ((size_t)MAXCHUNK * MAXG * 3 + (size_t)MAXT * 4 * 3) * sizeof(float) + 256;
+static __device__ __align__(256) char gn_scratch[kGnScratchBytes];
+
+size_t gn_scratch_bytes() { return kGnScratchBytes; }
+
+void *gn_scratch_ptr()
+{
+    constexpr int kMaxDev = 64;
+    static void *ptr[kMaxDev] = {};
+    static std::mutex mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(gn_scratch)) != hipSuccess || !p) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
 }
 
 bool gn_supported(int cp, int c_real, int groups)

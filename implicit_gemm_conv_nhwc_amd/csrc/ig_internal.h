@@ -134,6 +134,10 @@ void launch_rmsnorm(const float *x, int M, int cp, int c_real, const float *bias
 // GroupNorm: workspace for the per-chunk statistics, support check, launch
 size_t gn_workspace_bytes(int M, int cp, int groups);
 bool gn_supported(int cp, int c_real, int groups);
+// The device address of the GroupNorm scratch array on the current device
+// (looked up once per device; null on failure) and its size in bytes.
+void *gn_scratch_ptr();
+size_t gn_scratch_bytes();
 void launch_groupnorm(const float *x, int M, int cp, int c_real, int groups, const float *bias,
                       const float *gamma, const float *beta, int silu, float eps, void *ws, _Float16 *y,
                       hipStream_t s);

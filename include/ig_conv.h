@@ -199,6 +199,22 @@ int groupnorm_silu_f16(const float *x, int M, int cp, int c_real, int groups, co
                        const float *gamma, const float *beta, int silu, float eps, void *ws, size_t ws_bytes,
                        uint16_t *y, void *stream);
 
+/* groupnorm_silu_f16 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Its per-chunk statistics live in
+ * a device array built into the library (about 1.5 MiB, one copy per GPU,
+ * held until the process ends; every shape groupnorm_silu_f16 supports
+ * fits, larger needs give IG_EUNSUPPORTED). Nothing is allocated: no
+ * hipMalloc, no library allocator. The kernels write every scratch byte
+ * they read, so no call depends on what an earlier one left there, but all
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Arguments, outputs and errors otherwise as groupnorm_silu_f16 (IG_EHIP
+ * if the array's device address cannot be obtained). */
+int groupnorm_silu_f16_noalloc(const float *x, int M, int cp, int c_real, int groups, const float *bias,
+                               const float *gamma, const float *beta, int silu, float eps, uint16_t *y,
+                               void *stream);
+
 /* ---------------------------------------------------------------------
  * The range-guarded f16 cast of the raw residual stream ([QI] `guard`,
  * CAST_SRC, `Rec::cast`): y = f16((x + bias) * 2^-guard_log2); the
