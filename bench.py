@@ -174,7 +174,7 @@ def bench_conv_roofline(reps, H=512, W=512, C=128):
     M = H * W
     dev = torch.device("cuda")
     w16 = torch.from_numpy(d["w"]).to(dev)
-    plane = torch.empty((C, 9, C), dtype=torch.float16, device=dev)
+    plane = torch.empty(ig.plane_shape(C, C, 3), dtype=torch.float16, device=dev)
     ig.pack_conv_weights(w16, C, C, 3, C, C, plane)
     bias = torch.from_numpy(d["b"]).to(dev)
     gamma = torch.from_numpy(d["gamma"]).to(dev)

@@ -40,6 +40,7 @@ from ._lib import (  # noqa: F401
     lib,
     nhwc_to_nchw,
     pack_conv_weights,
+    plane_shape,
     rmsnorm_silu_f16,
     rmsnorm_silu_guard_cast_f16,
     softmax_rows_f16,

@@ -124,8 +124,14 @@ def version():
 # ---------------------------------------------------------------------------
 
 
+def plane_shape(cout_p, cin_p, k):
+    """Shape of a packed weight plane (include/ig_conv.h, weight packing):
+    3x3 -> [cin_p/16][9][cout_p][16], 1x1 -> [cout_p][cin_p]."""
+    return (cin_p // 16, 9, cout_p, 16) if k == 3 else (cout_p, cin_p)
+
+
 def pack_conv_weights(w, cout, cin, k, cout_p, cin_p, plane, stream=None):
-    """OIHW f16 w -> plane [cout_p][k*k][cin_p] (zero padded)."""
+    """OIHW f16 w -> the zero-padded plane of plane_shape(cout_p, cin_p, k)."""
     return _check(_pack(_ptr(w), cout, cin, k, cout_p, cin_p, _ptr(plane), _stream(stream)))
 
 

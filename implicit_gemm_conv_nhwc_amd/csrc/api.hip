@@ -430,7 +430,8 @@ int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int 
     if (m <= 0 || m >= (1 << 22)) return fail(IG_EINVAL, "attention m=%d outside 1..2^22-1", m);
     if (C != 512) return fail(IG_EUNSUPPORTED, "attention width %d: the single-pass kernel takes 512", C);
     if (!flash_supported(m, ld, C))
-        return fail(IG_EINVAL, "ld=%d must be >= m rounded up to 32 (%d) and a multiple of 8", ld, (m + 31) / 32 * 32);
+        return fail(IG_EINVAL, "ld=%d must be >= m rounded up to 32 (%d), a multiple of 8, and ld*C*2 below %lld bytes",
+                    ld, (m + 31) / 32 * 32, (long long)kConvInMaxBytes);
     int r;
     if ((r = check_ptr(q, "q", true)) || (r = check_ptr(k, "k", true)) || (r = check_ptr(vt, "vt", true)) ||
         (r = check_ptr(out, "out", true)))
@@ -518,10 +519,11 @@ int ig_dupup_add(const float *src, int H, int W, int cin_p, float *x, int cout, 
         return fail(IG_EINVAL, "bad DupUp arguments");
     const int64_t jmax = ((int64_t)(cout - 1) * factor + (int64_t)(ft - 1) * 4 + 3) / repeats;
     if (jmax >= cin_p) return fail(IG_EINVAL, "shuffled channel %lld outside cin_p=%d", (long long)jmax, cin_p);
+    if (cout_p % 4) return fail(IG_EUNSUPPORTED, "cout_p=%d must be a multiple of 4", cout_p);
     if ((int64_t)4 * H * W * cout_p >= (1LL << 40)) return fail(IG_EUNSUPPORTED, "too many elements");
     if (H == 0 || W == 0) return IG_OK;
     int r;
-    if ((r = check_ptr(src, "src", false)) || (r = check_ptr(x, "x", false))) return r;
+    if ((r = check_ptr(src, "src", false)) || (r = check_ptr(x, "x"))) return r;
     (void)hipGetLastError();
     launch_dupup(src, H, W, cin_p, x, cout, cout_p, factor, repeats, ft, reinterpret_cast<hipStream_t>(stream));
     return check_launch("dupup launch");

@@ -172,13 +172,14 @@ void k_flash(FlashArgs p)
     // index and the block move the scalar offset.
     u32x4 *const ldv = lds + 2 * KBUF;
     const int kvoff = 16 * lane;
-    const int vvoff = (16 * wave + (lane >> 2)) * p.ld * 2 + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+    const int vvoff = (int)((uint32_t)(16 * wave + (lane >> 2)) * (uint32_t)p.ld * 2u +
+                            16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)));
     auto issue_k = [&](int blk, int kbuf, int i) __attribute__((always_inline)) {
         const int kr = wave + 4 * i;
         dma16(k_src, lds + kbuf * KBUF + kr * KROW, kvoff, (blk * BK + kr) * C * 2);
     };
     auto issue_v = [&](int blk, int vbuf, int i) __attribute__((always_inline)) {
-        dma16(v_src, ldv + vbuf * VU + (wave + 4 * i) * 64, vvoff, i * 64 * p.ld * 2 + blk * BK * 2);
+        dma16(v_src, ldv + vbuf * VU + (wave + 4 * i) * 64, vvoff, (int)((uint32_t)i * 64u * (uint32_t)p.ld * 2u + (uint32_t)blk * BK * 2u));
     };
 
     // fragment reads (units): K step s of MFMA row r reads key row
@@ -419,7 +420,13 @@ void flash_split(int m, int &nsplit, int &bps)
 
 }  // namespace
 
-bool flash_supported(int m, int ld, int c) { return c == C && m > 0 && ld >= ((m + BK - 1) / BK) * BK && ld % 8 == 0; }
+// q, k and V^T are addressed with 32-bit byte offsets: each stays below
+// kConvInMaxBytes (ld < 2,096,960 rows at C = 512)
+bool flash_supported(int m, int ld, int c)
+{
+    return c == C && m > 0 && ld >= ((m + BK - 1) / BK) * BK && ld % 8 == 0 &&
+           (int64_t)ld * C * 2 < kConvInMaxBytes;
+}
 
 size_t flash_workspace_bytes(int m)
 {

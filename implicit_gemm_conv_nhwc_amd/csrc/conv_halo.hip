@@ -97,11 +97,12 @@ constexpr int stage_units()
 {
     return (Geo<MODE>::PH * Geo<MODE>::PW * 2 + 63) / 64 * 64 + 9 * BN * 2;
 }
-// Staging pitch: the fused norm reads a pixel's channels 32 per lane; at
-// 128 channels (4 lanes per pixel) 8 floats of padding per pixel spread those
-// reads over the LDS banks. The plain epilogue reads the rows linearly and
-// needs none; the 64-channel norm keeps the plain pitch (padding it costs
-// that instantiation register spills).
+// Staging pitch: the 128-channel fused norm (8 lanes per pixel, 16
+// channels each) keeps 8 floats of padding per staged pixel, chosen when its
+// lanes read 32 channels each (4 lanes per pixel, 8 lanes then met on one
+// bank group without it). The plain epilogue reads the rows linearly and
+// needs none; the 64-channel norm (2 lanes per pixel, 32 channels each)
+// keeps the plain pitch (padding it costs that instantiation spills).
 template <int BN, bool NORM>
 constexpr int stage_pitch()
 {
@@ -418,19 +419,13 @@ void k_conv_halo(IgemmArgs p)
             constexpr int NV = CPL / 4;  // float4 per lane
             static_assert(CPL == 32 || CPL == 16, "16 or 32 channels per lane");
             const int pi = tid / TPP, q4 = tid % TPP, cb = q4 * CPL;
-            // lanes 2 and 3 of a pixel take their 32 channels starting at the
-            // fifth float4: with the padded pitch, a read then touches at most
-            // two lanes per bank group (8 when every lane starts at its first);
-            // with 2 lanes per pixel rot is 0; with 16 channels per lane
-            // there is no rotation
-            const int rot = (CPL == 32) ? (q4 >> 1) * 4 : 0;
             const int wr = pi / TW, px = pi % TW;
             const float4 *sv = reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + cb);
-            float4 v[NV];  // v[k] holds channels cb + 4 ((k + rot) % NV) .. + 3
+            float4 v[NV];  // v[k] holds channels cb + 4 k .. + 3
             float ss = 0.f;
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
-                v[k] = sv[(k + rot) & (NV - 1)];
+                v[k] = sv[k];
                 ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
             }
 #pragma unroll
@@ -447,7 +442,7 @@ void k_conv_halo(IgemmArgs p)
                 const bool silu = p.norm_silu != 0;
 #pragma unroll
                 for (int k = 0; k < NV; k += 2) {
-                    const int u = (k + rot) & (NV - 1);  // even: 8 channels, 16-byte aligned
+                    const int u = k;  // even: 8 channels, 16-byte aligned
                     float o[8] = {v[k].x, v[k].y, v[k].z, v[k].w, v[k + 1].x, v[k + 1].y, v[k + 1].z, v[k + 1].w};
                     const float4 ga = g4[u], gb = g4[u + 1];
                     const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};

@@ -10,9 +10,9 @@
 //    2048^2 decode is 2.1 GB, far inside 288 GB of HBM); decoder_forward_bands
 //    runs the up blocks from a chosen one on in horizontal bands with exact
 //    halos, as the pages do to bound memory (page "cortiq-engine 0.8.3,
-//    src/gpu_wgpu/qi21_vae.rs", the bands section, `grow`, `half`,
-//    `plan_band`, `run_blocks`, `output_rows`): its output is bit for bit the
-//    whole-frame decode's;
+//    src/gpu_wgpu/qi21_vae.rs", the bands section, `run_blocks`,
+//    `output_rows`); each kept pixel goes through the same kernels with the
+//    same inputs as in the whole frame, so the two outputs are identical;
 //  * the combine passes are folded into conv epilogues: the up conv and
 //    conv_in write x = oscale*acc + b directly, the second conv of a
 //    resnet adds into the stream (x += acc + b2), and a shortcut writes
@@ -35,40 +35,58 @@ constexpr size_t kAlign = 256;
 inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 constexpr float kEps = 1e-12f;
 
-// Rows [lo, hi) of one resolution level of the frame.
-struct Rows {
-    int lo = 0, hi = 0;
-    int n() const { return hi - lo; }
+// A contiguous range of image rows [first, end) at one resolution of the
+// up path.
+struct Span {
+    int first = 0, end = 0;
+    int rows() const { return end - first; }
 };
 
-// a 3x3 conv needs k more rows on each side of the rows it must produce,
-// clamped to the frame's h rows (the frame edge is the real zero padding)
-Rows grow(Rows r, int k, int h) { return {r.lo - k > 0 ? r.lo - k : 0, r.hi + k < h ? r.hi + k : h}; }
-// a nearest-2x upsample reads half the rows, rounded outward
-Rows half(Rows r) { return {r.lo / 2, (r.hi + 1) / 2}; }
+// One operation of the up path, seen from the rows it produces: a 3x3 conv
+// on a level of `height` rows, or the nearest-2x upsample that a block
+// `block` ends with (its output level has twice the rows of its input).
+struct PathStep {
+    bool upsample;
+    int height;
+    int block;
+};
 
-// Walk back from the kept output rows through conv_out and up blocks
-// s..n_up-1 (each: n_res resnets of two 3x3 convs, then, with has_up, the
-// upsample and its 3x3 conv): the rows of block s's input the band starts
-// from, and the rows of its input each up block feeds to its upsample.
-void plan_band(int n_up, const int *n_res, const int *has_up, int h0, int s, Rows keep, Rows &input, Rows *feed)
+// The rows one step reads to produce the rows `out`: a 3x3 conv one more on
+// each side, cut at the level's edges (there the zero padding is the frame's
+// own); an upsample the source rows of out's rows, row r coming from r / 2.
+Span read_rows(const PathStep &p, Span out)
 {
-    int lvl[IG_MAX_UP + 1], l = 0;
-    for (int i = 0; i < n_up; ++i) {
-        lvl[i] = l;
-        l += has_up[i] ? 1 : 0;
-    }
-    Rows e = grow(keep, 1, h0 << l);  // conv_out
-    for (int i = n_up - 1; i >= s; --i) {
-        feed[i] = Rows{};
+    if (p.upsample) return Span{out.first / 2, (out.end + 1) / 2};
+    return Span{out.first > 0 ? out.first - 1 : 0, out.end < p.height ? out.end + 1 : p.height};
+}
+
+// Band planning by receptive fields: list the steps from block s's input to
+// the frame (each block: 2 n_res 3x3 convs, then, with has_up, the upsample
+// and its 3x3 conv; conv_out last), then fold the kept output rows back
+// through them. input: the rows of block s's input the band needs; feed[i]:
+// the rows block i (i >= s, with has_up) hands to its upsample.
+void plan_band(int n_up, const int *n_res, const int *has_up, int h0, int s, Span keep, Span &input, Span *feed)
+{
+    PathStep steps[IG_MAX_UP * (2 * IG_MAX_RES + 2) + 1];
+    int n = 0, height = h0;
+    for (int i = 0; i < s; ++i)
+        if (has_up[i]) height *= 2;
+    for (int i = s; i < n_up; ++i) {
+        for (int k = 0; k < 2 * n_res[i]; ++k) steps[n++] = PathStep{false, height, i};
         if (has_up[i]) {
-            const Rows a = half(grow(e, 1, h0 << (lvl[i] + 1)));
-            feed[i] = a;
-            e = a;
+            steps[n++] = PathStep{true, 0, i};
+            height *= 2;
+            steps[n++] = PathStep{false, height, i};
         }
-        e = grow(e, 2 * n_res[i], h0 << lvl[i]);
     }
-    input = e;
+    steps[n++] = PathStep{false, height, -1};  // conv_out
+    for (int i = 0; i < n_up; ++i) feed[i] = Span{};
+    Span span = keep;
+    for (int j = n - 1; j >= 0; --j) {
+        span = read_rows(steps[j], span);
+        if (steps[j].upsample) feed[steps[j].block] = span;
+    }
+    input = span;
 }
 
 struct Plan {
@@ -206,7 +224,7 @@ int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
 // Sizes of up blocks s0..s1-1 run on `rows` rows (of W columns) of block
 // s0's input level; feed[i]: the rows block i feeds to its upsample (NULL:
 // all). fin: the output stage follows. xmax: the stream's maximum.
-void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Rows *feed, bool fin, int cp,
+void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Span *feed, bool fin, int cp,
                  int64_t &xmax, Plan &pl)
 {
     for (int s = s0; s < s1; ++s) {
@@ -218,7 +236,7 @@ void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Row
             cp = u.res[r].c2.cout_p;
         }
         if (u.has_up) {
-            const int fr = feed ? feed[s].n() : rows;
+            const int fr = feed ? feed[s].rows() : rows;
             upd(pl.max_xn, (int64_t)fr * W * cp);
             // the last resnet's conv2 casts all its rows; else only the fed ones
             upd(pl.max_xg, (int64_t)(u.n_res > 0 ? rows : fr) * W * cp);
@@ -250,7 +268,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     if (e) return e;
     pl.s = (band_rows > 0 && band_from >= 0 && band_from < d->n_up) ? band_from : d->n_up;
     pl.band_rows = pl.s < d->n_up ? band_rows : 0;
-    // the head (conv_in, mid block, attention) at the latent resolution
+    // conv_in, the mid block and its attention run on the latent grid
     int64_t M = (int64_t)h0 * w0;
     const int c = d->mid[0].c2.cout;
     upd(pl.max_xn, M * d->conv_in.cin_p);
@@ -275,10 +293,10 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
         int n_res[IG_MAX_UP], has_up[IG_MAX_UP];
         band_structure(*d, n_res, has_up);
         for (int k0 = 0; k0 < pl.H; k0 += pl.band_rows) {
-            const Rows keep{k0, k0 + pl.band_rows < pl.H ? k0 + pl.band_rows : pl.H};
-            Rows input, feed[IG_MAX_UP];
+            const Span keep{k0, k0 + pl.band_rows < pl.H ? k0 + pl.band_rows : pl.H};
+            Span input, feed[IG_MAX_UP];
             plan_band(d->n_up, n_res, has_up, h0, pl.s, keep, input, feed);
-            size_blocks(*d, pl.s, d->n_up, input.n(), w0 << lv, feed, true, wd.cp_in[pl.s], pl.max_xb, pl);
+            size_blocks(*d, pl.s, d->n_up, input.rows(), w0 << lv, feed, true, wd.cp_in[pl.s], pl.max_xb, pl);
         }
     }
     // every 3x3 conv reads its f16 input from xn or xg
@@ -405,11 +423,11 @@ struct Run {
     }
 
     // Up blocks s0..s1-1 on the stream x holding rows cur (buffer row 0 =
-    // cur.lo) of W columns and padded width cp ([QI] `run_blocks`); feed[i]:
+    // cur.first) of W columns and padded width cp ([QI] `run_blocks`); feed[i]:
     // the rows block i feeds to its upsample (NULL: all). Returns through
     // cur, W, cp the rows the stream then holds; normed: the last up conv
     // emitted norm_out's f16 input of conv_out into xn.
-    void blocks(const ig_decoder &d, int s0, int s1, const Rows *feed, Rows &cur, int &W, int &cp, bool &normed)
+    void blocks(const ig_decoder &d, int s0, int s1, const Span *feed, Span &cur, int &W, int &cp, bool &normed)
     {
         const float gs = ldexpf(1.f, g);
         normed = false;
@@ -419,26 +437,26 @@ struct Run {
                 // a stage's last resnet before its up conv emits the
                 // guarded cast itself
                 const bool last = u.has_up && k == u.n_res - 1;
-                resnet(u.res[k], cur.n(), W, cp, last ? xg : nullptr);
+                resnet(u.res[k], cur.rows(), W, cp, last ? xg : nullptr);
                 cp = u.res[k].c2.cout_p;
             }
             if (u.has_up) {
-                const Rows f = feed ? feed[st] : cur;
-                const int64_t skip = (int64_t)(f.lo - cur.lo) * W;
+                const Span f = feed ? feed[st] : cur;
+                const int64_t skip = (int64_t)(f.first - cur.first) * W;
                 const _Float16 *up_in = xg + skip * cp;
                 if (u.n_res == 0) {
-                    launch_guard_cast(x + skip * cp, f.n() * W, cp, nullptr, g, xg, s);
+                    launch_guard_cast(x + skip * cp, f.rows() * W, cp, nullptr, g, xg, s);
                     up_in = xg;
                 }
                 if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout) {
                     // the last up conv's epilogue applies norm_out + SiLU; the
                     // f32 stream is not needed after it
-                    conv_norm(kConv3x3Up2, up_in, f.n(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
+                    conv_norm(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
                     normed = true;
                 } else {
-                    conv(kConv3x3Up2, up_in, f.n(), W, u.up, u.up.b, gs, 0, x);
+                    conv(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, 0, x);
                 }
-                cur = Rows{2 * f.lo, 2 * f.hi};
+                cur = Span{2 * f.first, 2 * f.end};
                 W *= 2;
                 cp = u.up.cout_p;
             }
@@ -448,22 +466,22 @@ struct Run {
     // norm_out + SiLU (unless fused), conv_out on the rows cur of the output
     // level (W columns), the rows keep of them into the NCHW frame of Hf
     // rows ([QI] `output_rows`)
-    void output(const ig_decoder &d, Rows cur, int W, int cp, bool normed, Rows keep, int Hf, float *out)
+    void output(const ig_decoder &d, Span cur, int W, int cp, bool normed, Span keep, int Hf, float *out)
     {
-        const int H = cur.n();
+        const int H = cur.rows();
         if (!normed) launch_rmsnorm(x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, xn, s);
-        float *o = out + (int64_t)cur.lo * W;
+        float *o = out + (int64_t)cur.first * W;
         const int64_t plane = (int64_t)Hf * W;
         if (d.conv_out.cout <= 16) {
             // few output channels: straight into the NCHW frame
             launch_conv_out(xn, H, W, d.conv_out.cin_p, reinterpret_cast<const _Float16 *>(d.conv_out.w),
-                            d.conv_out.cout, d.conv_out.cout_p, d.conv_out.b, o, s, keep.lo - cur.lo,
-                            keep.hi - cur.lo, plane);
+                            d.conv_out.cout, d.conv_out.cout_p, d.conv_out.b, o, s, keep.first - cur.first,
+                            keep.end - cur.first, plane);
         } else {
             conv(kConv3x3, xn, H, W, d.conv_out, d.conv_out.b, 1.f, 0, h);
-            const int64_t r0 = (int64_t)(keep.lo - cur.lo) * W;
-            launch_nhwc_to_nchw(h + r0 * d.conv_out.cout_p, keep.n() * W, d.conv_out.cout_p, d.conv_out.cout,
-                                nullptr, out + (int64_t)keep.lo * W, s, plane);
+            const int64_t r0 = (int64_t)(keep.first - cur.first) * W;
+            launch_nhwc_to_nchw(h + r0 * d.conv_out.cout_p, keep.rows() * W, d.conv_out.cout_p, d.conv_out.cout,
+                                nullptr, out + (int64_t)keep.first * W, s, plane);
         }
     }
 
@@ -610,12 +628,12 @@ int run_decoder(const ig_decoder *dec, const float *latent, int h0, int w0, int 
     r.attention(d.attn);
     r.resnet(d.mid[1], h0, w0, d.mid[0].c2.cout_p);
     // up blocks 0..s-1 on the whole frame
-    Rows cur{0, h0};
+    Span cur{0, h0};
     int W = w0, cp = d.mid[1].c2.cout_p;
     bool normed = false;
     r.blocks(d, 0, pl.s, nullptr, cur, W, cp, normed);
     if (pl.s == d.n_up) {
-        r.output(d, cur, W, cp, normed, Rows{0, pl.H}, pl.H, out);
+        r.output(d, cur, W, cp, normed, Span{0, pl.H}, pl.H, out);
         return check_launch("decoder_forward");
     }
     // the bands: blocks s.. from the saved whole-frame stream, each band's
@@ -625,14 +643,14 @@ int run_decoder(const ig_decoder *dec, const float *latent, int h0, int w0, int 
     Run rb = r;
     rb.x = reinterpret_cast<float *>(w + pl.off_xb);
     for (int k0 = 0; k0 < pl.H; k0 += pl.band_rows) {
-        const Rows keep{k0, k0 + pl.band_rows < pl.H ? k0 + pl.band_rows : pl.H};
-        Rows input, feed[IG_MAX_UP];
+        const Span keep{k0, k0 + pl.band_rows < pl.H ? k0 + pl.band_rows : pl.H};
+        Span input, feed[IG_MAX_UP];
         plan_band(d.n_up, n_res, has_up, h0, pl.s, keep, input, feed);
         const size_t row_bytes = (size_t)W * cp * sizeof(float);
-        if (hipMemcpyAsync(rb.x, r.x + (int64_t)input.lo * W * cp, row_bytes * input.n(), hipMemcpyDeviceToDevice,
+        if (hipMemcpyAsync(rb.x, r.x + (int64_t)input.first * W * cp, row_bytes * input.rows(), hipMemcpyDeviceToDevice,
                            s) != hipSuccess)
             return fail(IG_EHIP, "band copy failed");
-        Rows bcur = input;
+        Span bcur = input;
         int bW = W, bcp = cp;
         bool bnormed = false;
         rb.blocks(d, pl.s, d.n_up, feed, bcur, bW, bcp, bnormed);
@@ -691,13 +709,13 @@ int ig_band_plan(int n_up, const int *n_res, const int *has_up, int h0, int band
     if (ups >= 24 || ((int64_t)h0 << ups) >= (1LL << 30)) return fail(IG_EINVAL, "frame too tall");
     const int hf = h0 << ups;
     if (keep_lo < 0 || keep_hi > hf || keep_lo >= keep_hi) return fail(IG_EINVAL, "keep rows [%d, %d) outside [0, %d)", keep_lo, keep_hi, hf);
-    Rows in, fd[IG_MAX_UP];
-    plan_band(n_up, n_res, has_up, h0, band_from, Rows{keep_lo, keep_hi}, in, fd);
-    input[0] = in.lo;
-    input[1] = in.hi;
+    Span in, fd[IG_MAX_UP];
+    plan_band(n_up, n_res, has_up, h0, band_from, Span{keep_lo, keep_hi}, in, fd);
+    input[0] = in.first;
+    input[1] = in.end;
     for (int i = 0; i < n_up; ++i) {
-        feed[2 * i] = i >= band_from ? fd[i].lo : 0;
-        feed[2 * i + 1] = i >= band_from ? fd[i].hi : 0;
+        feed[2 * i] = i >= band_from ? fd[i].first : 0;
+        feed[2 * i + 1] = i >= band_from ? fd[i].end : 0;
     }
     return IG_OK;
 }

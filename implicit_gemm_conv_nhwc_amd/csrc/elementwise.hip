@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256) void k_guard_cast(const float *__restrict__ x,
 }
 
 // ---------------------------------------------------------------------
-// combine: mode 0 x += h + hb; mode 1 x = s + sb + h + hb; mode 2 x = h + hb
+// combine: t = h + hb is added into x (mode 0), replaces x together with
+// the shortcut s + sb (mode 1), or replaces x alone (mode 2)
 // ---------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(float *__restrict__ x, const float *__restrict__ h,
                                                  const float *__restrict__ hb,
@@ -346,20 +347,44 @@ __global__ __launch_bounds__(256) void k_pack(const _Float16 *__restrict__ w, in
     }
 }
 
-// DupUp: x[2y+sy][2x+sx][o] += src[y][x][(o*factor + (ft-1)*4 + 2sy + sx) / repeats]
+// DupUp shortcut: the output pixel in corner q = 2 sy + sx of the 2x2 block
+// over half-resolution pixel p gets, in output channel o, the value of p's
+// channel (factor o + 4 (ft - 1) + q) / repeats (a channel-to-space shuffle
+// of repeated channels). A thread owns one half-resolution pixel and four
+// consecutive output channels, and updates the four corners of its block
+// with one 16-byte read-add-write each; its source channels lie in the
+// pixel's row of src, which the four corners share.
 __global__ __launch_bounds__(256) void k_dupup(const float *__restrict__ src, int W, int cin_p,
                                                float *__restrict__ x, int cout, int cout_p,
                                                int factor, int repeats, int ft, int64_t n)
 {
-    const int W2 = 2 * W;
+    const int q4 = cout_p / 4;  // channel quads per output pixel
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int o = (int)(i % cout);
-        const int64_t pix = i / cout;
-        const int64_t yy = pix / W2;
-        const int xx = (int)(pix - yy * W2);
-        const int j = (o * factor + (ft - 1) * 4 + 2 * (int)(yy & 1) + (xx & 1)) / repeats;
-        const int64_t s = ((yy >> 1) * W + (xx >> 1)) * cin_p + j;
-        x[pix * cout_p + o] += src[s];
+        const int64_t p = i / q4;
+        const int o0 = (int)(i - p * q4) * 4;
+        if (o0 >= cout) continue;
+        const int64_t y = p / W;
+        const int xc = (int)(p - y * W);
+        const float *row = src + p * cin_p;
+        const int shift = 4 * (ft - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 add;
+            float *a = &add.x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int o = o0 + e;
+                a[e] = o < cout ? row[(factor * o + shift + q) / repeats] : 0.f;
+            }
+            const int64_t out_pix = (2 * y + (q >> 1)) * (2 * (int64_t)W) + 2 * xc + (q & 1);
+            float4 *dst = reinterpret_cast<float4 *>(x + out_pix * cout_p + o0);
+            float4 v = *dst;
+            v.x += add.x;
+            v.y += add.y;
+            v.z += add.z;
+            v.w += add.w;
+            *dst = v;
+        }
     }
 }
 
@@ -469,8 +494,8 @@ void launch_zero_rows_f16(_Float16 *y, int r0, int r1, int ld, hipStream_t s)
 void launch_dupup(const float *src, int H, int W, int cin_p, float *x, int cout, int cout_p,
                   int factor, int repeats, int ft, hipStream_t s)
 {
-    const int64_t n = (int64_t)4 * H * W * cout;
-    if (n <= 0) return;
+    const int64_t n = (int64_t)H * W * (cout_p / 4);
+    if (n <= 0 || cout <= 0) return;
     hipLaunchKernelGGL(k_dupup, dim3(blocks_for(n, 256, 1 << 20)), dim3(256), 0, s, src, W, cin_p, x,
                        cout, cout_p, factor, repeats, ft, n);
 }

@@ -1,31 +1,22 @@
-// MFMA implicit GEMM for gfx950: the decoder's 3x3 convolutions (plain and
-// with the nearest-2x upsample folded into the gather), its 1x1 convs and
-// the attention's products, all as C[M][N] = oscale * A.B^T (+ bias).
+// The plain NT GEMM fallback for gfx950 and the dispatch of the decoder's
+// products: C[M][N] = oscale * A.B^T (+ bias), the 1x1 convs and the
+// attention's products (page "cortiq-engine 0.8.3,
+// src/gpu_wgpu/qi21_vae.rs": module doc, 1x1 convs as plain GEMMs, f16
+// inputs, f32 accumulation; `mmc`, B is the weight "plane" [N][K], A the
+// activations). Shapes the direct-to-LDS GEMM (gemm2.hip) takes go there;
+// the 3x3 convolutions go to their own kernels (conv_ws.hip, conv_halo.hip).
 //
-// Page "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs": module doc (every
-// 3x3 conv an implicit GEMM with the nearest-2x upsample folded into the
-// A-tile gather, 1x1 convs as plain GEMMs, f16 inputs, f32 accumulation),
-// `mmc` (B is the weight "plane" [N][K], A the activations) and `qconv`
-// (the plane's K order is (tap, channel)).
-//
-// Design for CDNA4 (not the pages' 128x64 cooperative-matrix tiling):
+// This kernel takes the rest (K a multiple of 32, any M):
 //  * one workgroup = 4 wave64s in a 2x2 grid, tile BM x BN (256|128 x
 //    128|64); each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles,
 //    v_mfma_f32_32x32x16_f16 with the f32 accumulators kept in registers;
-//  * K advances 32 channels per step. For a conv a step is (channel chunk,
-//    tap), taps innermost, so the nine shifted gathers of one 64-byte
-//    channel chunk follow each other and hit the same cache lines;
-//  * the gather is implicit: each thread owns fixed output pixels and
-//    computes the source pixel of every tap on the fly (zero outside the
-//    image; for up2 in upsampled coordinates, then halved), so no im2col
-//    matrix ever exists;
-//  * global -> registers -> LDS, double-buffered, the next step's loads in
-//    flight during the current step's MFMAs; one barrier per step. LDS rows
-//    are 64 B of data + 16 B of padding so the 16-byte fragment reads of
-//    consecutive rows fall in different banks;
+//  * K advances 32 per step, global -> registers -> LDS, double-buffered,
+//    the next step's loads in flight during the current step's MFMAs; one
+//    barrier per step. LDS rows are 64 B of data + 16 B of padding so the
+//    16-byte fragment reads of consecutive rows fall in different banks;
+//  * rows past M read zero through the buffer resource's bound;
 //  * the tile order is XCD-aware: workgroups are dealt round robin to the 8
-//    XCDs, so block b is remapped to run tile (b % 8) * (grid / 8) + b / 8,
-//    keeping neighbouring image rows (the 3x3 halos) in one XCD's L2;
+//    XCDs, so block b is remapped to run tile (b % 8) * (grid / 8) + b / 8;
 //  * the epilogue applies oscale, the bias and optionally the residual add
 //    (y += ...) and writes f32 or f16 with rows >= M masked.
 #include "ig_internal.h"
@@ -50,41 +41,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-constexpr int kOOB = 0x7fffffff;  // an offset past every resource
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int MODE, int A_PER, int B_PER>
-__device__ __forceinline__ void load_step(const IgemmArgs &p, __amdgpu_buffer_rsrc_t ra_src,
-                                          int4v g_oy, int4v g_ox, const _Float16 *b_base,
-                                          int64_t b_stride, int q, int ks,
-                                          int Hout, int Wout, u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER])
+template <int A_PER, int B_PER>
+__device__ __forceinline__ void load_step(const IgemmArgs &p, __amdgpu_buffer_rsrc_t ra_src, int4v g_row,
+                                          const _Float16 *b_base, int64_t b_stride, int q, int ks,
+                                          u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER])
 {
-    int kb;
-    if (MODE == kGemm) {
-        kb = ks * BK;
+    const int kb = ks * BK;
 #pragma unroll
-        for (int j = 0; j < A_PER; ++j)  // rows past M are past the resource
-            ra[j] = buf_load16(ra_src, (g_oy[j] * p.lda + kb + q * 8) * 2);
-    } else {
-        const int c = ks / 9;
-        const int tap = ks - 9 * c;
-        const int dy = tap / 3, dx = tap - 3 * dy;
-        kb = tap * p.cin_p + c * BK;
-        const int cofs = c * BK + q * 8;
-#pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-            const int uy = g_oy[j] + dy - 1, ux = g_ox[j] + dx - 1;
-            const bool ok = (uy >= 0) & (uy < Hout) & (ux >= 0) & (ux < Wout);
-            const int sy = (MODE == kConv3x3Up2) ? (uy >> 1) : uy;
-            const int sx = (MODE == kConv3x3Up2) ? (ux >> 1) : ux;
-            const int off = ok ? ((sy * p.W + sx) * p.cin_p + cofs) * 2 : kOOB;
-            ra[j] = buf_load16(ra_src, off);
-        }
-    }
+    for (int j = 0; j < A_PER; ++j)  // rows past M are past the resource
+        ra[j] = buf_load16(ra_src, (g_row[j] * p.lda + kb + q * 8) * 2);
 #pragma unroll
     for (int j = 0; j < B_PER; ++j) rb[j] = *reinterpret_cast<const u32x4 *>(b_base + j * b_stride + kb);
 }
@@ -120,7 +91,7 @@ __device__ __forceinline__ void mma_step(const _Float16 (*sA)[LDS_ROW], const _F
     }
 }
 
-template <int MODE, int BM, int BN, bool OUT_F16>
+template <int BM, int BN, bool OUT_F16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_igemm(IgemmArgs p)
 {
     constexpr int WTM = BM / 2, WTN = BN / 2;        // wave tile
@@ -147,38 +118,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int q = tid & 3;       // which 16-byte chunk of the 64-byte K slice
     const int rbase = tid >> 2;  // 0..63: row within each group of 64
 
-    const int Wout = (MODE == kConv3x3Up2) ? 2 * p.W : p.W;
-    const int Hout = (MODE == kConv3x3Up2) ? 2 * p.H : p.H;
-
-    // per-thread gather state: output pixel (convs) or block row (GEMM) of
-    // each row this thread loads
-    int4v g_oy = {0, 0, 0, 0}, g_ox = {0, 0, 0, 0};
-    __amdgpu_buffer_rsrc_t a_src;
-    if (MODE == kGemm) {
-        // the block's rows only: offsets stay small, rows past M read zero
-        const int rows = (p.M - m0) < BM ? (p.M - m0) : BM;
-        a_src = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)rows * p.lda * 2);
+    // the block's rows only: offsets stay small, rows past M read zero
+    const int rows = (p.M - m0) < BM ? (p.M - m0) : BM;
+    const __amdgpu_buffer_rsrc_t a_src = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)rows * p.lda * 2);
+    int4v g_row = {0, 0, 0, 0};  // the block rows this thread loads
 #pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-            g_oy[j] = rbase + 64 * j;
-            g_ox[j] = 0;
-        }
-    } else {
-        a_src = make_rsrc(p.a, (uint32_t)p.H * p.W * p.cin_p * 2);
-#pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-            const int m = m0 + rbase + 64 * j;
-            const bool in = m < p.M;
-            const int oy = m / Wout;
-            g_oy[j] = in ? oy : -(1 << 28);  // an out-of-range row fails every bounds test
-            g_ox[j] = m - oy * Wout;
-        }
-    }
+    for (int j = 0; j < A_PER; ++j) g_row[j] = rbase + 64 * j;
     // B rows n0 + rbase + 64j
     const _Float16 *b_base = p.b + (int64_t)(n0 + rbase) * p.ldb + q * 8;
     const int64_t b_stride = (int64_t)64 * p.ldb;
 
-    const int nks = (MODE == kGemm) ? (p.K / BK) : 9 * (p.cin_p / BK);
+    const int nks = p.K / BK;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -192,7 +142,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int fk = (lane >> 5) * 8;  // this lane's 8 K elements within 16
 
     u32x4 ra[A_PER], rb[B_PER];
-    load_step<MODE, A_PER, B_PER>(p, a_src, g_oy, g_ox, b_base, b_stride, q, 0, Hout, Wout, ra, rb);
+    load_step<A_PER, B_PER>(p, a_src, g_row, b_base, b_stride, q, 0, ra, rb);
     store_step<BM, BN, A_PER, B_PER>(sA[0], sB[0], rbase, q, ra, rb);
     __syncthreads();
 
@@ -200,7 +150,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     for (int ks = 0; ks < nks - 1; ++ks) {
         // the next step's loads go out first and stay first: the MFMAs of
         // this step hide their latency
-        load_step<MODE, A_PER, B_PER>(p, a_src, g_oy, g_ox, b_base, b_stride, q, ks + 1, Hout, Wout, ra, rb);
+        load_step<A_PER, B_PER>(p, a_src, g_row, b_base, b_stride, q, ks + 1, ra, rb);
         __builtin_amdgcn_sched_barrier(0);
         mma_step<FM, FN, WTM, WTN>(sA[cur], sB[cur], wm, wn, frow, fk, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -239,15 +189,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
 }
 
-template <int MODE, int BM, int BN, bool F16>
+template <int BM, int BN, bool F16>
 void launch_t(const IgemmArgs &a, hipStream_t s)
 {
     const int mt = (a.M + BM - 1) / BM;
     const int grid = mt * (a.N / BN);
-    hipLaunchKernelGGL((k_igemm<MODE, BM, BN, F16>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_igemm<BM, BN, F16>), dim3(grid), dim3(NT), 0, s, a);
 }
 
-template <int MODE, bool F16>
+template <bool F16>
 void launch_mode(const IgemmArgs &a, hipStream_t s)
 {
     const bool bn128 = (a.N % 128) == 0;
@@ -255,10 +205,10 @@ void launch_mode(const IgemmArgs &a, hipStream_t s)
     // prefer the 256-row tile when it still gives two workgroups per CU
     const long tiles256 = (long)((a.M + 255) / 256) * (a.N / bn);
     const bool bm256 = tiles256 >= 512;
-    if (bm256 && bn128) launch_t<MODE, 256, 128, F16>(a, s);
-    else if (bm256) launch_t<MODE, 256, 64, F16>(a, s);
-    else if (bn128) launch_t<MODE, 128, 128, F16>(a, s);
-    else launch_t<MODE, 128, 64, F16>(a, s);
+    if (bm256 && bn128) launch_t<256, 128, F16>(a, s);
+    else if (bm256) launch_t<256, 64, F16>(a, s);
+    else if (bn128) launch_t<128, 128, F16>(a, s);
+    else launch_t<128, 64, F16>(a, s);
 }
 
 }  // namespace
@@ -285,9 +235,9 @@ void launch_igemm(int mode, const IgemmArgs &a, hipStream_t s)
         if (gemm2_supported(g) && !(a.out_f16 && a.accumulate)) {
             launch_gemm2(a.out_f16 ? kEpiF16 : kEpiF32, g, s);
         } else if (a.out_f16) {
-            launch_mode<kGemm, true>(a, s);
+            launch_mode<true>(a, s);
         } else {
-            launch_mode<kGemm, false>(a, s);
+            launch_mode<false>(a, s);
         }
         break;
     }

@@ -80,7 +80,7 @@ class DeviceDecoder:
         cout, cin, k, _ = wt.shape
         cout_p, cin_p = cpad(cout), cpad(cin)
         src = self._dev(wt, torch.float16)
-        plane = torch.empty((cout_p, k * k, cin_p), dtype=torch.float16, device=self.device)
+        plane = torch.empty(L.plane_shape(cout_p, cin_p, k), dtype=torch.float16, device=self.device)
         self._keep.append(plane)
         L.pack_conv_weights(src, cout, cin, k, cout_p, cin_p, plane, self.stream)
         cw = L.ConvW()

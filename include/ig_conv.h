@@ -226,8 +226,9 @@ int guard_cast(const float *x, int M, int C, const float *bias, int guard_log2, 
                void *stream);
 
 /* ---------------------------------------------------------------------
- * The residual combine ([QI] `Rec::combine`), f32 [M][C]:
- *   mode 0: x += h + hb;  mode 1: x = s + sb + h + hb;  mode 2: x = h + hb.
+ * The residual combine ([QI] `Rec::combine`), f32 [M][C], with t = h + hb:
+ *   mode 0 adds t into x; mode 1 sets x to t plus the shortcut s + sb;
+ *   mode 2 sets x to t.
  *   hb, sb: [C] or NULL (zero). C % 4 == 0.
  * --------------------------------------------------------------------- */
 int ig_combine(float *x, const float *h, const float *hb, const float *s, const float *sb, int M,
@@ -260,7 +261,8 @@ int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols,
  *         (0 bytes for small m: ws may then be NULL); its contents on
  *         entry do not matter.
  * C must be 512 (IG_EUNSUPPORTED otherwise); ld >= m rounded up to 32,
- * ld % 8 == 0; q, k, vt, out 16-byte aligned. m < 2^22.
+ * ld % 8 == 0 and ld * C * 2 < 0x7fff0000 (the kernel addresses q, k and
+ * V^T with 32-bit byte offsets); q, k, vt, out 16-byte aligned. m < 2^22.
  * --------------------------------------------------------------------- */
 size_t ig_attention_workspace_bytes(int m, int C);
 int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int m, int ld, int C,
@@ -288,13 +290,14 @@ int ig_nhwc_to_nchw(const float *y, int M, int ld, int nch, const float *bias, f
 int ig_conv3x3_out_nchw(const uint16_t *x, int H, int W, int cin_p, const uint16_t *w, int cout, int cout_p,
                         const float *bias, float *out, void *stream);
 
-/* The DupUp shortcut ([QI] DUPUP_SRC and `run_blocks`): a channel shuffle
- * of the half-resolution input added onto the 2x grid,
- *   x[2y+sy][2x+sx][o] += src[y][x][(o*factor + (ft-1)*4 + 2*sy + sx) / repeats]
- * for o < cout, sy, sx in {0, 1}. With factor = repeats = 4 and ft = 1 it is
- * the nearest-2x broadcast of src added into x (in = out channels).
- *   src: f32 [H*W][cin_p]; x: f32 [4*H*W][cout_p]; every shuffled channel
- *   index must be < cin_p. */
+/* The DupUp shortcut ([QI] DUPUP_SRC and `run_blocks`): the half-resolution
+ * input, its channels repeated and moved to space, added onto the 2x grid.
+ * Output pixel (2y + sy, 2x + sx), channel o < cout, gets src pixel (y, x)'s
+ * channel (o * factor + 4 * (ft - 1) + 2 * sy + sx) / repeats. With
+ * factor = repeats = 4 and ft = 1 every output channel reads its own
+ * channel: the nearest-2x upsample of src added into x (in = out channels).
+ *   src: f32 [H*W][cin_p]; x: f32 [4*H*W][cout_p], 16-byte aligned,
+ *   cout_p % 4 == 0; every shuffled channel index must be < cin_p. */
 int ig_dupup_add(const float *src, int H, int W, int cin_p, float *x, int cout, int cout_p,
                  int factor, int repeats, int ft, void *stream);
 
@@ -370,16 +373,17 @@ int decoder_forward(const ig_decoder *dec, const float *latent, int h0, int w0, 
                     int q_chunk, void *ws, size_t ws_bytes, float *out, void *stream);
 
 /* ---------------------------------------------------------------------
- * Banded decode ([QI] the bands section: `grow`, `half`, `plan_band`,
- * `run_blocks`, `output_rows`). Everything after the mid block is local in
- * space, so up blocks band_from.. can run in horizontal bands of band_rows
- * kept output rows: each band starts from rows of the whole-frame stream
- * saved at block band_from's input, walked back from its kept rows (a 3x3
- * conv needs one more row per side, an upsample halves the range rounded
- * outward, both clamped to the frame); rows next to a band edge come out
- * wrong but never reach a kept row, so the kept rows are bit for bit the
- * whole-frame decode's. The workspace holds the whole-frame tensors up to
- * block band_from and one band's tensors after it.
+ * Banded decode ([QI] the bands section, `run_blocks`, `output_rows`).
+ * After the mid block every step only looks at nearby pixels, so up blocks
+ * band_from.. can run on horizontal bands of band_rows kept output rows.
+ * Each band starts from the rows of the whole-frame stream (saved at block
+ * band_from's input) that its kept rows depend on: tracing back, a 3x3 conv
+ * widens the range by a row per side and an upsample halves it, rounded
+ * outward, both cut at the frame's edges. Rows near a band's edge see zero
+ * padding where the whole frame has data, and so differ, but no kept row
+ * depends on them: the kept rows equal the whole-frame decode's exactly.
+ * The workspace holds the whole-frame tensors up to block band_from and one
+ * band's tensors after it.
  * band_rows <= 0 or band_from >= n_up: the whole frame (decoder_forward).
  * Returns 0 from the size query on invalid arguments (ig_last_error()).
  * --------------------------------------------------------------------- */

@@ -19,12 +19,13 @@ Sources (the pages are cited by title and item):
 
 * qi21_vae.rs (cortiq-engine 0.8.3): module doc; RMSN_SRC; CAST_SRC;
   `guard`; `Rec::resnet`; `attention`; `run_blocks`; `output_rows`; `decode`.
-* vae.rs (cortiq-engine 0.7.6): `Conv2d::apply`; `upsample2x`; `silu`;
+* vae.rs (cortiq-engine 0.7.6): `Conv2d::apply`; `upsample2x`; `silu` (the
+  SiLU inside ``rmsnorm``);
   `AttnBlock::apply`; `VaeDecoder::decode`; `GroupNorm::apply`; its unit
   tests.
-* qi21_vae.rs, the bands section: `grow`, `half`, `plan_band` (the band
-  planner, pinned by the pages' walk-back test and by brute force on a
-  1-D decoder).
+* qi21_vae.rs, the bands section: which rows a band of the up path needs
+  (exact dependency sets; pinned by the pages' walk-back test and by banded
+  evaluation of a 1-D decoder).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (library routines, closed forms, invariants, the pages' own worked values).
@@ -113,12 +114,6 @@ def f16(a) -> np.ndarray:
     out = np.empty_like(a)
     _load().orc_f16_round_n(_p(a), _p(out), a.size)
     return out
-
-
-def silu(v):
-    """y / (1 + e^-y) (vae.rs, `silu`)."""
-    v = _f64(v)
-    return v / (1.0 + np.exp(-v))
 
 
 def guard_cast(x, guard_log2, bias=None):
@@ -380,44 +375,44 @@ def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
 
 
 # ---------------------------------------------------------------------------
-# bands (qi21_vae.rs, the bands section: `grow`, `half`, `plan_band`)
+# bands (qi21_vae.rs, the bands section)
 # ---------------------------------------------------------------------------
 
 
-def rows_grow(lo, hi, k, h):
-    """Rows a 3x3-conv stack of k convs reads to produce rows [lo, hi) of an
-    h-row level: k more on each side, clamped to the level (the frame edge is
-    the convs' real zero padding)."""
-    return max(lo - k, 0), min(hi + k, h)
-
-
-def rows_half(lo, hi):
-    """Rows of the half-resolution input a nearest-2x upsample reads to
-    produce rows [lo, hi): output row r reads input row r // 2, so
-    [lo // 2, ceil(hi / 2))."""
-    return lo // 2, -(-hi // 2)
-
-
 def plan_band(n_res, has_up, h0, band_from, keep):
-    """Walk back from kept output rows through conv_out (one 3x3 conv) and
-    up blocks band_from.. in reverse (block i: n_res[i] resnets of two 3x3
-    convs, then, when has_up[i], the nearest-2x upsample and its 3x3 conv).
-    Returns (rows of block band_from's input, {i: rows block i feeds to its
-    upsample})."""
-    n_up = len(n_res)
-    lvl, l = [], 0
-    for u in has_up:
-        lvl.append(l)
-        l += 1 if u else 0
-    e = rows_grow(keep[0], keep[1], 1, h0 << l)
-    feed = {}
-    for i in range(n_up - 1, band_from - 1, -1):
+    """The rows a band of the up path needs, as exact dependency sets.
+
+    After the mid block every step only looks at nearby rows (qi21_vae.rs,
+    the bands section), so a band of kept output rows needs only some rows
+    of each level. The steps from block band_from's input to the frame are
+    listed in order -- per block 2 n_res 3x3 convs, then, with has_up, the
+    nearest-2x upsample and its 3x3 conv; conv_out last -- and the set of
+    kept rows is carried back through them: a 3x3 conv on a level of h rows
+    reads rows r - 1, r, r + 1 of its input where they exist (0 <= . < h;
+    outside, the zero padding), an upsample reads row r // 2.
+
+    Returns ((first, end) of the rows of block band_from's input the band
+    needs, {block i: (first, end) of the rows block i hands to its
+    upsample}). Every set is a contiguous range; the returned ranges are
+    its first row and one past its last."""
+    h = h0 << sum(1 for u in has_up[:band_from] if u)
+    steps = []
+    for i in range(band_from, len(n_res)):
+        steps += [("conv", h, i)] * (2 * n_res[i])
         if has_up[i]:
-            g = rows_grow(e[0], e[1], 1, h0 << (lvl[i] + 1))
-            e = rows_half(*g)
-            feed[i] = e
-        e = rows_grow(e[0], e[1], 2 * n_res[i], h0 << lvl[i])
-    return e, feed
+            steps.append(("up", 0, i))
+            h *= 2
+            steps.append(("conv", h, i))
+    steps.append(("conv", h, None))  # conv_out
+    rows = set(range(keep[0], keep[1]))
+    feed = {}
+    for kind, height, block in reversed(steps):
+        if kind == "conv":
+            rows = {r + d for r in rows for d in (-1, 0, 1) if 0 <= r + d < height}
+        else:
+            rows = {r // 2 for r in rows}
+            feed[block] = (min(rows), max(rows) + 1)
+    return (min(rows), max(rows) + 1), feed
 
 
 # ---------------------------------------------------------------------------

@@ -50,7 +50,7 @@ def packed(w16, stream=None):
 
     cout, cin, k, _ = w16.shape
     src = dev(w16)
-    plane = torch.empty((cpad(cout), k * k, cpad(cin)), dtype=torch.float16, device=DEV)
+    plane = torch.empty(ig.plane_shape(cpad(cout), cpad(cin), k), dtype=torch.float16, device=DEV)
     ig.pack_conv_weights(src, cout, cin, k, cpad(cout), cpad(cin), plane, stream)
     return plane
 

@@ -108,6 +108,26 @@ def test_validation_rejects_before_enqueueing(ig):
     assert lib.ig_softmax_rows_f16(fake, 4, 64, 65, 65, fake, 64, None) == -1
     assert "valid" in ig.last_error() or "softmax" in ig.last_error()
     assert lib.ig_dupup_add(fake, 2, 2, 64, fake, 64, 64, 4, 1, 1, None) == -1
+    assert lib.ig_dupup_add(fake, 2, 2, 64, fake, 62, 66, 4, 4, 1, None) == -2  # cout_p % 4
+    # attention: q, k and V^T are addressed with 32-bit byte offsets, so a
+    # row stride whose ld * C * 2 reaches 0x7fff0000 bytes is refused (a
+    # wrapped offset would silently read zeros)
+    lib.attention_f16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2 + \
+        [ctypes.c_size_t] + [ctypes.c_void_p] * 2
+    big = 0x7fff0000 // (512 * 2)
+    assert lib.attention_f16(fake, fake, fake, 1024, big + 8, 512, None, fake, 1 << 30, fake, None) == -1
+    assert "ld" in ig.last_error()
+    assert lib.attention_f16(fake, fake, fake, 1024, 1 << 22, 512, None, fake, 1 << 30, fake, None) == -1
+    # groupnorm without a workspace: the same checks as with one
+    lib.groupnorm_silu_f16_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.groupnorm_silu_f16_noalloc(fake, 8, 1028, 1028, 4, None, fake, fake, 1, ctypes.c_float(1e-6), fake,
+                                          None) == -2
+    assert lib.groupnorm_silu_f16_noalloc(fake, 8, 128, 128, 3, None, fake, fake, 1, ctypes.c_float(1e-6), fake,
+                                          None) == -2
+    assert lib.groupnorm_silu_f16_noalloc(fake, 8, 128, 128, 32, None, None, fake, 1, ctypes.c_float(1e-6), fake,
+                                          None) == -1
 
 
 def test_decoder_descriptor_validation(ig):

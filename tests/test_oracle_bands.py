@@ -1,9 +1,9 @@
 """The band planner (page "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs",
-the bands section): the oracle's `plan_band` against the pages' own
-walk-back test, against an exact backward dependency analysis, and against
-banded evaluation of a 1-D integer decoder (bands computed from the planned
-rows only reproduce the whole-frame rows exactly); then the library's host
-planner against the oracle's on random decoders."""
+the bands section): the oracle's dependency-set `plan_band` against the
+pages' own walk-back test, closed forms, and banded evaluation of a 1-D
+integer decoder (bands computed from the planned rows only reproduce the
+whole-frame rows exactly); then the library's interval planner against the
+oracle's sets on random decoders."""
 
 import json
 import os
@@ -17,23 +17,6 @@ import oracle as O
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "band_walk_back_case.json")
 
 
-def test_walk_back_matches_the_pages_case():
-    g = json.load(open(GOLDEN))
-    inp, feed = O.plan_band(g["n_res"], g["has_up"], g["h0"], g["band_from"], tuple(g["keep"]))
-    assert list(feed[0]) == g["expected_feed_block0"]
-    assert list(inp) == g["expected_input"]
-    e = g["edge_case"]
-    assert list(O.rows_grow(e["rows"][0], e["rows"][1], e["grow"], e["h"])) == e["expected"]
-
-
-def test_half_rounds_outward():
-    # output row r of a 2x upsample reads input row r // 2
-    for lo in range(0, 9):
-        for hi in range(lo + 1, 12):
-            need = {r // 2 for r in range(lo, hi)}
-            assert O.rows_half(lo, hi) == (min(need), max(need) + 1)
-
-
 def _levels(has_up):
     lvl, l = [], 0
     for u in has_up:
@@ -42,22 +25,36 @@ def _levels(has_up):
     return lvl, l
 
 
-def _needed(n_res, has_up, h0, band_from, keep):
-    """Exact backward dependency as sets of rows."""
-    lvl, lf = _levels(has_up)
+def test_walk_back_matches_the_pages_case():
+    g = json.load(open(GOLDEN))
+    inp, feed = O.plan_band(g["n_res"], g["has_up"], g["h0"], g["band_from"], tuple(g["keep"]))
+    assert list(feed[0]) == g["expected_feed_block0"]
+    assert list(inp) == g["expected_input"]
+    # the clamp at the frame edge: three 3x3 convs (one resnet, then
+    # conv_out) on a 12-row frame, keeping rows [0, 10), need all 12 rows
+    e = g["edge_case"]
+    inp, feed = O.plan_band([1], [0], e["h"], 0, tuple(e["rows"]))
+    assert e["grow"] == 3 and list(inp) == e["expected"] and feed == {}
 
-    def conv_back(rows, h):
-        return {r + d for r in rows for d in (-1, 0, 1) if 0 <= r + d < h}
 
-    rows = conv_back(set(range(*keep)), h0 << lf)
-    feed = {}
-    for i in range(len(n_res) - 1, band_from - 1, -1):
-        if has_up[i]:
-            rows = {r // 2 for r in conv_back(rows, h0 << (lvl[i] + 1))}
-            feed[i] = rows
-        for _ in range(2 * n_res[i]):
-            rows = conv_back(rows, h0 << lvl[i])
-    return rows, feed
+def test_plan_band_closed_forms():
+    """Without upsamples the band grows by one row per 3x3 conv on each
+    side, cut at the frame: [max(lo - n, 0), min(hi + n, h)) for n convs. An
+    upsample then a 3x3 conv then conv_out (no resnets) needs
+    [(lo - 2) // 2, (hi + 1) // 2 + 1) of the half-resolution rows, cut."""
+    for h in (5, 9, 16):
+        for n_res in (0, 1, 3):
+            for lo in range(h):
+                for hi in range(lo + 1, h + 1):
+                    n = 2 * n_res + 1
+                    inp, feed = O.plan_band([n_res], [0], h, 0, (lo, hi))
+                    assert inp == (max(lo - n, 0), min(hi + n, h)) and feed == {}
+    for h0 in (3, 8):
+        for lo in range(2 * h0):
+            for hi in range(lo + 1, 2 * h0 + 1):
+                inp, feed = O.plan_band([0], [1], h0, 0, (lo, hi))
+                want = (max((lo - 2) // 2, 0), min((hi + 1) // 2 + 1, h0))
+                assert inp == want and feed == {0: want}
 
 
 def _random_decoder(rng):
@@ -65,22 +62,6 @@ def _random_decoder(rng):
     n_res = [rng.randint(0, 2) for _ in range(n_up)]
     has_up = [rng.random() < 0.7 for _ in range(n_up)]
     return n_res, has_up, rng.randint(3, 9)
-
-
-def test_plan_band_equals_exact_dependencies():
-    rng = random.Random(5)
-    for _ in range(300):
-        n_res, has_up, h0 = _random_decoder(rng)
-        hf = h0 << sum(has_up)
-        s = rng.randint(0, len(n_res))
-        lo = rng.randrange(hf)
-        keep = (lo, rng.randint(lo + 1, hf))
-        inp, feed = O.plan_band(n_res, has_up, h0, s, keep)
-        rows, need_feed = _needed(n_res, has_up, h0, s, keep)
-        assert (min(rows), max(rows) + 1) == inp
-        assert sorted(feed) == sorted(need_feed)
-        for i, f in feed.items():
-            assert (min(need_feed[i]), max(need_feed[i]) + 1) == f
 
 
 def _conv3(x, taps):
