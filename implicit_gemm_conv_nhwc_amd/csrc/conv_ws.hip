@@ -41,6 +41,8 @@
 //  * workgroups walk the tiles persistently; workgroup b runs on XCD b % 8
 //    and each XCD takes a contiguous range of tile rows (shared halos stay
 //    in its L2).
+#include <type_traits>
+
 #include "ig_internal.h"
 
 namespace ig {
@@ -164,6 +166,42 @@ __device__ __forceinline__ void mma(f32x16 &acc, const half8 &w, const half8 &b,
     }
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1: the loops
+// whose index selects registers (weight fragments, accumulators, fragment
+// buffers) are expanded at compile time, whatever their body's size.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The i-th (output row r, tap row dy, patch row pr) of a fragment group, in
+// patch-row order: each patch-row fragment read from LDS feeds every
+// (r, dy) that reads it. 3 TH pairs per group.
+template <int MODE>
+struct Triple {
+    int r, dy, pr;
+};
+template <int MODE>
+constexpr Triple<MODE> group_triple(int i)
+{
+    constexpr int ph = WGeo<MODE>::PH;
+    int n = 0;
+    for (int pr = 0; pr < ph; ++pr)
+        for (int dy = 0; dy < 3; ++dy)
+            for (int r = 0; r < TH; ++r)
+                if (WGeo<MODE>::arow(r, dy) == pr) {
+                    if (n == i) return Triple<MODE>{r, dy, pr};
+                    ++n;
+                }
+    return Triple<MODE>{-1, -1, -1};
+}
+
 struct WTile {
     int y0, x0;
     uint32_t aoff[4];  // per patch load of this lane: source byte offset at stage 0 (kOOB: zeros)
@@ -180,11 +218,25 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
-// The epilogue's outputs, fixed per instantiation so that every stage
-// issues the same number of memory operations (the stage wait counts them):
-// ACC adds the f32 output's current values (the residual stream), WOUT
-// stores the f32 result, YG stores its guarded f16 cast, NORM stores the
-// pixel's f16 RMS_norm (+ SiLU).
+// The epilogue's outputs, fixed per instantiation: ACC adds the f32
+// output's current values (the residual stream), WOUT stores the f32
+// result, YG stores its guarded f16 cast, NORM stores the pixel's f16
+// RMS_norm (+ SiLU).
+//
+// Schedule. A stage is six fragment groups of 12 MFMAs (72 slots). The wait
+// and barrier for the next stage sit between groups 4 and 5: every wave has
+// then read group 5's fragments into registers, so the stage's buffer is
+// free, and the next stage's first fragments load while group 5 runs. The
+// epilogue of the tile staged before (the "staged" tile) runs as small
+// items between the MFMAs of the next tile's stages 1-3, and the patch
+// loads go out after the barrier, one per slot from slot 60:
+//   stage 0: -                  (the staged tile becomes visible at its barrier)
+//   stage 1: rows 0, 1          (stream loads of row 2)
+//   stage 2: row 2              (stream loads of row 3)
+//   stage 3: row 3              (stream loads of this tile's rows 0, 1)
+// Every wait counts exactly the operations that may stay in flight: the
+// stream loads a drained row needs land by the barrier before it; stores
+// and the latest patch loads do not hold a wait up.
 template <int MODE, bool NORM, bool ACC, bool WOUT, bool YG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_conv_ws(IgemmArgs p)
@@ -193,19 +245,19 @@ void k_conv_ws(IgemmArgs p)
     constexpr int PH = G::PH, PW = G::PW;
     constexpr int A_INSTR = G::A_INSTR, A_PAD = G::A_PAD, APW = G::APW;
     static_assert(APW <= 4, "patch loads per lane");
-    static_assert(NST == TH, "one staged row drained per stage");
+    static_assert(NST == 4 && TH == 4, "the drain schedule covers 4 rows over 4 stages");
     static_assert(NBUF == NST, "stage s lands in buffer s");
     static_assert(!(NORM && (ACC || YG)), "the fused norm writes neither a sum nor a cast");
-    // memory operations per stage besides the patch loads
-    constexpr int NDL = ACC ? 4 : 0;                                   // stream loads
-    constexpr int NDS = (WOUT ? 4 : 0) + (YG ? 4 : 0) + (NORM ? 2 : 0);  // stores
-    // At a stage's start the stage's patch (issued three stages earlier)
-    // and the stream values of the row it drains (two stages earlier) must
-    // have landed; after those loads each stage issues its stores, the next
-    // stream loads and its patch loads, and at most this many operations
-    // issued later may still be in flight.
-    constexpr int WAITN = 2 * APW + NDS + NDL;
-    static_assert(WAITN < 64, "vmcnt range");
+    // vector-memory operations of the drain's items
+    constexpr int OPS_L = ACC ? 4 : 0;                               // stream loads of a row
+    constexpr int OPS_ROW = (WOUT ? 4 : 0) + (YG ? 4 : 0) + (NORM ? 2 : 0);  // stores of a row
+    // operations that may stay in flight at the wait in stage st (see the
+    // schedule): after the loads that must have landed come only these
+    constexpr int WAIT0 = APW;                                  // stream rows 0, 1 (staged in stage 3)
+    constexpr int WAIT1 = ACC ? OPS_ROW : 2 * OPS_ROW + APW;    // stream row 2, then row 1's stores
+    constexpr int WAIT2 = ACC ? OPS_ROW : OPS_ROW + APW;        // stream row 3, then row 2's stores
+    constexpr int WAIT3 = OPS_ROW + 2 * OPS_L + APW;            // nothing of the drain
+    static_assert(WAIT3 < 64 && WAIT1 < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(16))) u32x4 lds[ws_lds_bytes<MODE>() / 16];
     float *stg = reinterpret_cast<float *>(lds + NBUF * A_PAD);  // [TH][TW][SP]
@@ -264,15 +316,12 @@ void k_conv_ws(IgemmArgs p)
         }
         return r;
     };
-    // this wave's APW patch loads of stage st of tile tl into buffer buf
-    // (loads past the patch read zeros into the buffer's padding)
-    auto issue = [&](const WTile &tl, int st, int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < APW; ++k) {
-            const int ii = wave + NW * k;
-            const uint32_t off = tl.aoff[k] == kOOB ? kOOB : tl.aoff[k] + st * CK * 2;
-            dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, ii < A_INSTR ? off : kOOB);
-        }
+    // patch load k (of APW) of stage st of tile tl into buffer buf (loads
+    // past the patch read zeros into the buffer's padding)
+    auto issue_one = [&](const WTile &tl, int st, int buf, int k) __attribute__((always_inline)) {
+        const int ii = wave + NW * k;
+        const uint32_t off = tl.aoff[k] == kOOB ? kOOB : tl.aoff[k] + st * CK * 2;
+        dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, ii < A_INSTR ? off : kOOB);
     };
 
     // the wave's weights: fragment f = (2 s + ks) 9 + tap = output channel
@@ -298,9 +347,10 @@ void k_conv_ws(IgemmArgs p)
     // 16 h + tid / 16, channels 8 (tid % 16) .. + 7, a pixel per DPP row.
     const int dpx = tid >> 5, dc = (tid & 31) * 4;
     const int npx = tid >> 4, nc = (tid & 15) * 8;
-    int sy0 = 0, sx0 = 0;       // the staged tile
+    int sy0 = 0, sx0 = 0;  // the staged tile
     bool staged = false;
-    // stream values of the next two drained rows: even rows in xa, odd in xb
+    // a row's values in flight: the stream values it adds to (loaded a stage
+    // ahead), then the row's results; even rows in xa, odd rows in xb
     f32x4 xa[4] = {}, xb[4] = {};
     // byte offset of (row r of a tile at y0, pixel x0 + px, channel c) in an
     // output of esz-byte elements with row pitch ld, relative to row y0;
@@ -316,159 +366,182 @@ void k_conv_ws(IgemmArgs p)
         return srd(reinterpret_cast<const char *>(base) + (int64_t)y0 * Wout * ld * esz,
                    (uint32_t)(rem < (int64_t)kOOB ? rem : (int64_t)kOOB));
     };
-    // stream loads of row r of the tile at (y0, x0) into x (xa or xb: the
-    // callers pick the array by the row's parity with a plain branch, which
-    // keeps both in registers)
-    auto load_row = [&](f32x4 (&x)[4], bool live, int y0, int x0, int r) __attribute__((always_inline)) {
+    // item L: the stream values of row r of the tile at (y0, x0) into x
+    auto item_load = [&](f32x4 (&x)[4], bool live, int y0, int x0, int r) __attribute__((always_inline)) {
         if constexpr (ACC) {
             const i32x4 rs = out_srd(p.c, y0, p.ldc, 4);
 #pragma unroll
             for (int k = 0; k < 4; ++k) x[k] = ld16(rs, doff(live, y0, x0, r, 8 * k + dpx, dc, p.ldc, 4));
         }
     };
-    auto drain_load = [&](bool live, int y0, int x0, int r) __attribute__((always_inline)) {
-        if (r & 1) load_row(xb, live, y0, x0, r);
-        else load_row(xa, live, y0, x0, r);
-    };
-    // the outputs of row r of the staged tile (stores only when live); x:
-    // the row's stream values
-    auto store_row = [&](const f32x4 (&x)[4], bool live, int r) __attribute__((always_inline)) {
+    // item A: row r's staged results (plus the stream values) into x
+    auto item_read = [&](f32x4 (&x)[4], int r) __attribute__((always_inline)) {
         if constexpr (WOUT || YG) {
-            f32x4 v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                v[k] = *reinterpret_cast<const f32x4 *>(stg + (r * TW + 8 * k + dpx) * SP + dc);
-                if constexpr (ACC) v[k] += x[k];
-            }
-            if constexpr (WOUT) {
-                const i32x4 rs = out_srd(p.c, sy0, p.ldc, 4);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) st16(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 4), v[k], true);
-            }
-            if constexpr (YG) {
-                const i32x4 rs = out_srd(p.yg, sy0, p.ldc, 2);
-                const float gs = p.gscale;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    half4v h;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) h[e] = (_Float16)(v[k][e] * gs);
-                    st8(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 2), h);
-                }
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + (r * TW + 8 * k + dpx) * SP + dc);
+                if constexpr (ACC) x[k] += v;
+                else x[k] = v;
             }
         }
+    };
+    // item S: pass k of row r's f32 and guarded-cast stores
+    auto item_store = [&](const f32x4 (&x)[4], bool live, int r, int k) __attribute__((always_inline)) {
+        if constexpr (WOUT) {
+            const i32x4 rs = out_srd(p.c, sy0, p.ldc, 4);
+            st16(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 4), x[k], true);
+        }
+        if constexpr (YG) {
+            const i32x4 rs = out_srd(p.yg, sy0, p.ldc, 2);
+            half4v h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = (_Float16)(x[k][e] * p.gscale);
+            st8(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 2), h);
+        }
+    };
+    // item N: pass h of row r's RMS_norm (+ SiLU), f16
+    auto item_norm = [&](bool live, int r, int h) __attribute__((always_inline)) {
         if constexpr (NORM) {
-            const bool silu = p.norm_silu != 0;
+            const float *sv = stg + (r * TW + 16 * h + npx) * SP + nc;
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(sv);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(sv + 4);
+            float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] +
+                       b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+            ss = row16_sum(ss);
+            const float inv = sqrtf((float)p.norm_c) / fmaxf(sqrtf(ss), p.norm_eps);
             const f32x4 ga = *reinterpret_cast<const f32x4 *>(sgam + nc);
             const f32x4 gb = *reinterpret_cast<const f32x4 *>(sgam + nc + 4);
-            const float rc = sqrtf((float)p.norm_c);
-            const i32x4 rs = out_srd(p.ny, sy0, BN, 2);
+            const bool silu = p.norm_silu != 0;
+            half8 o;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float *sv = stg + (r * TW + 16 * h + npx) * SP + nc;
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(sv);
-                const f32x4 b = *reinterpret_cast<const f32x4 *>(sv + 4);
-                float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] +
-                           b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
-                ss = row16_sum(ss);
-                const float inv = rc / fmaxf(sqrtf(ss), p.norm_eps);
-                half8 o;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float y = (e < 4 ? a[e] * ga[e] : b[e - 4] * gb[e - 4]) * inv;
-                    // SiLU as y * rcp(1 + exp(-y)) (hardware reciprocal, ~1 ulp)
-                    const float ex = silu ? __expf(-y) : 0.f;
-                    o[e] = (_Float16)(y * __builtin_amdgcn_rcpf(1.0f + ex));
-                }
-                st16(rs, doff(live, sy0, sx0, r, 16 * h + npx, nc, BN, 2), __builtin_bit_cast(f32x4, o), false);
+            for (int e = 0; e < 8; ++e) {
+                const float y = (e < 4 ? a[e] * ga[e] : b[e - 4] * gb[e - 4]) * inv;
+                // SiLU as y * rcp(1 + exp(-y)) (hardware reciprocal, ~1 ulp)
+                const float ex = silu ? __expf(-y) : 0.f;
+                o[e] = (_Float16)(y * __builtin_amdgcn_rcpf(1.0f + ex));
             }
+            const i32x4 rs = out_srd(p.ny, sy0, BN, 2);
+            st16(rs, doff(live, sy0, sx0, r, 16 * h + npx, nc, BN, 2), __builtin_bit_cast(f32x4, o), false);
         }
     };
-    auto drain_store = [&](bool live, int r) __attribute__((always_inline)) {
-        if (r & 1) store_row(xb, live, r);
-        else store_row(xa, live, r);
+    // a whole drained row (the end of the kernel)
+    auto drain_row = [&](f32x4 (&x)[4], int r) __attribute__((always_inline)) {
+        item_read(x, r);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) item_store(x, true, r, k);
+        item_norm(true, r, 0);
+        item_norm(true, r, 1);
     };
-    // all but the last WAITN memory operations have landed (and, after the
-    // barrier, every wave's); the stream values are ready from here on
-    auto stage_wait = [&]() __attribute__((always_inline)) {
+    // the wait: all but the last n vector-memory operations have landed (and,
+    // after the barrier, every wave's); the stream values are ready
+    auto wait_n = [&](auto n) __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(%8)"
                      : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]), "+v"(xb[2]),
                        "+v"(xb[3])
-                     : "n"(WAITN)
+                     : "n"(decltype(n)::value)
                      : "memory");
         lds_barrier();
     };
 
     WTile cur = make_tile(t);
     WTile nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
-    // the three stages before the first: placeholder stores and stream
-    // loads (outside every output; the loads go straight to the unused
-    // staging area, so no register waits for them) and this tile's first
-    // three patches, so the first stages wait exactly as the later ones
-    const i32x4 none = srd(p.a, 0);
+    // the first tile's four patches, with placeholder stream loads where a
+    // tile's rows 0 and 1 would be loaded, so the first waits count as the
+    // later ones
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        drain_store(false, 0);
+    for (int st = 0; st < 3; ++st)
 #pragma unroll
-        for (int k = 0; k < NDL; ++k) dma16(none, lds_base + (NBUF * A_PAD + (wave * NDL + k) * 64) * 16, kOOB);
-        issue(cur, j, j);
-    }
+        for (int k = 0; k < APW; ++k) issue_one(cur, st, st, k);
+    item_load(xa, false, 0, 0, 0);
+    item_load(xb, false, 0, 0, 1);
+#pragma unroll
+    for (int k = 0; k < APW; ++k) issue_one(cur, NST - 1, NST - 1, k);
+    wait_n(std::integral_constant<int, 3 * APW + 2 * OPS_L>{});
+
+    // fragment groups (K-step ks, tap column dx) g = 3 ks + dx; group g's
+    // PH patch-row fragments live in bf[g & 1]
+    half8 bf[2][PH];
+    auto load_group = [&](const u32x4 *sA, int g, half8 *b) __attribute__((always_inline)) {
+        const int ks = g / 3, dx = g % 3;
+        const int pc = G::pcol(fx, dx);
+        const int sq = (2 * ks + fh) ^ ((pc >> 2) & 3);
+        const half8 *sa = reinterpret_cast<const half8 *>(sA) + pc * 4 + sq;
+#pragma unroll
+        for (int pr = 0; pr < PH; ++pr) b[pr] = sa[pr * PW * 4];
+    };
+    load_group(lds, 0, bf[0]);
 
     for (;;) {
         f32x16 acc[TH];
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            stage_wait();
-            drain_store(staged, st);
-            // stream values two rows ahead: the staged tile's rows 2, 3, then
-            // this tile's rows 0, 1
-            if (st + 2 < NST) drain_load(staged, sy0, sx0, st + 2);
-            else drain_load(true, cur.y0, cur.x0, st + 2 - NST);
-            // patches three stages ahead: this tile's last stage, then the
-            // next tile's first three (zeros when there is none)
-            if (st == 0) issue(cur, NST - 1, NST - 1);
-            else issue(nxt, st - 1, st - 1);
-
+        // one stage; st is a compile-time constant (the weight fragments are
+        // indexed by it and must stay in registers)
+        auto run_stage = [&](auto stc) __attribute__((always_inline)) {
+            constexpr int st = decltype(stc)::value;
             const u32x4 *sA = lds + st * A_PAD;
-            // six fragment groups (K-step ks, tap column dx): each group's
-            // PH patch-row fragments are read before the previous group's
-            // MFMAs run
-            half8 bf[2][PH];
-            auto load_group = [&](int g, half8 *b) __attribute__((always_inline)) {
-                const int ks = g / 3, dx = g % 3;
-                const int pc = G::pcol(fx, dx);
-                const int sq = (2 * ks + fh) ^ ((pc >> 2) & 3);
-                const half8 *sa = reinterpret_cast<const half8 *>(sA) + pc * 4 + sq;
-#pragma unroll
-                for (int pr = 0; pr < PH; ++pr) b[pr] = sa[pr * PW * 4];
+            // the drain item after the MFMA in slot i of this stage
+            auto hook = [&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (st == 1) {
+                    if constexpr (i == 0) item_read(xa, 0);
+                    if constexpr (i == 2) item_read(xb, 1);
+                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, staged, 0, (i - 4) / 4);
+                    if constexpr (i == 20) item_load(xa, staged, sy0, sx0, 2);
+                    if constexpr (i >= 24 && i < 40 && i % 4 == 0) item_store(xb, staged, 1, (i - 24) / 4);
+                    if constexpr (i == 6) item_norm(staged, 0, 0);
+                    if constexpr (i == 18) item_norm(staged, 0, 1);
+                    if constexpr (i == 30) item_norm(staged, 1, 0);
+                    if constexpr (i == 42) item_norm(staged, 1, 1);
+                } else if constexpr (st == 2) {
+                    if constexpr (i == 0) item_read(xa, 2);
+                    if constexpr (i == 2) item_load(xb, staged, sy0, sx0, 3);
+                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, staged, 2, (i - 4) / 4);
+                    if constexpr (i == 6) item_norm(staged, 2, 0);
+                    if constexpr (i == 18) item_norm(staged, 2, 1);
+                } else if constexpr (st == 3) {
+                    if constexpr (i == 0) item_read(xb, 3);
+                    if constexpr (i == 2) item_load(xa, true, cur.y0, cur.x0, 0);
+                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xb, staged, 3, (i - 4) / 4);
+                    if constexpr (i == 20) item_load(xb, true, cur.y0, cur.x0, 1);
+                    if constexpr (i == 6) item_norm(staged, 3, 0);
+                    if constexpr (i == 18) item_norm(staged, 3, 1);
+                }
+                // after the barrier: the next tile's patch for this stage's buffer
+                if constexpr (i >= 60 && i < 60 + APW) issue_one(nxt, st, st, i - 60);
             };
-            load_group(0, bf[0]);
-#pragma unroll
-            for (int g = 0; g < 6; ++g) {
-                if (g + 1 < 6) load_group(g + 1, bf[(g + 1) & 1]);
-                const int ks = g / 3, dx = g % 3;
-                const half8 *b = bf[g & 1];
-#pragma unroll
-                for (int pr = 0; pr < PH; ++pr)
-#pragma unroll
-                    for (int dy = 0; dy < 3; ++dy)
-#pragma unroll
-                        for (int r = 0; r < TH; ++r)
-                            if (G::arow(r, dy) == pr) {
-                                const int f = (2 * st + ks) * 9 + dy * 3 + dx;
-                                // the first and last MFMA of each accumulator's chain
-                                const bool first = st == 0 && ks == 0 && dx == 0 && dy == 0;
-                                const bool lastm = st == NST - 1 && ks == 1 && dx == 2 && dy == 2;
-                                const int kind = first ? 0 : (lastm ? 2 : 1);
-                                if (f < NST * 18 - NWF) mma<true>(acc[r], wr[f], b[pr], kind);
-                                else mma<false>(acc[r], wr[f], b[pr], kind);
-                            }
-            }
-        }
-        // every wave is done with the staged rows before they are replaced
-        lds_barrier();
+            static_for<6>([&](auto gc) __attribute__((always_inline)) {
+                constexpr int g = decltype(gc)::value;
+                if constexpr (g == 5) {
+                    // the next stage's buffer has landed and every wave is
+                    // past this stage's LDS reads; its first fragments load
+                    // under group 5's MFMAs
+                    if constexpr (st == 0) wait_n(std::integral_constant<int, WAIT0>{});
+                    else if constexpr (st == 1) wait_n(std::integral_constant<int, WAIT1>{});
+                    else if constexpr (st == 2) wait_n(std::integral_constant<int, WAIT2>{});
+                    else wait_n(std::integral_constant<int, WAIT3>{});
+                    load_group(lds + ((st + 1) % NBUF) * A_PAD, 0, bf[0]);
+                } else {
+                    load_group(sA, g + 1, bf[(g + 1) & 1]);
+                }
+                constexpr int ks = g / 3, dx = g % 3;
+                static_for<3 * TH>([&](auto ic) __attribute__((always_inline)) {
+                    constexpr int i = decltype(ic)::value;
+                    constexpr Triple<MODE> tr = group_triple<MODE>(i);
+                    static_assert(tr.r >= 0, "a group has 3 TH MFMAs");
+                    constexpr int f = (2 * st + ks) * 9 + tr.dy * 3 + dx;
+                    // the first and last MFMA of each accumulator's chain
+                    constexpr bool first = st == 0 && ks == 0 && dx == 0 && tr.dy == 0;
+                    constexpr bool lastm = st == NST - 1 && ks == 1 && dx == 2 && tr.dy == 2;
+                    constexpr int kind = first ? 0 : (lastm ? 2 : 1);
+                    if constexpr (f < NST * 18 - NWF) mma<true>(acc[tr.r], wr[f], bf[g & 1][tr.pr], kind);
+                    else mma<false>(acc[tr.r], wr[f], bf[g & 1][tr.pr], kind);
+                    hook(std::integral_constant<int, g * 3 * TH + i>{});
+                });
+            });
+        };
+        static_for<NST>(run_stage);
         // stage the tile (oscale, bias): lane l holds pixel fx, channels
-        // 32 wave + 8 k + 4 fh .. + 3
+        // 32 wave + 8 k + 4 fh .. + 3. The staged tile before it was drained
+        // before the last barrier; this one is read after the next.
 #pragma unroll
         for (int r = 0; r < TH; ++r)
 #pragma unroll
@@ -489,17 +562,14 @@ void k_conv_ws(IgemmArgs p)
         nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
     }
     // the last tile's rows (the stream values of rows 0 and 1 are loading)
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]),
-                 "+v"(xb[2]), "+v"(xb[3]) :: "memory");
-    lds_barrier();
-    drain_store(true, 0);
-    drain_store(true, 1);
-    drain_load(true, sy0, sx0, 2);
-    drain_load(true, sy0, sx0, 3);
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]),
-                 "+v"(xb[2]), "+v"(xb[3]) :: "memory");
-    drain_store(true, 2);
-    drain_store(true, 3);
+    wait_n(std::integral_constant<int, 0>{});
+    drain_row(xa, 0);
+    drain_row(xb, 1);
+    item_load(xa, true, sy0, sx0, 2);
+    item_load(xb, true, sy0, sx0, 3);
+    wait_n(std::integral_constant<int, 0>{});
+    drain_row(xa, 2);
+    drain_row(xb, 3);
 }
 
 int cu_count()
