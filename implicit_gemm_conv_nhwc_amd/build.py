@@ -10,6 +10,7 @@ know the feature; that is harmless).
 from __future__ import annotations
 
 import concurrent.futures as cf
+import importlib.util
 import os
 import subprocess
 import sys
@@ -49,11 +50,39 @@ def _compile(src: str) -> str:
     return obj
 
 
+# sources whose MFMAs are inline asm: their device assembly is scanned for
+# accesses the compiler placed inside an MFMA's latency window
+ASM_MFMA_SOURCES = ["conv_ws.hip", "attn_flash.hip"]
+
+
+def _check_isa(src: str) -> list:
+    out = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *CFLAGS, "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc -S failed for %s:\n%s" % (src, r.stderr))
+    spec = importlib.util.spec_from_file_location("_ig_isa_check", os.path.join(HERE, "isa_check.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with open(out) as f:
+        text = f.read()
+    return [(src,) + x for x in mod.scan(text) + mod.scan_m0(text)]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libigconv.so; returns its path."""
+    """Compile every HIP source and link libigconv.so; returns its path.
+
+    Refuses to link when the device code of an asm-MFMA source reads an
+    MFMA result (or overwrites its accumulator) too early."""
     os.makedirs(OUT_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(ASM_MFMA_SOURCES))) as ex:
+        objs_f = [ex.submit(_compile, src) for src in SOURCES]
+        isa_f = [ex.submit(_check_isa, src) for src in ASM_MFMA_SOURCES]
+        objs = [f.result() for f in objs_f]
+        findings = [x for f in isa_f for x in f.result()]
+    if findings:
+        raise RuntimeError("MFMA latency hazards in the device code:\n" +
+                           "\n".join("%s %s: %s -> %s" % f for f in findings[:20]))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

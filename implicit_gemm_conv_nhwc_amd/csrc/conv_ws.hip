@@ -28,7 +28,7 @@
 //    pixel; four stage buffers, filled three stages ahead, so a patch has
 //    two stages (~2 us) to arrive. Each fragment read from LDS feeds every
 //    (output row, tap row) pair that uses it;
-//  * the finished tile (oscale, bias applied) is staged in LDS and leaves
+//  * the finished tile's sums are staged in LDS and leave (oscale, bias)
 //    during the next tile's stages, one row per stage: its stores (and,
 //    when accumulating, the loads of the stream it adds to, issued a stage
 //    ahead) overlap the next tile's MFMAs instead of following them. The
@@ -100,15 +100,22 @@ __device__ __forceinline__ i32x4 srd(const void *base, uint32_t bytes)
 // A 16-byte-per-lane direct-to-LDS buffer load as asm: the kernel orders
 // these loads itself (the wait at each stage's start), so the compiler must
 // not see them -- as builtins, every LDS read after one would wait for it.
-__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds_addr, uint32_t voff)
+// voff + soff is the source byte offset (voff alone decides whether it is
+// in range: the stage's channel offset goes in soff); M0 is the LDS
+// address, set here and left clobbered.
+// (M0 is a reserved register: clang warns about the clobber. No code the
+// compiler emits in these kernels reads M0; the build's ISA scan checks.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds_addr, uint32_t voff, int soff)
 {
-    unsigned saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
-                 : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // 16-byte buffer load into registers, also hidden from the compiler's wait
 // tracking (the stage-start wait covers it)
@@ -135,12 +142,20 @@ __device__ __forceinline__ void st8(i32x4 rsrc, uint32_t voff, half4v v)
     asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 0" ::"v"(v), "v"(voff), "s"(rsrc) : "memory");
 }
 
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima) as a
+// builtin: the compiler sees it and drops its own later LDS waits.
+__device__ __forceinline__ void lgkm_wait0()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
 // A workgroup barrier after this wave's LDS operations have completed. No
 // wait for vector memory: the stage loop orders its loads itself (the
 // fence of __syncthreads would drain the prefetched stages).
 __device__ __forceinline__ void lds_barrier()
 {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    lgkm_wait0();
+    __builtin_amdgcn_s_barrier();
 }
 
 // The MFMAs: acc += W.B with the weight fragment in an AGPR ("a") or a
@@ -155,8 +170,10 @@ template <bool AG>
 __device__ __forceinline__ void mma(f32x16 &acc, const half8 &w, const half8 &b, int kind)
 {
     if (kind == 0) {
-        if (AG) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "a"(w), "v"(b));
-        else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(w), "v"(b));
+        // tied like the others: an accumulator keeps its registers from tile
+        // to tile, so the compiler has no reason to move one
+        if (AG) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "+v"(acc) : "a"(w), "v"(b));
+        else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "+v"(acc) : "v"(w), "v"(b));
     } else if (kind == 1) {
         if (AG) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "a"(w), "v"(b));
         else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(w), "v"(b));
@@ -202,6 +219,16 @@ constexpr Triple<MODE> group_triple(int i)
     return Triple<MODE>{-1, -1, -1};
 }
 
+// the position in a group of output row r's MFMA at tap row 2 (in the
+// last group of the last stage, the row's final MFMA)
+template <int MODE>
+constexpr int group_last(int r)
+{
+    for (int i = 0; i < 3 * TH; ++i)
+        if (group_triple<MODE>(i).r == r && group_triple<MODE>(i).dy == 2) return i;
+    return -1;
+}
+
 struct WTile {
     int y0, x0;
     uint32_t aoff[4];  // per patch load of this lane: source byte offset at stage 0 (kOOB: zeros)
@@ -243,7 +270,7 @@ void k_conv_ws(IgemmArgs p)
 {
     using G = WGeo<MODE>;
     constexpr int PH = G::PH, PW = G::PW;
-    constexpr int A_INSTR = G::A_INSTR, A_PAD = G::A_PAD, APW = G::APW;
+    constexpr int A_PAD = G::A_PAD, APW = G::APW;
     static_assert(APW <= 4, "patch loads per lane");
     static_assert(NST == 4 && TH == 4, "the drain schedule covers 4 rows over 4 stages");
     static_assert(NBUF == NST, "stage s lands in buffer s");
@@ -257,7 +284,6 @@ void k_conv_ws(IgemmArgs p)
     constexpr int WAIT1 = ACC ? OPS_ROW : 2 * OPS_ROW + APW;    // stream row 2, then row 1's stores
     constexpr int WAIT2 = ACC ? OPS_ROW : OPS_ROW + APW;        // stream row 3, then row 2's stores
     constexpr int WAIT3 = OPS_ROW + 2 * OPS_L + APW;            // nothing of the drain
-    static_assert(WAIT3 < 64 && WAIT1 < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(16))) u32x4 lds[ws_lds_bytes<MODE>() / 16];
     float *stg = reinterpret_cast<float *>(lds + NBUF * A_PAD);  // [TH][TW][SP]
@@ -320,8 +346,7 @@ void k_conv_ws(IgemmArgs p)
     // past the patch read zeros into the buffer's padding)
     auto issue_one = [&](const WTile &tl, int st, int buf, int k) __attribute__((always_inline)) {
         const int ii = wave + NW * k;
-        const uint32_t off = tl.aoff[k] == kOOB ? kOOB : tl.aoff[k] + st * CK * 2;
-        dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, ii < A_INSTR ? off : kOOB);
+        dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, tl.aoff[k], st * CK * 2);
     };
 
     // the wave's weights: fragment f = (2 s + ks) 9 + tap = output channel
@@ -339,6 +364,7 @@ void k_conv_ws(IgemmArgs p)
     }
 
     const float osc = p.oscale;
+    f32x4 bq = {};  // the bias of the f32 drain's channels (read after the first barrier)
 
     // The drain. A staged row is 32 pixels x 32 float4. f32 passes: in
     // pass k thread tid takes float4 tid + 256 k (pixel 8 k + tid / 32,
@@ -347,64 +373,95 @@ void k_conv_ws(IgemmArgs p)
     // 16 h + tid / 16, channels 8 (tid % 16) .. + 7, a pixel per DPP row.
     const int dpx = tid >> 5, dc = (tid & 31) * 4;
     const int npx = tid >> 4, nc = (tid & 15) * 8;
-    int sy0 = 0, sx0 = 0;  // the staged tile
-    bool staged = false;
     // a row's values in flight: the stream values it adds to (loaded a stage
     // ahead), then the row's results; even rows in xa, odd rows in xb
     f32x4 xa[4] = {}, xb[4] = {};
-    // byte offset of (row r of a tile at y0, pixel x0 + px, channel c) in an
-    // output of esz-byte elements with row pitch ld, relative to row y0;
-    // kOOB outside the output or when !live
-    auto doff = [&](bool live, int y0, int x0, int r, int px, int c, int ld, int esz) __attribute__((always_inline)) {
-        const int oy = y0 + r, ox = x0 + px;
-        return (live && oy < Hout && ox < Wout) ? (uint32_t)(((r * Wout + ox) * ld + c) * esz) : kOOB;
-    };
-    // descriptors over the output rows from tile row y0 on (offsets inside a
-    // tile stay below 4 rows; past the last row they fall outside)
-    auto out_srd = [&](const void *base, int y0, int ld, int esz) __attribute__((always_inline)) {
+    // descriptors over the output rows from tile row y0 on, num_records
+    // capped at lim (offsets inside a tile stay below 4 rows; past the last
+    // row they fall outside)
+    auto out_srd = [&](const void *base, int y0, int ld, int esz, uint32_t lim) __attribute__((always_inline)) {
         const int64_t rem = (int64_t)(Hout - y0) * Wout * ld * esz;
         return srd(reinterpret_cast<const char *>(base) + (int64_t)y0 * Wout * ld * esz,
-                   (uint32_t)(rem < (int64_t)kOOB ? rem : (int64_t)kOOB));
+                   (uint32_t)(rem < (int64_t)lim ? rem : (int64_t)lim));
     };
-    // item L: the stream values of row r of the tile at (y0, x0) into x
-    auto item_load = [&](f32x4 (&x)[4], bool live, int y0, int x0, int r) __attribute__((always_inline)) {
-        if constexpr (ACC) {
-            const i32x4 rs = out_srd(p.c, y0, p.ldc, 4);
+    // Where a tile's outputs go, set once per tile: per lane, the byte
+    // offset in the tile's first row of the f32 drain's pixels (f[k]: pixel
+    // 8 k + dpx, channel dc; kOOB past the right edge or for no tile) and of
+    // the norm's (n[h]: pixel 16 h + npx, channel nc, f16 rows of BN); the
+    // descriptors from the tile's first row on. Row r adds r row pitches;
+    // the guarded cast's offsets are f[k] / 2 under a descriptor capped at
+    // kOOB / 2, so kOOB / 2 stays out of range too.
+    struct OutPos {
+        uint32_t f[4], n[2];
+        i32x4 rc, ry, rn;
+    };
+    const uint32_t rowc = (uint32_t)Wout * p.ldc * 4, rowy = rowc / 2, rown = (uint32_t)Wout * BN * 2;
+    auto make_out = [&](bool live, int y0, int x0) __attribute__((always_inline)) {
+        OutPos o;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) x[k] = ld16(rs, doff(live, y0, x0, r, 8 * k + dpx, dc, p.ldc, 4));
+        for (int k = 0; k < 4; ++k) {
+            const int ox = x0 + 8 * k + dpx;
+            o.f[k] = (live && ox < Wout) ? (uint32_t)((ox * p.ldc + dc) * 4) : kOOB;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ox = x0 + 16 * h + npx;
+            o.n[h] = (live && ox < Wout) ? (uint32_t)((ox * BN + nc) * 2) : kOOB;
+        }
+        if constexpr (WOUT || ACC) o.rc = out_srd(p.c, y0, p.ldc, 4, kOOB);
+        if constexpr (YG) o.ry = out_srd(p.yg, y0, p.ldc, 2, kOOB / 2);
+        if constexpr (NORM) o.rn = out_srd(p.ny, y0, BN, 2, kOOB);
+        return o;
+    };
+    OutPos spos = make_out(false, 0, 0);  // the staged tile's
+    OutPos cpos = spos;                   // this tile's (from its stage 3 on)
+    // item L: the stream values of row r of the tile at o into x
+    auto item_load = [&](f32x4 (&x)[4], const OutPos &o, int r) __attribute__((always_inline)) {
+        if constexpr (ACC) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = ld16(o.rc, o.f[k] + r * rowc);
         }
     };
-    // item A: row r's staged results (plus the stream values) into x
+    // item A: row r's staged sums, scaled and biased (plus the stream
+    // values), into x
     auto item_read = [&](f32x4 (&x)[4], int r) __attribute__((always_inline)) {
         if constexpr (WOUT || YG) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + (r * TW + 8 * k + dpx) * SP + dc);
-                if constexpr (ACC) x[k] += v;
-                else x[k] = v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float o = __builtin_fmaf(osc, v[e], bq[e]);
+                    if constexpr (ACC) x[k][e] += o;
+                    else x[k][e] = o;
+                }
             }
         }
     };
-    // item S: pass k of row r's f32 and guarded-cast stores
-    auto item_store = [&](const f32x4 (&x)[4], bool live, int r, int k) __attribute__((always_inline)) {
-        if constexpr (WOUT) {
-            const i32x4 rs = out_srd(p.c, sy0, p.ldc, 4);
-            st16(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 4), x[k], true);
-        }
+    // item S: pass k of row r's f32 and guarded-cast stores (staged tile)
+    auto item_store = [&](const f32x4 (&x)[4], int r, int k) __attribute__((always_inline)) {
+        if constexpr (WOUT) st16(spos.rc, spos.f[k] + r * rowc, x[k], true);
         if constexpr (YG) {
-            const i32x4 rs = out_srd(p.yg, sy0, p.ldc, 2);
             half4v h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) h[e] = (_Float16)(x[k][e] * p.gscale);
-            st8(rs, doff(live, sy0, sx0, r, 8 * k + dpx, dc, p.ldc, 2), h);
+            st8(spos.ry, (spos.f[k] >> 1) + r * rowy, h);
         }
     };
-    // item N: pass h of row r's RMS_norm (+ SiLU), f16
-    auto item_norm = [&](bool live, int r, int h) __attribute__((always_inline)) {
+    // item N: pass h of row r's RMS_norm (+ SiLU), f16 (staged tile)
+    auto item_norm = [&](int r, int h) __attribute__((always_inline)) {
         if constexpr (NORM) {
             const float *sv = stg + (r * TW + 16 * h + npx) * SP + nc;
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(sv);
-            const f32x4 b = *reinterpret_cast<const f32x4 *>(sv + 4);
+            const f32x4 sa = *reinterpret_cast<const f32x4 *>(sv);
+            const f32x4 sb = *reinterpret_cast<const f32x4 *>(sv + 4);
+            const f32x4 ba = *reinterpret_cast<const f32x4 *>(sbias + nc);
+            const f32x4 bb = *reinterpret_cast<const f32x4 *>(sbias + nc + 4);
+            f32x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = __builtin_fmaf(osc, sa[e], ba[e]);
+                b[e] = __builtin_fmaf(osc, sb[e], bb[e]);
+            }
             float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] +
                        b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
             ss = row16_sum(ss);
@@ -420,31 +477,45 @@ void k_conv_ws(IgemmArgs p)
                 const float ex = silu ? __expf(-y) : 0.f;
                 o[e] = (_Float16)(y * __builtin_amdgcn_rcpf(1.0f + ex));
             }
-            const i32x4 rs = out_srd(p.ny, sy0, BN, 2);
-            st16(rs, doff(live, sy0, sx0, r, 16 * h + npx, nc, BN, 2), __builtin_bit_cast(f32x4, o), false);
+            st16(spos.rn, spos.n[h] + r * rown, __builtin_bit_cast(f32x4, o), false);
+        }
+    };
+    // stage accumulator row r (the raw sums): lane l holds pixel fx,
+    // channels 32 wave + 8 k + 4 fh .. + 3
+    auto stage_row = [&](const f32x16 &a, int r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ch = 32 * wave + 8 * k + 4 * fh;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = a[4 * k + e];
+            *reinterpret_cast<f32x4 *>(stg + (r * TW + fx) * SP + ch) = v;
         }
     };
     // a whole drained row (the end of the kernel)
     auto drain_row = [&](f32x4 (&x)[4], int r) __attribute__((always_inline)) {
         item_read(x, r);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) item_store(x, true, r, k);
-        item_norm(true, r, 0);
-        item_norm(true, r, 1);
+        for (int k = 0; k < 4; ++k) item_store(x, r, k);
+        item_norm(r, 0);
+        item_norm(r, 1);
     };
     // the wait: all but the last n vector-memory operations have landed (and,
     // after the barrier, every wave's); the stream values are ready
     auto wait_n = [&](auto n) __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%8)"
-                     : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]), "+v"(xb[2]),
-                       "+v"(xb[3])
-                     : "n"(decltype(n)::value)
-                     : "memory");
+        if constexpr (ACC)
+            asm volatile("s_waitcnt vmcnt(%8)"
+                         : "+v"(xa[0]), "+v"(xa[1]), "+v"(xa[2]), "+v"(xa[3]), "+v"(xb[0]), "+v"(xb[1]), "+v"(xb[2]),
+                           "+v"(xb[3])
+                         : "n"(decltype(n)::value)
+                         : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n)::value) : "memory");
         lds_barrier();
     };
 
     WTile cur = make_tile(t);
-    WTile nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
+    WTile nxt = cur;  // set in each tile's stage 0, before its first use
     // the first tile's four patches, with placeholder stream loads where a
     // tile's rows 0 and 1 would be loaded, so the first waits count as the
     // later ones
@@ -452,11 +523,16 @@ void k_conv_ws(IgemmArgs p)
     for (int st = 0; st < 3; ++st)
 #pragma unroll
         for (int k = 0; k < APW; ++k) issue_one(cur, st, st, k);
-    item_load(xa, false, 0, 0, 0);
-    item_load(xb, false, 0, 0, 1);
+    item_load(xa, spos, 0);
+    item_load(xb, spos, 1);
 #pragma unroll
     for (int k = 0; k < APW; ++k) issue_one(cur, NST - 1, NST - 1, k);
+    // a wait the compiler sees: the weight loads are not outstanding in the
+    // loop (else it would wait for the stores and patch loads in flight
+    // before each MFMA that reads a late weight)
+    __builtin_amdgcn_s_waitcnt(0);
     wait_n(std::integral_constant<int, 3 * APW + 2 * OPS_L>{});
+    if constexpr (WOUT || YG) bq = *reinterpret_cast<const f32x4 *>(sbias + dc);
 
     // fragment groups (K-step ks, tap column dx) g = 3 ks + dx; group g's
     // PH patch-row fragments live in bf[g & 1]
@@ -471,8 +547,8 @@ void k_conv_ws(IgemmArgs p)
     };
     load_group(lds, 0, bf[0]);
 
+    f32x16 acc[TH];
     for (;;) {
-        f32x16 acc[TH];
         // one stage; st is a compile-time constant (the weight fragments are
         // indexed by it and must stay in registers)
         auto run_stage = [&](auto stc) __attribute__((always_inline)) {
@@ -484,27 +560,38 @@ void k_conv_ws(IgemmArgs p)
                 if constexpr (st == 1) {
                     if constexpr (i == 0) item_read(xa, 0);
                     if constexpr (i == 2) item_read(xb, 1);
-                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, staged, 0, (i - 4) / 4);
-                    if constexpr (i == 20) item_load(xa, staged, sy0, sx0, 2);
-                    if constexpr (i >= 24 && i < 40 && i % 4 == 0) item_store(xb, staged, 1, (i - 24) / 4);
-                    if constexpr (i == 6) item_norm(staged, 0, 0);
-                    if constexpr (i == 18) item_norm(staged, 0, 1);
-                    if constexpr (i == 30) item_norm(staged, 1, 0);
-                    if constexpr (i == 42) item_norm(staged, 1, 1);
+                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, 0, (i - 4) / 4);
+                    if constexpr (i == 20) item_load(xa, spos, 2);
+                    if constexpr (i >= 24 && i < 40 && i % 4 == 0) item_store(xb, 1, (i - 24) / 4);
+                    if constexpr (i == 6) item_norm(0, 0);
+                    if constexpr (i == 18) item_norm(0, 1);
+                    if constexpr (i == 30) item_norm(1, 0);
+                    if constexpr (i == 42) item_norm(1, 1);
                 } else if constexpr (st == 2) {
                     if constexpr (i == 0) item_read(xa, 2);
-                    if constexpr (i == 2) item_load(xb, staged, sy0, sx0, 3);
-                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, staged, 2, (i - 4) / 4);
-                    if constexpr (i == 6) item_norm(staged, 2, 0);
-                    if constexpr (i == 18) item_norm(staged, 2, 1);
+                    if constexpr (i == 2) item_load(xb, spos, 3);
+                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, 2, (i - 4) / 4);
+                    if constexpr (i == 6) item_norm(2, 0);
+                    if constexpr (i == 18) item_norm(2, 1);
                 } else if constexpr (st == 3) {
                     if constexpr (i == 0) item_read(xb, 3);
-                    if constexpr (i == 2) item_load(xa, true, cur.y0, cur.x0, 0);
-                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xb, staged, 3, (i - 4) / 4);
-                    if constexpr (i == 20) item_load(xb, true, cur.y0, cur.x0, 1);
-                    if constexpr (i == 6) item_norm(staged, 3, 0);
-                    if constexpr (i == 18) item_norm(staged, 3, 1);
+                    if constexpr (i == 1) cpos = make_out(true, cur.y0, cur.x0);
+                    if constexpr (i == 2) item_load(xa, cpos, 0);
+                    if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xb, 3, (i - 4) / 4);
+                    if constexpr (i == 20) item_load(xb, cpos, 1);
+                    if constexpr (i == 6) item_norm(3, 0);
+                    if constexpr (i == 18) item_norm(3, 1);
                 }
+                // the next tile, well before its first patch load
+                if constexpr (st == 0 && i == 24) nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
+                // the rows whose last MFMA has run, into the staging area
+                // (the staged tile before was read before this stage's barrier)
+                if constexpr (st == NST - 1 && i == 61 + group_last<MODE>(0)) stage_row(acc[0], 0);
+                if constexpr (st == NST - 1 && i == 61 + group_last<MODE>(1)) stage_row(acc[1], 1);
+                // rows 2 and 3 of the tile before (garbage in the first
+                // tile: no drain writes it), before their first MFMAs here
+                if constexpr (st == 0 && i == 0) stage_row(acc[2], 2);
+                if constexpr (st == 0 && i == 1) stage_row(acc[3], 3);
                 // after the barrier: the next tile's patch for this stage's buffer
                 if constexpr (i >= 60 && i < 60 + APW) issue_one(nxt, st, st, i - 60);
             };
@@ -520,6 +607,9 @@ void k_conv_ws(IgemmArgs p)
                     else wait_n(std::integral_constant<int, WAIT3>{});
                     load_group(lds + ((st + 1) % NBUF) * A_PAD, 0, bf[0]);
                 } else {
+                    // one wait per group: this group's fragments (loaded a
+                    // group ago) and the items' LDS accesses have landed
+                    lgkm_wait0();
                     load_group(sA, g + 1, bf[(g + 1) & 1]);
                 }
                 constexpr int ks = g / 3, dx = g % 3;
@@ -539,34 +629,23 @@ void k_conv_ws(IgemmArgs p)
             });
         };
         static_for<NST>(run_stage);
-        // stage the tile (oscale, bias): lane l holds pixel fx, channels
-        // 32 wave + 8 k + 4 fh .. + 3. The staged tile before it was drained
-        // before the last barrier; this one is read after the next.
-#pragma unroll
-        for (int r = 0; r < TH; ++r)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int ch = 32 * wave + 8 * k + 4 * fh;
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sbias + ch);
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = osc * acc[r][4 * k + e] + b4[e];
-                *reinterpret_cast<f32x4 *>(stg + (r * TW + fx) * SP + ch) = v;
-            }
-        sy0 = cur.y0;
-        sx0 = cur.x0;
-        staged = true;
+        static_assert(group_last<MODE>(1) < 3 * TH - 2, "rows 0 and 1 finish early");
+        static_assert(group_triple<MODE>(0).r != 2 && group_triple<MODE>(0).r != 3 && group_triple<MODE>(1).r != 2 &&
+                          group_triple<MODE>(1).r != 3 && group_triple<MODE>(2).r != 3,
+                      "rows 2 and 3 start after their staging");
+        spos = cpos;
         t += t_step;
         if (t >= t_end) break;
         cur = nxt;
-        nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
     }
     // the last tile's rows (the stream values of rows 0 and 1 are loading)
+    stage_row(acc[2], 2);
+    stage_row(acc[3], 3);
     wait_n(std::integral_constant<int, 0>{});
     drain_row(xa, 0);
     drain_row(xb, 1);
-    item_load(xa, true, sy0, sx0, 2);
-    item_load(xb, true, sy0, sx0, 3);
+    item_load(xa, spos, 2);
+    item_load(xb, spos, 3);
     wait_n(std::integral_constant<int, 0>{});
     drain_row(xa, 2);
     drain_row(xb, 3);
