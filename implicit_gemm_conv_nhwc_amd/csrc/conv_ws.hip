@@ -219,14 +219,14 @@ constexpr Triple<MODE> group_triple(int i)
     return Triple<MODE>{-1, -1, -1};
 }
 
-// the position in a group of output row r's MFMA at tap row 2 (in the
-// last group of the last stage, the row's final MFMA)
+// The last group of the last stage runs row by row instead: row r's three
+// MFMAs are 3 r .. 3 r + 2, so the rows finish one after another and their
+// staging spreads over the group's slots.
 template <int MODE>
-constexpr int group_last(int r)
+constexpr Triple<MODE> last_triple(int i)
 {
-    for (int i = 0; i < 3 * TH; ++i)
-        if (group_triple<MODE>(i).r == r && group_triple<MODE>(i).dy == 2) return i;
-    return -1;
+    const int r = i / 3, dy = i % 3;
+    return Triple<MODE>{r, dy, WGeo<MODE>::arow(r, dy)};
 }
 
 struct WTile {
@@ -323,6 +323,25 @@ void k_conv_ws(IgemmArgs p)
     const unsigned lds_base = (unsigned)(uintptr_t)lds;
 
     // a tile's patch sources; tt < 0: no tile (every load reads zeros)
+    // patch load k of this lane: unit u = (wave + 4 k) 64 + lane of the
+    // patch, pixel u / 4 (row pr, column pc), stored quarter u % 4
+    auto unit = [&](int k, int &pr, int &pc, int &q) __attribute__((always_inline)) {
+        const int u = (wave + NW * k) * 64 + lane;
+        const int pix = u >> 2;
+        pr = pix / PW;
+        pc = pix - pr * PW;
+        q = (u & 3) ^ ((pc >> 2) & 3);  // stored quarter -> channel quarter
+        return (k < APW) & (u < G::A_UNITS);
+    };
+    // its byte offset from the patch origin (the same for every tile; kOOB
+    // past the patch)
+    uint32_t prel[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int pr, pc, q;
+        const bool in = unit(k, pr, pc, q);
+        prel[k] = in ? (uint32_t)(((pr * W + pc) * cin_p + q * 8) * 2) : kOOB;
+    }
     auto make_tile = [&](int tt) __attribute__((always_inline)) {
         WTile r;
         const int tv = tt < 0 ? 0 : tt;
@@ -330,15 +349,21 @@ void k_conv_ws(IgemmArgs p)
         r.x0 = (tv % tiles_x) * TW;
         const int py0 = (MODE == kConv3x3) ? r.y0 - 1 : r.y0 / 2 - 1;
         const int px0 = (MODE == kConv3x3) ? r.x0 - 1 : r.x0 / 2 - 1;
+        if (tt >= 0 && py0 >= 0 && px0 >= 0 && py0 + PH <= H && px0 + PW <= W) {
+            // inside the image: one add per load (the input is below 2 GB,
+            // so base + kOOB neither wraps nor comes back in range)
+            const uint32_t base = (uint32_t)((py0 * W + px0) * cin_p * 2);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int u = (wave + NW * k) * 64 + lane;
-            const int pix = u >> 2;
-            const int pr = pix / PW, pc = pix - (pix / PW) * PW;
-            const int q = (u & 3) ^ ((pc >> 2) & 3);  // stored quarter -> channel quarter
-            const int sy = py0 + pr, sx = px0 + pc;
-            const bool ok = (tt >= 0) & (k < APW) & (u < G::A_UNITS) & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
-            r.aoff[k] = ok ? (uint32_t)(((sy * W + sx) * cin_p + q * 8) * 2) : kOOB;
+            for (int k = 0; k < 4; ++k) r.aoff[k] = base + prel[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                int pr, pc, q;
+                const bool in = unit(k, pr, pc, q);
+                const int sy = py0 + pr, sx = px0 + pc;
+                const bool ok = (tt >= 0) & in & (sy >= 0) & (sy < H) & (sx >= 0) & (sx < W);
+                r.aoff[k] = ok ? (uint32_t)(((sy * W + sx) * cin_p + q * 8) * 2) : kOOB;
+            }
         }
         return r;
     };
@@ -351,16 +376,16 @@ void k_conv_ws(IgemmArgs p)
 
     // the wave's weights: fragment f = (2 s + ks) 9 + tap = output channel
     // 32 wave + fx, input channels 16 (2 s + ks) + 8 fh .. + 7 of the
-    // [cin_p/16][9][cout_p][16] plane
+    // [cin_p/16][9][cout_p][16] plane. Stage 0's 18 load in the prologue,
+    // stage s + 1's during the first tile's stage s.
     half8 wr[NST * 2 * 9];
-    {
-        const half8 *wp = reinterpret_cast<const half8 *>(p.b) + (32 * wave + fx) * 2 + fh;
-#pragma unroll
-        for (int f = 0; f < NST * 2 * 9; ++f) wr[f] = wp[f * BN * 2];
-    }
+    const half8 *wp = reinterpret_cast<const half8 *>(p.b) + (32 * wave + fx) * 2 + fh;
+    // the bias and the norm's gain: into registers now, into LDS after the
+    // first wait
+    float bias_v = 0.f, gam_v = 0.f;
     if (tid < BN) {
-        sbias[tid] = p.bias ? p.bias[tid] : 0.f;
-        sgam[tid] = NORM ? p.ngamma[tid] : 0.f;
+        bias_v = p.bias ? p.bias[tid] : 0.f;
+        gam_v = NORM ? p.ngamma[tid] : 0.f;
     }
 
     const float osc = p.oscale;
@@ -480,17 +505,14 @@ void k_conv_ws(IgemmArgs p)
             st16(spos.rn, spos.n[h] + r * rown, __builtin_bit_cast(f32x4, o), false);
         }
     };
-    // stage accumulator row r (the raw sums): lane l holds pixel fx,
-    // channels 32 wave + 8 k + 4 fh .. + 3
-    auto stage_row = [&](const f32x16 &a, int r) __attribute__((always_inline)) {
+    // stage part k of accumulator row r (the raw sums): lane l holds
+    // pixel fx, channels 32 wave + 8 k + 4 fh .. + 3
+    auto stage_part = [&](const f32x16 &a, int r, int k) __attribute__((always_inline)) {
+        const int ch = 32 * wave + 8 * k + 4 * fh;
+        f32x4 v;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int ch = 32 * wave + 8 * k + 4 * fh;
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = a[4 * k + e];
-            *reinterpret_cast<f32x4 *>(stg + (r * TW + fx) * SP + ch) = v;
-        }
+        for (int e = 0; e < 4; ++e) v[e] = a[4 * k + e];
+        *reinterpret_cast<f32x4 *>(stg + (r * TW + fx) * SP + ch) = v;
     };
     // a whole drained row (the end of the kernel)
     auto drain_row = [&](f32x4 (&x)[4], int r) __attribute__((always_inline)) {
@@ -516,22 +538,28 @@ void k_conv_ws(IgemmArgs p)
 
     WTile cur = make_tile(t);
     WTile nxt = cur;  // set in each tile's stage 0, before its first use
-    // the first tile's four patches, with placeholder stream loads where a
-    // tile's rows 0 and 1 would be loaded, so the first waits count as the
-    // later ones
+    // the first tile's four patches (stage 0's weights after the first),
+    // with placeholder stream loads where a tile's rows 0 and 1 would be
+    // loaded, so the first waits count as the later ones
 #pragma unroll
-    for (int st = 0; st < 3; ++st)
+    for (int k = 0; k < APW; ++k) issue_one(cur, 0, 0, k);
+#pragma unroll
+    for (int f = 0; f < 18; ++f) wr[f] = wp[f * BN * 2];
+#pragma unroll
+    for (int st = 1; st < 3; ++st)
 #pragma unroll
         for (int k = 0; k < APW; ++k) issue_one(cur, st, st, k);
     item_load(xa, spos, 0);
     item_load(xb, spos, 1);
 #pragma unroll
     for (int k = 0; k < APW; ++k) issue_one(cur, NST - 1, NST - 1, k);
-    // a wait the compiler sees: the weight loads are not outstanding in the
-    // loop (else it would wait for the stores and patch loads in flight
-    // before each MFMA that reads a late weight)
-    __builtin_amdgcn_s_waitcnt(0);
-    wait_n(std::integral_constant<int, 3 * APW + 2 * OPS_L>{});
+    static_assert(18 + 3 * APW + 2 * OPS_L < 64, "vmcnt range");
+    wait_n(std::integral_constant<int, 18 + 3 * APW + 2 * OPS_L>{});
+    if (tid < BN) {
+        sbias[tid] = bias_v;
+        sgam[tid] = gam_v;
+    }
+    lds_barrier();
     if constexpr (WOUT || YG) bq = *reinterpret_cast<const f32x4 *>(sbias + dc);
 
     // fragment groups (K-step ks, tap column dx) g = 3 ks + dx; group g's
@@ -548,7 +576,11 @@ void k_conv_ws(IgemmArgs p)
     load_group(lds, 0, bf[0]);
 
     f32x16 acc[TH];
-    for (;;) {
+    // one tile; the first (FIRST) also loads the weights of stages 1-3, so
+    // every wait the compiler places for them falls in this copy and none
+    // in the loop
+    auto run_tile = [&](auto firstc) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(firstc)::value;
         // one stage; st is a compile-time constant (the weight fragments are
         // indexed by it and must stay in registers)
         auto run_stage = [&](auto stc) __attribute__((always_inline)) {
@@ -582,16 +614,27 @@ void k_conv_ws(IgemmArgs p)
                     if constexpr (i == 6) item_norm(3, 0);
                     if constexpr (i == 18) item_norm(3, 1);
                 }
+                // the next stage's weights, in the first tile
+                if constexpr (FIRST && st < NST - 1 && i < 36 && i % 2 == 0)
+                    wr[(st + 1) * 18 + i / 2] = wp[((st + 1) * 18 + i / 2) * BN * 2];
                 // the next tile, well before its first patch load
                 if constexpr (st == 0 && i == 24) nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
                 // the rows whose last MFMA has run, into the staging area
                 // (the staged tile before was read before this stage's barrier)
-                if constexpr (st == NST - 1 && i == 61 + group_last<MODE>(0)) stage_row(acc[0], 0);
-                if constexpr (st == NST - 1 && i == 61 + group_last<MODE>(1)) stage_row(acc[1], 1);
-                // rows 2 and 3 of the tile before (garbage in the first
-                // tile: no drain writes it), before their first MFMAs here
-                if constexpr (st == 0 && i == 0) stage_row(acc[2], 2);
-                if constexpr (st == 0 && i == 1) stage_row(acc[3], 3);
+                // this tile's rows into the staging area, one part per slot
+                // from each row's last MFMA (slot 62 + 3 r of the last stage)
+                // on; the rest in the next tile's first slots, before the
+                // rows' first MFMAs there (the first tile's are garbage: no
+                // drain reads them). The staged tile before was read before
+                // this stage's barrier.
+                // (part k of row r at slot 63 + 3 r + k, counted on into the
+                // next tile: d = 3 r + k)
+                constexpr int d = (st == NST - 1) ? i - 63 : (st == 0 ? i + 9 : -1);
+                if constexpr (d >= 0 && d <= 3 * TH && (st == NST - 1 || d >= 9)) {
+                    constexpr int r1 = d / 3, k1 = d % 3;
+                    if constexpr (r1 < TH) stage_part(acc[r1], r1, k1);
+                    if constexpr (k1 == 0 && r1 >= 1) stage_part(acc[r1 - 1], r1 - 1, 3);
+                }
                 // after the barrier: the next tile's patch for this stage's buffer
                 if constexpr (i >= 60 && i < 60 + APW) issue_one(nxt, st, st, i - 60);
             };
@@ -615,7 +658,7 @@ void k_conv_ws(IgemmArgs p)
                 constexpr int ks = g / 3, dx = g % 3;
                 static_for<3 * TH>([&](auto ic) __attribute__((always_inline)) {
                     constexpr int i = decltype(ic)::value;
-                    constexpr Triple<MODE> tr = group_triple<MODE>(i);
+                    constexpr Triple<MODE> tr = (st == NST - 1 && g == 5) ? last_triple<MODE>(i) : group_triple<MODE>(i);
                     static_assert(tr.r >= 0, "a group has 3 TH MFMAs");
                     constexpr int f = (2 * st + ks) * 9 + tr.dy * 3 + dx;
                     // the first and last MFMA of each accumulator's chain
@@ -629,18 +672,22 @@ void k_conv_ws(IgemmArgs p)
             });
         };
         static_for<NST>(run_stage);
-        static_assert(group_last<MODE>(1) < 3 * TH - 2, "rows 0 and 1 finish early");
-        static_assert(group_triple<MODE>(0).r != 2 && group_triple<MODE>(0).r != 3 && group_triple<MODE>(1).r != 2 &&
-                          group_triple<MODE>(1).r != 3 && group_triple<MODE>(2).r != 3,
+        static_assert(last_triple<MODE>(3 * TH - 1).r == TH - 1 && last_triple<MODE>(3 * TH - 1).dy == 2, "row by row");
+        static_assert(group_triple<MODE>(0).r != 2 && group_triple<MODE>(0).r != 3 && group_triple<MODE>(1).r != 3 &&
+                          group_triple<MODE>(2).r != 3 && group_triple<MODE>(3).r != 3,
                       "rows 2 and 3 start after their staging");
         spos = cpos;
         t += t_step;
-        if (t >= t_end) break;
+    };
+    run_tile(std::true_type{});
+    while (t < t_end) {
         cur = nxt;
+        run_tile(std::false_type{});
     }
     // the last tile's rows (the stream values of rows 0 and 1 are loading)
-    stage_row(acc[2], 2);
-    stage_row(acc[3], 3);
+    stage_part(acc[2], 2, 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) stage_part(acc[3], 3, k);
     wait_n(std::integral_constant<int, 0>{});
     drain_row(xa, 0);
     drain_row(xb, 1);
