@@ -473,37 +473,60 @@ void k_conv_ws(IgemmArgs p)
             st8(spos.ry, (spos.f[k] >> 1) + r * rowy, h);
         }
     };
-    // item N: pass h of row r's RMS_norm (+ SiLU), f16 (staged tile)
-    auto item_norm = [&](int r, int h) __attribute__((always_inline)) {
+    // The norm: pass h of row r, in 11 steps (one per MFMA slot), over the
+    // staged tile. One pass is in flight at a time: its values (then y), the
+    // sum of squares (then the scale), the exp terms, the f16 results.
+    f32x4 nbl = {}, nbh = {}, ngl = {}, ngh = {};  // this thread's bias, gain (channels nc .. + 7)
+    f32x4 nva, nvb, nea, neb;
+    float nss;
+    half8 nout;
+    const float nrt = sqrtf((float)p.norm_c), ninv_eps = 1.0f / p.norm_eps;
+    auto norm_step = [&](int r, int h, auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
         if constexpr (NORM) {
-            const float *sv = stg + (r * TW + 16 * h + npx) * SP + nc;
-            const f32x4 sa = *reinterpret_cast<const f32x4 *>(sv);
-            const f32x4 sb = *reinterpret_cast<const f32x4 *>(sv + 4);
-            const f32x4 ba = *reinterpret_cast<const f32x4 *>(sbias + nc);
-            const f32x4 bb = *reinterpret_cast<const f32x4 *>(sbias + nc + 4);
-            f32x4 a, b;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[e] = __builtin_fmaf(osc, sa[e], ba[e]);
-                b[e] = __builtin_fmaf(osc, sb[e], bb[e]);
-            }
-            float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3] +
-                       b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
-            ss = row16_sum(ss);
-            const float inv = sqrtf((float)p.norm_c) / fmaxf(sqrtf(ss), p.norm_eps);
-            const f32x4 ga = *reinterpret_cast<const f32x4 *>(sgam + nc);
-            const f32x4 gb = *reinterpret_cast<const f32x4 *>(sgam + nc + 4);
             const bool silu = p.norm_silu != 0;
-            half8 o;
+            if constexpr (m == 0) {
+                const float *sv = stg + (r * TW + 16 * h + npx) * SP + nc;
+                nva = *reinterpret_cast<const f32x4 *>(sv);
+                nvb = *reinterpret_cast<const f32x4 *>(sv + 4);
+            } else if constexpr (m == 1) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = (e < 4 ? a[e] * ga[e] : b[e - 4] * gb[e - 4]) * inv;
+                for (int e = 0; e < 4; ++e) {
+                    nva[e] = __builtin_fmaf(osc, nva[e], nbl[e]);
+                    nvb[e] = __builtin_fmaf(osc, nvb[e], nbh[e]);
+                }
+            } else if constexpr (m == 2) {
+                nss = nva[0] * nva[0] + nva[1] * nva[1] + nva[2] * nva[2] + nva[3] * nva[3] +
+                      nvb[0] * nvb[0] + nvb[1] * nvb[1] + nvb[2] * nvb[2] + nvb[3] * nvb[3];
+            } else if constexpr (m == 3) {
+                // sqrt(C) / max(|x|, eps) as sqrt(C) min(rsq(|x|^2), 1 / eps)
+                // (hardware rsq, ~1 ulp; rsq(0) = inf takes the clamp)
+                nss = nrt * fminf(__builtin_amdgcn_rsqf(row16_sum(nss)), ninv_eps);
+            } else if constexpr (m == 4 || m == 5) {
+                f32x4 &v = (m == 4) ? nva : nvb;
+                const f32x4 &g = (m == 4) ? ngl : ngh;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = v[e] * g[e] * nss;
+            } else if constexpr (m == 6 || m == 7) {
+                const f32x4 &v = (m == 6) ? nva : nvb;
+                f32x4 &x = (m == 6) ? nea : neb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = silu ? __expf(-v[e]) : 0.f;
+            } else if constexpr (m == 8 || m == 9) {
                 // SiLU as y * rcp(1 + exp(-y)) (hardware reciprocal, ~1 ulp)
-                const float ex = silu ? __expf(-y) : 0.f;
-                o[e] = (_Float16)(y * __builtin_amdgcn_rcpf(1.0f + ex));
+                const f32x4 &v = (m == 8) ? nva : nvb;
+                const f32x4 &x = (m == 8) ? nea : neb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nout[(m - 8) * 4 + e] = (_Float16)(v[e] * __builtin_amdgcn_rcpf(1.0f + x[e]));
+            } else {
+                st16(spos.rn, spos.n[h] + r * rown, __builtin_bit_cast(f32x4, nout), false);
             }
-            st16(spos.rn, spos.n[h] + r * rown, __builtin_bit_cast(f32x4, o), false);
         }
+    };
+    constexpr int NSTEPS = 11;
+    // a whole pass
+    auto item_norm = [&](int r, int h) __attribute__((always_inline)) {
+        static_for<NSTEPS>([&](auto mc) __attribute__((always_inline)) { norm_step(r, h, mc); });
     };
     // stage part k of accumulator row r (the raw sums): lane l holds
     // pixel fx, channels 32 wave + 8 k + 4 fh .. + 3
@@ -561,6 +584,12 @@ void k_conv_ws(IgemmArgs p)
     }
     lds_barrier();
     if constexpr (WOUT || YG) bq = *reinterpret_cast<const f32x4 *>(sbias + dc);
+    if constexpr (NORM) {
+        nbl = *reinterpret_cast<const f32x4 *>(sbias + nc);
+        nbh = *reinterpret_cast<const f32x4 *>(sbias + nc + 4);
+        ngl = *reinterpret_cast<const f32x4 *>(sgam + nc);
+        ngh = *reinterpret_cast<const f32x4 *>(sgam + nc + 4);
+    }
 
     // fragment groups (K-step ks, tap column dx) g = 3 ks + dx; group g's
     // PH patch-row fragments live in bf[g & 1]
@@ -595,24 +624,28 @@ void k_conv_ws(IgemmArgs p)
                     if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, 0, (i - 4) / 4);
                     if constexpr (i == 20) item_load(xa, spos, 2);
                     if constexpr (i >= 24 && i < 40 && i % 4 == 0) item_store(xb, 1, (i - 24) / 4);
-                    if constexpr (i == 6) item_norm(0, 0);
-                    if constexpr (i == 18) item_norm(0, 1);
-                    if constexpr (i == 30) item_norm(1, 0);
-                    if constexpr (i == 42) item_norm(1, 1);
                 } else if constexpr (st == 2) {
                     if constexpr (i == 0) item_read(xa, 2);
                     if constexpr (i == 2) item_load(xb, spos, 3);
                     if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xa, 2, (i - 4) / 4);
-                    if constexpr (i == 6) item_norm(2, 0);
-                    if constexpr (i == 18) item_norm(2, 1);
                 } else if constexpr (st == 3) {
                     if constexpr (i == 0) item_read(xb, 3);
                     if constexpr (i == 1) cpos = make_out(true, cur.y0, cur.x0);
                     if constexpr (i == 2) item_load(xa, cpos, 0);
                     if constexpr (i >= 4 && i < 20 && i % 4 == 0) item_store(xb, 3, (i - 4) / 4);
                     if constexpr (i == 20) item_load(xb, cpos, 1);
-                    if constexpr (i == 6) item_norm(3, 0);
-                    if constexpr (i == 18) item_norm(3, 1);
+                }
+                // the norm's eight passes, a step per slot (two slots after
+                // the LDS read for it to land): passes 0-2 in stage 1, 3-5 in
+                // stage 2, 6-7 in stage 3 (from slot 3), 14 slots apart. Row
+                // r's staged values are read before the barrier of stage 3,
+                // whose staging overwrites them.
+                if constexpr (NORM && st >= 1) {
+                    constexpr int off = (st == 3) ? 3 : 0, npass = (st == 3) ? 2 : 3;
+                    constexpr int q = (i - off) / 14, o = (i - off) % 14, pass = 3 * (st - 1) + q;
+                    constexpr int m = (o == 0) ? 0 : (o >= 3 ? o - 2 : -1);
+                    if constexpr (i >= off && q < npass && m >= 0 && m < NSTEPS)
+                        norm_step(pass / 2, pass % 2, std::integral_constant<int, m>{});
                 }
                 // the next stage's weights, in the first tile
                 if constexpr (FIRST && st < NST - 1 && i < 36 && i % 2 == 0)
@@ -668,6 +701,9 @@ void k_conv_ws(IgemmArgs p)
                     if constexpr (f < NST * 18 - NWF) mma<true>(acc[tr.r], wr[f], bf[g & 1][tr.pr], kind);
                     else mma<false>(acc[tr.r], wr[f], bf[g & 1][tr.pr], kind);
                     hook(std::integral_constant<int, g * 3 * TH + i>{});
+                    // the norm's steps stay in their slots (left alone, the
+                    // scheduler gathers them at the group's end)
+                    if constexpr (NORM) __builtin_amdgcn_sched_barrier(0);
                 });
             });
         };
