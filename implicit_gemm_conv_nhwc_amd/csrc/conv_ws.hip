@@ -219,9 +219,10 @@ constexpr Triple<MODE> group_triple(int i)
     return Triple<MODE>{-1, -1, -1};
 }
 
-// The last group of the last stage runs row by row instead: row r's three
-// MFMAs are 3 r .. 3 r + 2, so the rows finish one after another and their
-// staging spreads over the group's slots.
+// The last group of the last stage and the first of the first run row by
+// row instead: row r's three MFMAs are 3 r .. 3 r + 2, so a tile's rows
+// finish one after another and the next tile's start one after another,
+// and each row has nine slots between the two for its staging.
 template <int MODE>
 constexpr Triple<MODE> last_triple(int i)
 {
@@ -654,20 +655,19 @@ void k_conv_ws(IgemmArgs p)
                 if constexpr (st == 0 && i == 24) nxt = make_tile(t + t_step < t_end ? t + t_step : -1);
                 // the rows whose last MFMA has run, into the staging area
                 // (the staged tile before was read before this stage's barrier)
-                // this tile's rows into the staging area, one part per slot
-                // from each row's last MFMA (slot 62 + 3 r of the last stage)
-                // on; the rest in the next tile's first slots, before the
-                // rows' first MFMAs there (the first tile's are garbage: no
-                // drain reads them). The staged tile before was read before
-                // this stage's barrier.
-                // (part k of row r at slot 63 + 3 r + k, counted on into the
-                // next tile: d = 3 r + k)
-                constexpr int d = (st == NST - 1) ? i - 63 : (st == 0 ? i + 9 : -1);
-                if constexpr (d >= 0 && d <= 3 * TH && (st == NST - 1 || d >= 9)) {
-                    constexpr int r1 = d / 3, k1 = d % 3;
-                    if constexpr (r1 < TH) stage_part(acc[r1], r1, k1);
-                    if constexpr (k1 == 0 && r1 >= 1) stage_part(acc[r1 - 1], r1 - 1, 3);
-                }
+                // this tile's rows into the staging area: part k of row r at
+                // slot 63 + 3 r + 2 k of the last stage, counted on into the
+                // next tile's first slots -- after the row's last MFMA (slot
+                // 62 + 3 r), before its first one in the next tile (slot
+                // 3 r). The first tile's stage 0 writes garbage: no drain
+                // reads it. The staged tile before was read before this
+                // stage's barrier.
+                static_for<TH>([&](auto rc) __attribute__((always_inline)) {
+                    constexpr int r = decltype(rc)::value;
+                    constexpr int h = (st == NST - 1) ? i : (st == 0 ? i + 72 : -100);  // slot counted from the last stage
+                    constexpr int d = h - 63 - 3 * r;
+                    if constexpr (d >= 0 && d <= 6 && d % 2 == 0 && (st == NST - 1 || h > 71)) stage_part(acc[r], r, d / 2);
+                });
                 // after the barrier: the next tile's patch for this stage's buffer
                 if constexpr (i >= 60 && i < 60 + APW) issue_one(nxt, st, st, i - 60);
             };
@@ -691,7 +691,7 @@ void k_conv_ws(IgemmArgs p)
                 constexpr int ks = g / 3, dx = g % 3;
                 static_for<3 * TH>([&](auto ic) __attribute__((always_inline)) {
                     constexpr int i = decltype(ic)::value;
-                    constexpr Triple<MODE> tr = (st == NST - 1 && g == 5) ? last_triple<MODE>(i) : group_triple<MODE>(i);
+                    constexpr Triple<MODE> tr = ((st == NST - 1 && g == 5) || (st == 0 && g == 0)) ? last_triple<MODE>(i) : group_triple<MODE>(i);
                     static_assert(tr.r >= 0, "a group has 3 TH MFMAs");
                     constexpr int f = (2 * st + ks) * 9 + tr.dy * 3 + dx;
                     // the first and last MFMA of each accumulator's chain
@@ -709,9 +709,7 @@ void k_conv_ws(IgemmArgs p)
         };
         static_for<NST>(run_stage);
         static_assert(last_triple<MODE>(3 * TH - 1).r == TH - 1 && last_triple<MODE>(3 * TH - 1).dy == 2, "row by row");
-        static_assert(group_triple<MODE>(0).r != 2 && group_triple<MODE>(0).r != 3 && group_triple<MODE>(1).r != 3 &&
-                          group_triple<MODE>(2).r != 3 && group_triple<MODE>(3).r != 3,
-                      "rows 2 and 3 start after their staging");
+        static_assert(last_triple<MODE>(3).r == 1 && last_triple<MODE>(0).dy == 0, "row by row");
         spos = cpos;
         t += t_step;
     };
@@ -721,6 +719,8 @@ void k_conv_ws(IgemmArgs p)
         run_tile(std::false_type{});
     }
     // the last tile's rows (the stream values of rows 0 and 1 are loading)
+    stage_part(acc[1], 1, 3);
+    stage_part(acc[2], 2, 2);
     stage_part(acc[2], 2, 3);
 #pragma unroll
     for (int k = 0; k < 4; ++k) stage_part(acc[3], 3, k);
