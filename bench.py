@@ -62,8 +62,9 @@ def _warm(fn, seconds=WARM_SECONDS):
         torch.cuda.synchronize()
         if time.perf_counter() - t0 >= seconds:
             return i
-ROOF_KERNEL = "k_conv_halo<1, 64, 4, false>"  # the 3x3 conv instantiation for 512^2 x 128
-CONV_SRC = os.path.join(ROOT, "implicit_gemm_conv_nhwc_amd", "csrc", "conv_halo.hip")
+ROOF_KERNEL = "k_conv_ws<1, false, false, true, false>"  # the 3x3 conv instantiation for 512^2 x 128
+CONV_SRC = os.path.join(ROOT, "implicit_gemm_conv_nhwc_amd", "csrc", "conv_ws.hip")
+CHIP_CLOCK_GHZ = 2.4  # the clock the published peaks are quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_512x512x128_traffic.json")
 
 
@@ -89,6 +90,29 @@ def measured_traffic():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def _batches(fn, reps, batch=10):
+    """Time reps launches of fn(i) in batches of `batch`, each batch between
+    two HIP events on the current stream: per-launch ms as (median, mean)
+    over the batches."""
+    import statistics
+
+    import torch
+
+    per = []
+    i = 0
+    for _ in range(max(1, reps // batch)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(batch):
+            fn(i)
+            i += 1
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / batch)
+    return statistics.median(per), statistics.fmean(per)
 
 
 # ---------------------------------------------------------------------------
@@ -145,20 +169,23 @@ def bench_decode(steps, warmup, h0, q_chunk):
     for _ in range(warmup):
         dd.forward(zd, h0, h0, guard_log2=8, q_chunk=q_chunk, ws=ws, out=out)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    import statistics
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
+    evs[0].record()
+    for k in range(steps):
         dd.forward(zd, h0, h0, guard_log2=8, q_chunk=q_chunk, ws=ws, out=out)
-    ev1.record()
+        evs[k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
+    per = [evs[k].elapsed_time(evs[k + 1]) for k in range(steps)]
+    ev_ms = sum(per)
     finite = bool(torch.isfinite(out).all().item())
     flops = decode_flops(spec, h0, h0)
     del ws
-    return {"wall_s": wall, "event_ms": ev_ms, "flops": flops, "finite": finite, "H": H, "spec": spec}
+    return {"wall_s": wall, "event_ms": ev_ms, "median_ms": statistics.median(per), "flops": flops,
+            "finite": finite, "H": H, "spec": spec}
 
 
 def bench_conv_roofline(reps, H=512, W=512, C=128):
@@ -187,20 +214,34 @@ def bench_conv_roofline(reps, H=512, W=512, C=128):
         ig.rmsnorm_silu_f16(x32, M, C, C, None, gamma, 0, 1e-12, t)
     # warm up to the steady clock (the host-side setup above leaves the GPU
     # idle for seconds)
-    nwarm = _warm(lambda i: ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets]))
+    run = lambda i: ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets])  # noqa: E731
+    nwarm = _warm(run)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(reps):
-        ig.conv3x3_nhwc(xs[i % nsets], H, W, C, plane, C, bias, 1.0, ys[i % nsets])
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     avg_ms = e0.elapsed_time(e1) / reps
+    med_ms, _ = _batches(run, reps)
+    # the clock the conv runs at: its first wave's shader-clock and 100 MHz
+    # real-time counters, over a few more launches (the last one's kept)
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    ig.set_clock_probe(clk)
+    try:
+        for i in range(5):
+            run(i)
+        torch.cuda.synchronize()
+    finally:
+        ig.set_clock_probe(None)
+    ck0, rt0, ck1, rt1 = [int(v) for v in clk.cpu()]
+    ghz = (ck1 - ck0) / ((rt1 - rt0) / 1e8) / 1e9 if rt1 > rt0 else None
     flops = 2.0 * M * C * C * 9
     byts = M * C * 2 + C * 9 * C * 2 + M * C * 4
     ok = bool(torch.isfinite(ys[(reps - 1) % nsets]).all().item())
-    return {"avg_ms": avg_ms, "flops": flops, "bytes": byts, "launches": reps, "warm_launches": nwarm, "finite": ok,
-            "sets": nsets}
+    return {"avg_ms": avg_ms, "median_ms": med_ms, "clock_ghz": ghz, "flops": flops, "bytes": byts,
+            "launches": reps, "warm_launches": nwarm, "finite": ok, "sets": nsets}
 
 
 def bench_norm_roofline(reps, H=512, W=512, C=128):
@@ -219,17 +260,19 @@ def bench_norm_roofline(reps, H=512, W=512, C=128):
     x0 = torch.from_numpy(d["x"].reshape(M, C)).to(dev)
     xs = [x0.clone() for _ in range(nsets)]
     ys = [torch.empty((M, C), dtype=torch.float16, device=dev) for _ in range(nsets)]
-    _warm(lambda i: ig.rmsnorm_silu_f16(xs[i % nsets], M, C, C, None, gamma, 1, 1e-12, ys[i % nsets]))
+    run = lambda i: ig.rmsnorm_silu_f16(xs[i % nsets], M, C, C, None, gamma, 1, 1e-12, ys[i % nsets])  # noqa: E731
+    _warm(run)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(reps):
-        ig.rmsnorm_silu_f16(xs[i % nsets], M, C, C, None, gamma, 1, 1e-12, ys[i % nsets])
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     avg_ms = e0.elapsed_time(e1) / reps
-    return {"avg_ms": avg_ms, "bytes": M * C * 6, "sets": nsets}
+    med, _ = _batches(run, reps)
+    return {"avg_ms": avg_ms, "median_ms": med, "bytes": M * C * 6, "sets": nsets}
 
 
 def _pool_timed(fn, reps, per_set_bytes, make_set):
@@ -248,7 +291,8 @@ def _pool_timed(fn, reps, per_set_bytes, make_set):
         fn(sets[i % nsets])
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps, nsets
+    med, _ = _batches(lambda i: fn(sets[i % nsets]), reps)
+    return e0.elapsed_time(e1) / reps, nsets, med
 
 
 def bench_cast_roofline(reps, H=512, W=512, C=128):
@@ -260,9 +304,9 @@ def bench_cast_roofline(reps, H=512, W=512, C=128):
     M = H * W
     dev = torch.device("cuda")
     x0 = torch.randn((M, C), device=dev) * 300.0
-    ms, nsets = _pool_timed(lambda st: ig.guard_cast(st[0], M, C, None, 8, st[1]), reps, M * C * 6,
-                            lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
-    return {"avg_ms": ms, "bytes": M * C * 6, "sets": nsets}
+    ms, nsets, med = _pool_timed(lambda st: ig.guard_cast(st[0], M, C, None, 8, st[1]), reps, M * C * 6,
+                                 lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
+    return {"avg_ms": ms, "median_ms": med, "bytes": M * C * 6, "sets": nsets}
 
 
 def bench_groupnorm_roofline(reps, H=512, W=512, C=128, groups=32):
@@ -280,10 +324,10 @@ def bench_groupnorm_roofline(reps, H=512, W=512, C=128, groups=32):
     beta = torch.randn(C, device=dev) * 0.1
     nbytes = ig.groupnorm_workspace_bytes(M, C, groups)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    ms, nsets = _pool_timed(
+    ms, nsets, med = _pool_timed(
         lambda st: ig.groupnorm_silu_f16(st[0], M, C, C, groups, None, gamma, beta, 1, 1e-6, ws, nbytes, st[1]),
         reps, M * C * 6, lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
-    return {"avg_ms": ms, "bytes": M * C * 6, "sets": nsets}
+    return {"avg_ms": ms, "median_ms": med, "bytes": M * C * 6, "sets": nsets}
 
 
 def bench_attention_roofline(reps, m=16384, C=512):
@@ -302,15 +346,118 @@ def bench_attention_roofline(reps, m=16384, C=512):
     nb = ig.attention_workspace_bytes(m, C)
     ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((m, C), dtype=torch.float16, device=dev)
-    _warm(lambda i: ig.attention_f16(q, k, vt, m, m, C, bv, ws, nb, out))
+    run = lambda i: ig.attention_f16(q, k, vt, m, m, C, bv, ws, nb, out)  # noqa: E731
+    _warm(run)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        ig.attention_f16(q, k, vt, m, m, C, bv, ws, nb, out)
+    for i in range(reps):
+        run(i)
     e1.record()
     torch.cuda.synchronize()
-    return {"avg_ms": e0.elapsed_time(e1) / reps, "flops": 4.0 * m * m * C}
+    med, _ = _batches(run, reps, batch=1)
+    return {"avg_ms": e0.elapsed_time(e1) / reps, "median_ms": med, "flops": 4.0 * m * m * C}
+
+
+def bench_cfg2(reps):
+    """Config 2 at 128x128x256: the guarded input's nearest-2x 3x3 up conv
+    256 -> 256 (M = 65536 outputs, K = 2304: 77.3 GFLOP) and its 1x1
+    shortcut 256 -> 256 (2.15 GFLOP), outputs rotated past the cache."""
+    import numpy as np
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+    import synth
+
+    d = synth.config2()
+    H, W, C = d["x"].shape
+    M = H * W
+    dev = torch.device("cuda")
+    gs = float(2 ** d["guard_log2"])
+    xg = torch.empty((M, C), dtype=torch.float16, device=dev)
+    ig.guard_cast(torch.from_numpy(d["x"].reshape(M, C)).to(dev), M, C, None, d["guard_log2"], xg)
+    p_up = torch.empty(ig.plane_shape(C, C, 3), dtype=torch.float16, device=dev)
+    ig.pack_conv_weights(torch.from_numpy(d["w_up"]).to(dev), C, C, 3, C, C, p_up)
+    p_sc = torch.empty(ig.plane_shape(C, C, 1), dtype=torch.float16, device=dev)
+    ig.pack_conv_weights(torch.from_numpy(d["w_sc"]).to(dev), C, C, 1, C, C, p_sc)
+    b_up = torch.from_numpy(d["b_up"]).to(dev)
+    b_sc = torch.from_numpy(d["b_sc"]).to(dev)
+    n_up = max(2, int(np.ceil(1.2e9 / (4 * M * C * 4))))
+    ups = [torch.empty((4 * M, C), dtype=torch.float32, device=dev) for _ in range(n_up)]
+    run_up = lambda i: ig.conv3x3_up2_nhwc(xg, H, W, C, p_up, C, b_up, gs, ups[i % n_up])  # noqa: E731
+    _warm(run_up)
+    up_med, up_avg = _batches(run_up, reps)
+    n_sc = max(2, int(np.ceil(1.2e9 / (M * C * 4))))
+    scs = [torch.empty((M, C), dtype=torch.float32, device=dev) for _ in range(n_sc)]
+    run_sc = lambda i: ig.gemm1x1(xg, M, C, C, p_sc, C, C, b_sc, gs, scs[i % n_sc], C, 0)  # noqa: E731
+    _warm(run_sc)
+    sc_med, sc_avg = _batches(run_sc, reps)
+    out = {}
+    for name, med, avg, fl in (("up_conv_3x3_128x128x256_to_256x256x256", up_med, up_avg, 2.0 * 4 * M * C * C * 9),
+                               ("shortcut_1x1_128x128x256", sc_med, sc_avg, 2.0 * M * C * C)):
+        out[name] = {"median_us": round(med * 1000, 3), "mean_us": round(avg * 1000, 3), "gflop": round(fl / 1e9, 3),
+                     "tflops": round(fl / (med / 1000.0) / 1e12, 2),
+                     "frac_of_peak": round(fl / (med / 1000.0) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def bench_cfg3_padded(reps, c, H=512, W=512):
+    """Config 3's padded variant: c real channels stored in cp (288 in 320,
+    144 in 192), the 3x3 conv at 512x512; algorithmic FLOP counts the real
+    channels, executed FLOP the padded ones."""
+    import numpy as np
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+    import synth
+
+    cp = {288: 320, 144: 192}[c]
+    d = synth.config3(c, H, W)
+    M = H * W
+    dev = torch.device("cuda")
+    gamma = torch.zeros(cp, device=dev)
+    gamma[:c] = torch.from_numpy(d["gamma"]).to(dev)
+    bias = torch.zeros(cp, device=dev)
+    bias[:c] = torch.from_numpy(d["b"]).to(dev)
+    x32 = torch.zeros((M, cp), device=dev)
+    x32[:, :c] = torch.from_numpy(d["x"].reshape(M, c)).to(dev)
+    plane = torch.empty(ig.plane_shape(cp, cp, 3), dtype=torch.float16, device=dev)
+    ig.pack_conv_weights(torch.from_numpy(d["w"]).to(dev), c, c, 3, cp, cp, plane)
+    nsets = max(2, int(np.ceil(1.2e9 / (M * cp * 6))))
+    xs = [torch.empty((M, cp), dtype=torch.float16, device=dev) for _ in range(nsets)]
+    ys = [torch.empty((M, cp), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    for t in xs:
+        ig.rmsnorm_silu_f16(x32, M, cp, c, None, gamma, 0, 1e-12, t)
+    run = lambda i: ig.conv3x3_nhwc(xs[i % nsets], H, W, cp, plane, cp, bias, 1.0, ys[i % nsets])  # noqa: E731
+    _warm(run)
+    med, avg = _batches(run, reps)
+    alg = 2.0 * M * c * c * 9
+    exe = 2.0 * M * cp * cp * 9
+    return {"median_us": round(med * 1000, 3), "mean_us": round(avg * 1000, 3),
+            "algorithmic_gflop": round(alg / 1e9, 2), "executed_gflop": round(exe / 1e9, 2),
+            "algorithmic_tflops": round(alg / (med / 1000.0) / 1e12, 2),
+            "executed_tflops": round(exe / (med / 1000.0) / 1e12, 2),
+            "executed_frac_of_peak": round(exe / (med / 1000.0) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
+def cpu_conv(H=512, W=512, C=128):
+    """The oracle's 3x3 conv (float64 direct loop, OpenMP) at config 3's
+    512x512x128 -> 128 on the host: seconds for one conv."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    d = synth.config3(C, H, W)
+    x = np.ascontiguousarray(d["x"].transpose(2, 0, 1), dtype=np.float64)
+    O.conv2d(x[:, :8, :8], d["w"], d["b"])  # build + load the library
+    t0 = time.perf_counter()
+    O.conv2d(x, d["w"], d["b"])
+    t = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    fl = 2.0 * H * W * C * C * 9
+    return {"seconds": round(t, 3), "gflops": round(fl / t / 1e9, 2), "cores": threads, "kind": "oracle",
+            "sample": "one oracle conv2d (f64) at 512x512x128 -> 128, the roofline conv's configuration"}
 
 
 def cpu_baseline(min_seconds=10.0):
@@ -567,10 +714,29 @@ def main():
     log("attention 16384 x 512: %.1f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (
         att["avg_ms"] * 1000, att_tf, 100 * att_tf / MFMA_F16_PEAK_TFLOPS))
 
-    cpu = None
+    # the other configurations' figures
+    decodes = {}
+    for lat, st, wu in ((32, 10, 3), (256, 3, 1)):
+        dx = bench_decode(st, wu, lat, args.q_chunk)
+        decodes["%dx%d" % (dx["H"], dx["H"])] = {
+            "median_s": round(dx["median_ms"] / 1000.0, 6), "mean_s": round(dx["event_ms"] / st / 1000.0, 6),
+            "steps": st, "tflop": round(dx["flops"] / 1e12, 4),
+            "tflops": round(dx["flops"] / (dx["median_ms"] / 1000.0) / 1e12, 2), "output_finite": dx["finite"]}
+        log("decode %d^2: median %.3f ms" % (dx["H"], dx["median_ms"]))
+    cfg2 = bench_cfg2(args.roof_reps)
+    log("config 2:", json.dumps(cfg2))
+    cfg3p = {}
+    for c in (288, 144):
+        r = bench_cfg3_padded(args.roof_reps, c)
+        cfg3p["%d_in_%d" % (c, {288: 320, 144: 192}[c])] = r
+        log("config 3, %d channels padded: %s" % (c, json.dumps(r)))
+
+    cpu = cpu_c = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
         log("cpu baseline: %.4f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+        cpu_c = cpu_conv()
+        log("cpu conv: %.2f s (%.1f GFLOP/s) on %d threads" % (cpu_c["seconds"], cpu_c["gflops"], cpu_c["cores"]))
 
     spec = dec["spec"]
     res = {
@@ -597,6 +763,7 @@ def main():
             "q_chunk": args.q_chunk or "default",
         },
         "decode_s": round(ms / 1000.0, 6),
+        "decode_s_median": round(dec["median_ms"] / 1000.0, 6),
         "decode_tflop": round(dec["flops"] / 1e12, 4),
         "output_finite": dec["finite"],
         "roofline": {
@@ -608,7 +775,13 @@ def main():
             "frac": round(conv_tf / MFMA_F16_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(),
             "avg_launch_us": round(conv["avg_ms"] * 1000, 3),
+            "median_launch_us": round(conv["median_ms"] * 1000, 3),
             "algorithmic_bytes": conv["bytes"],
+            # the fraction of the peak at the clock the conv ran at (its first
+            # wave's shader-clock over 100 MHz real-time counters)
+            "clock_ghz": round(conv["clock_ghz"], 3) if conv["clock_ghz"] else None,
+            "frac_at_clock": round(conv_tf / (MFMA_F16_PEAK_TFLOPS * conv["clock_ghz"] / CHIP_CLOCK_GHZ), 4)
+            if conv["clock_ghz"] else None,
         },
         "roofline_norm": {
             "kernel": "rmsnorm_silu_f16 512x512x128",
@@ -618,6 +791,7 @@ def main():
             "unit": "GB/s",
             "frac": round(norm_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(norm["avg_ms"] * 1000, 3),
+            "median_launch_us": round(norm["median_ms"] * 1000, 3),
         },
         "roofline_cast": {
             "kernel": "guard_cast 512x512x128 (g=8)",
@@ -627,6 +801,7 @@ def main():
             "unit": "GB/s",
             "frac": round(cast_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(cast["avg_ms"] * 1000, 3),
+            "median_launch_us": round(cast["median_ms"] * 1000, 3),
         },
         "roofline_groupnorm": {
             "kernel": "groupnorm_silu_f16 512x512x128, 32 groups (stats + finalize + apply)",
@@ -636,6 +811,7 @@ def main():
             "unit": "GB/s",
             "frac": round(gn_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(gn["avg_ms"] * 1000, 3),
+            "median_us": round(gn["median_ms"] * 1000, 3),
         },
         "roofline_attention": {
             "kernel": "attention_f16 single pass (k_flash + k_flash_merge), 16384 tokens x 512",
@@ -645,9 +821,14 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4),
             "avg_us": round(att["avg_ms"] * 1000, 3),
+            "median_us": round(att["median_ms"] * 1000, 3),
             "algorithmic_flop": att["flops"],
         },
+        "decodes": decodes,
+        "config2": cfg2,
+        "config3_padded": cfg3p,
         "cpu_baseline": cpu,
+        "cpu_conv": cpu_c,
         "context": "pages: 0.49-0.61 s per 1024^2 decode on an RTX PRO 4000 Blackwell "
                    "(Qwen-Image-2.1 VAE, real weights; other model and machine)",
     }

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     conv3x3_up2_nhwc,
     conv_nhwc_ex,
     band_plan,
+    set_clock_probe,
     decoder_bands_workspace_bytes,
     decoder_forward,
     decoder_forward_bands,

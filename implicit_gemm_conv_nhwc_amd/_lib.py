@@ -285,6 +285,16 @@ def band_plan(n_res, has_up, h0, band_from, keep_lo, keep_hi):
     return (inp[0], inp[1]), [(feed[2 * i], feed[2 * i + 1]) for i in range(n)]
 
 
+_clock_probe = _sig("ig_set_clock_probe", [_vp])
+
+
+def set_clock_probe(buf):
+    """Measurement hook (benchmarks): while ``buf`` (a device tensor of 4
+    int64, or None to stop) is set, each launch of the register-weight 3x3
+    conv writes [clock0, realtime0, clock1, realtime1] of its first wave."""
+    return _check(_clock_probe(_ptr(buf)))
+
+
 def decoder_bands_workspace_bytes(desc, h0, w0, q_chunk, band_rows, band_from):
     n = int(_bws_bytes(ctypes.byref(desc), h0, w0, q_chunk, band_rows, band_from))
     if n == 0:

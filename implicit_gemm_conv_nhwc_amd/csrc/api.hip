@@ -159,6 +159,12 @@ const char *ig_last_error(void) { return g_err; }
 
 int ig_version(void) { return (1 << 16) | 0; }
 
+int ig_set_clock_probe(void *dev_buf)
+{
+    ig::set_clock_probe(dev_buf);
+    return 0;
+}
+
 int ig_pack_conv_weights(const uint16_t *w, int cout, int cin, int k, int cout_p, int cin_p,
                          uint16_t *plane, void *stream)
 {

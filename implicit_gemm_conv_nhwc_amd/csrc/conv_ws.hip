@@ -291,6 +291,12 @@ void k_conv_ws(IgemmArgs p)
     float *sbias = stg + TH * TW * SP;                           // [BN]
     float *sgam = sbias + BN;                                    // [BN]
 
+    // the clock probe (measurement only): counters at the start
+    unsigned long long ck0 = 0, rt0 = 0;
+    if (p.clk) {
+        ck0 = __builtin_amdgcn_s_memtime();
+        rt0 = __builtin_amdgcn_s_memrealtime();
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
@@ -732,6 +738,13 @@ void k_conv_ws(IgemmArgs p)
     wait_n(std::integral_constant<int, 0>{});
     drain_row(xa, 2);
     drain_row(xb, 3);
+    if (p.clk && blockIdx.x == 0 && tid == 0) {
+        const unsigned long long ck1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+        p.clk[0] = ck0;
+        p.clk[1] = rt0;
+        p.clk[2] = ck1;
+        p.clk[3] = rt1;
+    }
 }
 
 int cu_count()
@@ -747,9 +760,13 @@ int cu_count()
     return cus[dev];
 }
 
+void *g_clock_probe = nullptr;
+
 template <int MODE, bool NORM, bool ACC, bool WOUT, bool YG>
-void launch_ws_t(const IgemmArgs &a, hipStream_t s)
+void launch_ws_t(const IgemmArgs &a0, hipStream_t s)
 {
+    IgemmArgs a = a0;
+    a.clk = static_cast<unsigned long long *>(g_clock_probe);
     const int Hout = (MODE == kConv3x3Up2) ? 2 * a.H : a.H;
     const int Wout = (MODE == kConv3x3Up2) ? 2 * a.W : a.W;
     const int tiles = ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW);
@@ -780,6 +797,8 @@ void launch_ws_mode(const IgemmArgs &a, hipStream_t s)
 }
 
 }  // namespace
+
+void set_clock_probe(void *buf) { g_clock_probe = buf; }
 
 bool conv_ws_supported(int mode, const IgemmArgs &a)
 {

@@ -57,6 +57,10 @@ struct IgemmArgs {
     // yg [M][ldc] -- the cast of the stream before an up conv
     _Float16 *yg = nullptr;
     float gscale = 1.f;
+    // measurement: when set, the weight-stationary conv's first wave
+    // writes the shader-clock and real-time counters at its start and end
+    // (clk[0], clk[1], clk[2], clk[3])
+    unsigned long long *clk = nullptr;
 };
 
 // Launch the MFMA implicit GEMM for `mode`; picks the tile shape. The 3x3
@@ -71,6 +75,9 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s);
 // output width, not the height, so bands and whole frames agree).
 bool conv_ws_supported(int mode, const IgemmArgs &a);
 void launch_conv_ws(int mode, const IgemmArgs &a, hipStream_t s);
+// The buffer later launches of the weight-stationary conv record their
+// clock counters in (null: none).
+void set_clock_probe(void *buf);
 
 // ---------------------------------------------------------------------
 // plain NT GEMM C = oscale * A.B^T with the attention's softmax epilogues

@@ -403,6 +403,17 @@ int decoder_forward_bands(const ig_decoder *dec, const float *latent, int h0, in
 int ig_band_plan(int n_up, const int *n_res, const int *has_up, int h0, int band_from, int keep_lo,
                  int keep_hi, int *input, int *feed);
 
+/* Measurement hook, for benchmarks (not a step of the method): while
+ * dev_buf is set, every launch of the 3x3 conv kernel that holds its
+ * weights in registers (cin_p = cout_p = 128) has its first wave write,
+ * into dev_buf (device memory, 4 x uint64, owned by the caller), the
+ * shader-clock counter and the 100 MHz real-time counter at the wave's
+ * start and at its end: [clk0, rt0, clk1, rt1]. The clock the kernel ran
+ * at is (clk1 - clk0) / ((rt1 - rt0) / 1e8) Hz. NULL stops it. The
+ * setting is process-wide and the buffer is rewritten by each launch:
+ * not for concurrent launches. Returns 0. */
+int ig_set_clock_probe(void *dev_buf);
+
 #ifdef __cplusplus
 }
 #endif

@@ -470,6 +470,34 @@ def test_conv_with_guarded_cast_output(H, W, cin, cout, mode, acc, write_y, g):
     assert np.max(np.abs(got - want)) <= 2e-3 * np.sqrt(np.mean(conv ** 2)) + 1e-7 * np.max(np.abs(want))
 
 
+def test_clock_probe_reads_the_conv_clock():
+    """The measurement hook: the first wave's shader-clock and real-time
+    counters around a 512x512x128 conv give a clock in the chip's range, and
+    the conv's output is the same with the hook set."""
+    H = W = 512
+    C = 128
+    M = H * W
+    rng = np.random.default_rng(7)
+    x = dev(rng.standard_normal((M, C)).astype(np.float16))
+    plane = packed((rng.standard_normal((C, C, 3, 3)) / 34).astype(np.float16))
+    b = dev((rng.standard_normal(C) * 0.02).astype(np.float32))
+    y0, y1 = nan_f32((M, C)), nan_f32((M, C))
+    ig.conv3x3_nhwc(x, H, W, C, plane, C, b, 1.0, y0)
+    buf = torch.zeros(4, dtype=torch.int64, device="cuda")
+    ig.set_clock_probe(buf)
+    try:
+        ig.conv3x3_nhwc(x, H, W, C, plane, C, b, 1.0, y1)
+    finally:
+        ig.set_clock_probe(None)
+    torch.cuda.synchronize()
+    ck0, rt0, ck1, rt1 = [int(v) for v in buf.cpu()]
+    assert rt1 > rt0 and ck1 > ck0
+    ghz = (ck1 - ck0) / ((rt1 - rt0) / 1e8) / 1e9
+    print("clock during the conv: %.3f GHz over %.1f us" % (ghz, (rt1 - rt0) / 100.0))
+    assert 0.3 < ghz < 3.5
+    assert torch.equal(y0, y1)
+
+
 @pytest.mark.parametrize("H,W,mode,acc,write_y,g", [
     (258, 300, 1, 0, 1, 8), (258, 300, 1, 1, 1, 8), (259, 301, 1, 1, 0, 8),
     (130, 150, 2, 0, 1, 8), (131, 149, 2, 1, 0, 4)])
