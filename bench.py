@@ -32,6 +32,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import sys
 import time
@@ -500,6 +501,11 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print("copy calibration: %d launches, %d bytes read and %d written per launch" % (reps, nbytes, nbytes))
 
 
+def _is_roof(name):
+    """The roofline conv's kernel, by its demangled or mangled name."""
+    return ROOF_KERNEL.replace(" ", "") in name.replace(" ", "") or "k_conv_wsILi1ELb0ELb0ELb1ELb0E" in name
+
+
 def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
     """Average of `counter` over the roofline conv launches, scaled by the
     counter's reading for the plain copy (bytes moved / counter value)."""
@@ -509,8 +515,7 @@ def digest_pmc(conv_csv, copy_csv, counter, roof_launches, nbytes=1 << 30):
         return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
 
     conv = [float(r["Counter_Value"]) for r in sorted(rows(conv_csv), key=lambda r: int(r["Start_Timestamp"]))
-            if ROOF_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", "")
-            or "k_conv_halo" in r["Kernel_Name"] and "ILi1ELi64ELi4ELb0" in r["Kernel_Name"]][-roof_launches:]
+            if _is_roof(r["Kernel_Name"])][-roof_launches:]
     cp = [float(r["Counter_Value"]) for r in rows(copy_csv) if "mul" in r["Kernel_Name"].lower()
           or "elementwise" in r["Kernel_Name"].lower()]
     scale = nbytes / (sum(cp) / len(cp))
@@ -552,22 +557,24 @@ def digest_counters(path, roof_launches, n_xcd=8, n_simd=1024):
     import csv
 
     rows = list(csv.DictReader(open(path)))
-    kernels = [("conv3x3 512^2x128 (%s)" % ROOF_KERNEL,
-                lambda n: "k_conv_halo" in n and ("ILi1ELi64ELi4ELb0" in n or ROOF_KERNEL.replace(" ", "") in n.replace(" ", "")),
-                roof_launches),
-               ("attention 16384 x 512 (k_flash)", lambda n: "k_flash(" in n or "k_flashEN" in n, 10)]
-    # the decode's upsampling convs (k_conv_halo<2, 64, 4, false>), one entry per grid
-    up = lambda n: "k_conv_halo" in n and ("ILi2ELi64ELi4ELb0" in n or "<2, 64, 4, false>" in n)
-    for g in sorted({r["Grid_Size"] for r in rows if up(r["Kernel_Name"])}, key=int):
-        kernels.append(("decode up conv k_conv_halo<2, 64, 4, false>, grid %s" % g,
-                        (lambda g: lambda n, r=None: up(n))(g), 10, g))
+    kernels = [("conv3x3 512^2x128 (%s)" % ROOF_KERNEL, _is_roof, roof_launches, None, None),
+               ("attention 16384 x 512 (k_flash)", lambda n: "k_flash(" in n or "k_flashEN" in n, 10, None, None)]
+    # the 1024^2 decode's convs: every dispatch before the roofline region
+    # (the decodes run first), the last 10 of each conv kernel and grid
+    t_roof = min([int(r["Start_Timestamp"]) for r in rows if _is_roof(r["Kernel_Name"])] or [1 << 62])
+    conv = lambda n: "k_conv_ws" in n or "k_conv_halo" in n  # noqa: E731
+    seen = sorted({(r["Kernel_Name"], r["Grid_Size"]) for r in rows
+                   if conv(r["Kernel_Name"]) and int(r["Start_Timestamp"]) < t_roof})
+    for name, g in seen:
+        m = re.search(r"k_conv_\w+<[^>]*>", name)
+        short = m.group(0) if m else name[:60]
+        kernels.append(("1024^2 decode: %s, grid %s" % (short, g), (lambda nm: lambda n: n == nm)(name), 10, g, t_roof))
     res = {}
-    for entry in kernels:
-        title, match, last = entry[:3]
-        grid = entry[3] if len(entry) > 3 else None
+    for title, match, last, grid, before in kernels:
         by = {}
         for r in rows:
-            if match(r["Kernel_Name"]) and (grid is None or r["Grid_Size"] == grid):
+            if match(r["Kernel_Name"]) and (grid is None or r["Grid_Size"] == grid) and \
+                    (before is None or int(r["Start_Timestamp"]) < before):
                 by.setdefault(r["Counter_Name"], []).append((int(r["Start_Timestamp"]), float(r["Counter_Value"]),
                                                              int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
         if not by:
@@ -612,15 +619,17 @@ def digest_trace(path, roof_launches):
     for name, (n, t) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
         short = name if len(name) < 90 else name[:87] + "..."
         print("%s | %d | %.1f | %.2f | %.1f%%" % (short, n, t, t / n, 100 * t / tot))
-    roof = [x for x in seq if ROOF_KERNEL.replace(" ", "") in x[1].replace(" ", "")]
+    roof = [x for x in seq if _is_roof(x[1])]
     last = roof[-roof_launches:]
+    t_roof = roof[0][0] if roof else 1 << 62
     if last:
         avg = sum(x[2] for x in last) / len(last)
         print("roofline region: last %d dispatches of %s (grid %s): avg %.2f us" % (
             len(last), ROOF_KERNEL, last[-1][3], avg))
-    # the last decode alone: from its latent cast (k_latent) to its output
-    # conv (k_conv_out), by kernel and grid
-    starts = [i for i, x in enumerate(seq) if "k_latent" in x[1]]
+    # the last 1024^2 decode alone (the decodes before the roofline region):
+    # from its latent cast (k_latent) to its output conv (k_conv_out), by
+    # kernel and grid
+    starts = [i for i, x in enumerate(seq) if "k_latent" in x[1] and x[0] < t_roof]
     if starts:
         dec = seq[starts[-1]:]
         ends = [i for i, x in enumerate(dec) if "k_conv_out" in x[1]]
@@ -632,7 +641,7 @@ def digest_trace(path, roof_launches):
             e[0] += 1
             e[1] += t
         busy = sum(v[1] for v in per.values())
-        print("\nlast decode: %d dispatches, %.1f us of kernel time" % (len(dec), busy))
+        print("\nlast 1024^2 decode: %d dispatches, %.1f us of kernel time" % (len(dec), busy))
         print("kernel | grid (threads) | calls | total us | share")
         for (name, grid), (n, t) in sorted(per.items(), key=lambda kv: -kv[1][1]):
             print("%s | %s | %d | %.1f | %.1f%%" % (name, grid, n, t, 100 * t / busy))
