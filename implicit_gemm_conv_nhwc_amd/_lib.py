@@ -250,7 +250,8 @@ class AttnW(ctypes.Structure):
 
 
 class UpW(ctypes.Structure):
-    _fields_ = [("n_res", _c_int), ("res", ResnetW * IG_MAX_RES), ("has_up", _c_int), ("up", ConvW)]
+    _fields_ = [("n_res", _c_int), ("res", ResnetW * IG_MAX_RES), ("has_up", _c_int), ("up", ConvW),
+                ("dupup", _c_int), ("dupup_ft", _c_int)]
 
 
 class DecoderDesc(ctypes.Structure):

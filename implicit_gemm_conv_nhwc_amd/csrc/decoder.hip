@@ -95,12 +95,13 @@ struct Plan {
     int64_t max_h = 0;   // f32 conv outputs
     int64_t max_xn = 0;  // f16 conv inputs
     int64_t max_xg = 0;  // f16 guarded shortcut input
+    int64_t max_cp = 0;  // f32 up-stage input kept for its DupUp shortcut
     int m = 0, mp = 0, C = 0, qc = 0;
     bool flash = false;  // single-pass attention (else query chunks)
     int H = 0, W = 0;    // output frame
     int s = 0;           // up blocks s.. run in bands (s == n_up: none)
     int band_rows = 0;   // kept output rows per band
-    size_t off_x, off_xb, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, total;
+    size_t off_x, off_xb, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, off_cp, total;
 };
 
 int check_conv_w(const ig_conv_w &c, const char *name, int k)
@@ -194,6 +195,7 @@ int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
         const ig_up_w &u = d->ups[s];
         if (u.n_res < 0 || u.n_res > IG_MAX_RES) return fail(IG_EINVAL, "ups[%d].n_res=%d", s, u.n_res);
         wd.cp_in[s] = cp;
+        const int c_in = c;
         for (int r = 0; r < u.n_res; ++r) {
             char nm[32];
             snprintf(nm, sizeof nm, "ups.%d.res.%d", s, r);
@@ -204,11 +206,19 @@ int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
             snprintf(nm, sizeof nm, "ups.%d.up", s);
             if ((e = check_conv_w(u.up, nm, 3))) return e;
             if (u.up.cin != c || u.up.cin_p != cp) return fail(IG_EINVAL, "%s: input %d, stream %d", nm, u.up.cin, c);
+            if (u.dupup) {
+                if (u.dupup_ft < 1 || u.dupup_ft > 16) return fail(IG_EINVAL, "ups[%d].dupup_ft=%d", s, u.dupup_ft);
+                if ((4LL * u.dupup_ft * u.up.cout) % c_in)
+                    return fail(IG_EUNSUPPORTED, "ups[%d]: DupUp needs %d * %d a multiple of the input's %d channels", s,
+                                u.up.cout, 4 * u.dupup_ft, c_in);
+            }
             H *= 2;
             W *= 2;
             if (H * W >= (1LL << 31)) return fail(IG_EUNSUPPORTED, "frame too large");
             c = u.up.cout;
             cp = u.up.cout_p;
+        } else if (u.dupup) {
+            return fail(IG_EINVAL, "ups[%d]: a DupUp shortcut without an upsample", s);
         }
         wd.cp_out[s] = cp;
     }
@@ -231,6 +241,7 @@ void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Spa
         const ig_up_w &u = d.ups[s];
         const int64_t M = (int64_t)rows * W;
         upd(xmax, M * cp);
+        if (u.has_up && u.dupup) upd(pl.max_cp, M * cp);
         for (int r = 0; r < u.n_res; ++r) {
             size_resnet(u.res[r], M, cp, xmax, pl);
             cp = u.res[r].c2.cout_p;
@@ -319,6 +330,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     pl.off_q = take(mp * C * 2);
     pl.off_k = take(mp * C * 2);
     pl.off_vt = take(C * mp * 2);
+    pl.off_cp = take(pl.max_cp * 4);
     if (pl.flash) {
         // the single-pass kernel's key-range partials (if any)
         pl.off_o = take(0);
@@ -342,6 +354,7 @@ struct Run {
     int g;
     float *x, *h, *o32, *S;
     _Float16 *xn, *xg, *q16, *k16, *vt16, *P;
+    float *cpb = nullptr;  // an up stage's input, for its DupUp shortcut
 
     void conv(int mode, const _Float16 *in, int H, int W, const ig_conv_w &cw, const float *bias,
               float oscale, int acc, float *out, _Float16 *yg = nullptr)
@@ -433,6 +446,12 @@ struct Run {
         normed = false;
         for (int st = s0; st < s1; ++st) {
             const ig_up_w &u = d.ups[st];
+            // the stage's input, for its DupUp shortcut (its real channels
+            // decide the repeats)
+            const int cp0 = cp, c0 = u.n_res > 0 ? u.res[0].c1.cin : u.up.cin;
+            const bool dup = u.has_up && u.dupup;
+            if (dup)
+                (void)hipMemcpyAsync(cpb, x, (size_t)cur.rows() * W * cp * sizeof(float), hipMemcpyDeviceToDevice, s);
             for (int k = 0; k < u.n_res; ++k) {
                 // a stage's last resnet before its up conv emits the
                 // guarded cast itself
@@ -448,13 +467,20 @@ struct Run {
                     launch_guard_cast(x + skip * cp, f.rows() * W, cp, nullptr, g, xg, s);
                     up_in = xg;
                 }
-                if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout) {
+                if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout && !dup) {
                     // the last up conv's epilogue applies norm_out + SiLU; the
                     // f32 stream is not needed after it
                     conv_norm(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
                     normed = true;
                 } else {
                     conv(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, 0, x);
+                }
+                if (dup) {
+                    // x[2y + sy][2x + sx] += the shuffled channels of the
+                    // input's row y (the fed rows of the saved input)
+                    const int factor = 4 * u.dupup_ft, repeats = u.up.cout * factor / c0;
+                    launch_dupup(cpb + skip * cp0, f.rows(), W, cp0, x, u.up.cout, u.up.cout_p, factor, repeats,
+                                 u.dupup_ft, s);
                 }
                 cur = Span{2 * f.first, 2 * f.end};
                 W *= 2;
@@ -619,6 +645,7 @@ int run_decoder(const ig_decoder *dec, const float *latent, int h0, int w0, int 
           reinterpret_cast<_Float16 *>(w + pl.off_xn), reinterpret_cast<_Float16 *>(w + pl.off_xg),
           reinterpret_cast<_Float16 *>(w + pl.off_q), reinterpret_cast<_Float16 *>(w + pl.off_k),
           reinterpret_cast<_Float16 *>(w + pl.off_vt), reinterpret_cast<_Float16 *>(w + pl.off_p)};
+    r.cpb = reinterpret_cast<float *>(w + pl.off_cp);
     hipStream_t s = r.s;
     (void)hipGetLastError();
     // latent -> f16 NHWC -> conv_in, x = conv + b

@@ -53,6 +53,9 @@ class DeviceDecoder:
             if st.get("up") is not None:
                 d.ups[s].has_up = 1
                 d.ups[s].up = self._conv(st["up"])
+                if st.get("dupup") is not None:
+                    d.ups[s].dupup = 1
+                    d.ups[s].dupup_ft = int(st["dupup"].get("ft", 1))
         d.norm_out_gamma = self._vec(w["norm_out"], cpad(len(w["norm_out"])))
         d.norm_out_c = len(w["norm_out"])
         d.conv_out = self._conv(w["conv_out"])

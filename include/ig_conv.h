@@ -310,6 +310,7 @@ int ig_zero_rows_f16(uint16_t *y, int r0, int r1, int ld, void *stream);
  * `attention`, `run_blocks`, `output_rows`; [VAE] `VaeDecoder::decode`):
  *   f16(latent) -> conv_in -> resnet -> attention -> resnet
  *   -> per up stage: resnets, x = 2^g conv_up2(f16(x 2^-g)) + b
+ *      (+ the DupUp shuffle of the stage's input when dupup)
  *   -> f16(RMS_norm(x; norm_out) -> SiLU) -> conv_out -> NCHW output.
  * Every weight is device memory the caller owns, packed by
  * ig_pack_conv_weights; biases and gammas are f32 zero-padded to the
@@ -342,6 +343,12 @@ typedef struct ig_up_w {
     ig_resnet_w res[IG_MAX_RES];
     int has_up;   /* 1: a nearest-2x upsample conv ends the stage */
     ig_conv_w up; /* 3x3 */
+    /* 1 (with has_up): after the up conv, add the DupUp shortcut of the
+     * stage's input ([QI] `run_blocks`, DUPUP_SRC; ig_dupup_add) with
+     * factor = 4 dupup_ft and repeats = up.cout * factor / cin, cin the
+     * stage input's real channels (up.cout * factor must be a multiple of
+     * it). dupup_ft: the temporal factor, 1 for images. */
+    int dupup, dupup_ft;
 } ig_up_w;
 
 typedef struct ig_decoder {

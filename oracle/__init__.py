@@ -29,9 +29,12 @@ Sources (the pages are cited by title and item):
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (library routines, closed forms, invariants, the pages' own worked values).
-The synthetic decoder as a whole (``decode``) has no value printed on the
-pages: **parity unpinned** at the decoder level; it is pinned only through
-its parts and their composition.
+The synthetic decoder as a whole (``decode``, with ``resnet`` and
+``attention``) has no value printed on the pages; its composition -- the
+order of the steps, the bias sites, the f16 sites, the DupUp shortcut -- is
+pinned by ``tests/test_oracle_composition.py`` against a second, independent
+transcription of the pages' recipe in torch float64 built from library
+routines only, together with planted slips that this comparison catches.
 """
 
 from __future__ import annotations
@@ -343,10 +346,31 @@ def resnet(x, r, guard_log2, emulate_f16=True, trace=None):
     return x + h + b2
 
 
+def dupup(src, cout, ft=1):
+    """The DupUp shortcut of an up stage (qi21_vae.rs, DUPUP_SRC and
+    `run_blocks`): src [cin, h, w] -> [cout, 2h, 2w]; output channel o at
+    sub-pixel (sy, sx) of source pixel (y, x) is src channel
+    (o factor + 4 (ft - 1) + 2 sy + sx) // repeats of that pixel, with
+    factor = 4 ft and repeats = cout factor / cin (an integer)."""
+    src = _f64(src)
+    cin, h, w = src.shape
+    factor = 4 * int(ft)
+    assert ft >= 1 and (cout * factor) % cin == 0
+    repeats = cout * factor // cin
+    out = np.empty((cout, 2 * h, 2 * w), np.float64)
+    o = np.arange(cout)
+    for sy in (0, 1):
+        for sx in (0, 1):
+            j = (o * factor + 4 * (ft - 1) + 2 * sy + sx) // repeats
+            out[:, sy::2, sx::2] = src[j]
+    return out
+
+
 def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
     """The synthetic decoder (readings stated in the design notes):
     f16(latent) -> conv_in (+b) -> resnet -> attention -> resnet -> per up
-    stage: resnets, then x = 2^g conv_up2(f16(x 2^-g)) + b -> f16(RMSn(x;
+    stage: resnets, then x = 2^g conv_up2(f16(x 2^-g)) + b (+ the DupUp
+    shortcut of the stage's input, for stages that have one) -> f16(RMSn(x;
     norm_out) -> SiLU) -> conv_out (+b). z: NCHW [zc, h0, w0]; returns
     [out_c, 2^s h0, 2^s w0] (qi21_vae.rs, `decode`, `run_blocks`,
     `output_rows`; vae.rs, `VaeDecoder::decode`)."""
@@ -361,6 +385,7 @@ def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
     if trace is not None:
         trace.stages["mid"] = x.copy()
     for si, st in enumerate(wts["ups"]):
+        x_in = x
         for r in st["res"]:
             x = resnet(x, r, g, emulate_f16, trace)
         if trace is not None:
@@ -368,6 +393,8 @@ def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
         xg = guard_cast(x, g) if emulate_f16 else x / gs
         x = gs * conv2d_up2(xg, st["up"]["w"])
         x = x + _bcast(st["up"]["b"], x)
+        if st.get("dupup") is not None:
+            x = x + dupup(x_in, x.shape[0], st["dupup"].get("ft", 1))
         if trace is not None:
             trace.stages["up%d" % si] = x.copy() if x.size <= (1 << 24) else None
     xn = rnd(rmsnorm(x, wts["norm_out"], silu=True))

@@ -121,13 +121,14 @@ class DecoderSpec:
     """Shape of the synthetic decoder: latent channels, conv_in width, the
     channel count of each up stage, resnets per stage, output channels."""
 
-    def __init__(self, zc=16, c_in=512, stages=(512, 256, 128), n_res=2, out_c=3):
+    def __init__(self, zc=16, c_in=512, stages=(512, 256, 128), n_res=2, out_c=3, dupup=False):
         self.zc = zc
         self.c_in = c_in
         self.stages = tuple(stages)
         self.n_res = n_res
         self.out_c = out_c
         self.attn_c = c_in
+        self.dupup = bool(dupup)  # every up stage adds the DupUp shortcut of its input (ft = 1)
 
     def as_dict(self):
         return {
@@ -136,15 +137,18 @@ class DecoderSpec:
             "stages": list(self.stages),
             "n_res": self.n_res,
             "out_c": self.out_c,
+            "dupup": self.dupup,
         }
 
 
-def decoder_spec(small=False):
+def decoder_spec(small=False, dupup=False):
     """The decoder of the full-decode configurations, or a narrow copy with
-    the same structure for CPU-sized tests."""
+    the same structure for CPU-sized tests; dupup: the up stages also add
+    the DupUp shortcut of their input (stage channel pairs (in, out) then
+    take repeats 4 when in == out and 2 when in == 2 out)."""
     if small:
-        return DecoderSpec(zc=4, c_in=128, stages=(128, 64, 64), n_res=2, out_c=3)
-    return DecoderSpec()
+        return DecoderSpec(zc=4, c_in=128, stages=(128, 64, 64), n_res=2, out_c=3, dupup=dupup)
+    return DecoderSpec(dupup=dupup)
 
 
 def _conv(cfg, idx, cout, cin, k, gain=1.0):
@@ -203,6 +207,7 @@ def decoder_weights(spec: DecoderSpec, seed_config=4, conv_in_gain=1.0):
             st["res"].append(_resnet(cfg, idx, prev if r == 0 else cs, cs))
             idx += 10
         st["up"] = _conv(cfg, idx, cs, cs, 3)
+        st["dupup"] = {"ft": 1} if spec.dupup else None
         idx += 10
         d["ups"].append(st)
         prev = cs

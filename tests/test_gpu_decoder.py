@@ -156,6 +156,49 @@ def test_banded_decode_full_size_1024(full_decoder):
     assert torch.equal(banded, whole)
 
 
+@pytest.mark.parametrize("small,h0,w0", [(True, 5, 7), (True, 8, 8), (False, 32, 32)])
+def test_decoder_with_dupup(small, h0, w0):
+    """Every up stage adds the DupUp shortcut of its input (the pages'
+    `run_blocks`): stage widths (in, out) = (c, c) take repeats 4 and
+    (2c, c) repeats 2; the last stage's norm_out is not fused into its up
+    conv then. Against the oracle's decode, and banded == whole."""
+    spec = synth.decoder_spec(small=small, dupup=True)
+    w = synth.decoder_weights(spec, seed_config=4)
+    z = synth.decoder_latent(h0, w0, zc=spec.zc, config=4)
+    dd = ig.DeviceDecoder(w)
+    qc = 8 if small else 256
+    got = _run(dd, z, q_chunk=qc)
+    ref = O.decode(w, z, guard_log2=8, q_chunk=qc)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got))
+    assert _report("DupUp %s %dx%d" % ("small" if small else "full", h0, w0), got, ref) >= PSNR_MIN
+    zd = dev(z)
+    whole = dd.forward(zd, h0, w0, q_chunk=qc)
+    H = h0 << dd.n_up
+    for band_rows, band_from in ((3, 0), (H // 3 + 1, 1), (H - 1, 2)):
+        banded = dd.forward_bands(zd, h0, w0, band_rows, band_from, q_chunk=qc)
+        assert torch.equal(banded, whole), (band_rows, band_from)
+
+
+def test_decode_4096_in_bands_with_dupup():
+    """A 4096x4096 frame (latent 512x512, 262144 attention tokens), the
+    DupUp decoder with the guarded stream: up block 0 on the whole frame,
+    the rest in bands (the pages' large-frame path). Two band sizes give the
+    same frame bit for bit, and it is finite. No oracle at this size."""
+    spec = synth.decoder_spec(dupup=True)
+    w = synth.decoder_weights(spec, seed_config=4, conv_in_gain=2.0 ** 11)
+    dd = ig.DeviceDecoder(w)
+    z = dev(synth.decoder_latent(512, 512, zc=spec.zc, config=5, scale=8.0))
+    a = dd.forward_bands(z, 512, 512, 373, 1, q_chunk=0)
+    b = dd.forward_bands(z, 512, 512, 1024, 1, q_chunk=0)
+    torch.cuda.synchronize()
+    assert a.shape == (3, 4096, 4096)
+    assert bool(torch.isfinite(a).all())
+    d = float((a - b).abs().max())
+    print("4096^2 in bands of 373 and 1024 rows: max|d| %g, mean |x| %.3f" % (d, float(a.abs().mean())), flush=True)
+    assert torch.equal(a, b)
+
+
 def test_guard_on_a_stream_past_f16():
     spec = synth.decoder_spec()
     w = synth.decoder_weights(spec, seed_config=4, conv_in_gain=2.0 ** 11)

@@ -116,6 +116,16 @@ class Recipe:
             h = h + bp[:, None]
         return x + h.reshape(C, H, W)
 
+    @staticmethod
+    def dupup(src, cout, ft):
+        """The stage input's channels, each repeated cout 4 ft / cin times,
+        grouped [cout][ft][4]; chunk ft - 1 moved to the 2x grid
+        (depth-to-space)."""
+        cin, h, w = src.shape
+        rep = cout * 4 * ft // cin
+        e = src.repeat_interleave(rep, dim=0).reshape(cout, ft, 4, h, w)[:, ft - 1]
+        return F.pixel_shuffle(e.reshape(1, 4 * cout, h, w), 2)[0]
+
     def decode(self, z):
         w = self.w
         x = self.conv(self.site("z", _t(z)), w["conv_in"], with_bias=True)
@@ -124,17 +134,20 @@ class Recipe:
         x = self.resnet(x, w["mid"][1])
         gs = 2.0 ** self.g
         for st in w["ups"]:
+            x_in = x
             for r in st["res"]:
                 x = self.resnet(x, r)
             xg = self.site("xg", x / gs)
             u = F.interpolate(xg[None], scale_factor=2, mode="nearest")[0]
             x = gs * self.conv(u, st["up"]) + _t(st["up"]["b"])[:, None, None]
+            if st.get("dupup") is not None and self.skip != "dupup":
+                x = x + self.dupup(x_in, x.shape[0], st["dupup"]["ft"])
         xn = self.site("xno", self.rmsn(x, w["norm_out"], silu=True))
         return self.conv(xn, w["conv_out"], with_bias=True)
 
 
-def _wide_spec():
-    return synth.DecoderSpec(zc=4, c_in=256, stages=(256, 128, 64), n_res=2, out_c=3)
+def _wide_spec(dupup=False):
+    return synth.DecoderSpec(zc=4, c_in=256, stages=(256, 128, 64), n_res=2, out_c=3, dupup=dupup)
 
 
 def _rel(a, b):
@@ -143,17 +156,18 @@ def _rel(a, b):
     return float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
 
 
+@pytest.mark.parametrize("dupup", [False, True])
 @pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("emulate", [False, True])
-def test_decode_matches_the_recipe_transcription(wide, emulate):
-    spec = _wide_spec() if wide else synth.decoder_spec(small=True)
+def test_decode_matches_the_recipe_transcription(wide, emulate, dupup):
+    spec = _wide_spec(dupup) if wide else synth.decoder_spec(small=True, dupup=dupup)
     wts = synth.decoder_weights(spec, seed_config=4)
     z = synth.decoder_latent(4, 5 if wide else 6, zc=spec.zc)
     got = O.decode(wts, z, guard_log2=8, emulate_f16=emulate)
     want = Recipe(wts, 8, emulate).decode(z).numpy()
     assert got.shape == want.shape
     r = _rel(got, want)
-    print("decode vs transcription (wide %s, f16 sites %s): %.2e" % (wide, emulate, r))
+    print("decode vs transcription (wide %s, f16 sites %s, DupUp %s): %.2e" % (wide, emulate, dupup, r))
     assert r <= 1e-12
 
 
@@ -213,6 +227,17 @@ def test_a_slip_in_the_recipe_is_caught(skip):
     r = _rel(bad, good)
     print("slip %s: %.2e" % (skip, r))
     assert r > 1e-9
+
+
+def test_a_dropped_dupup_is_caught():
+    """With the DupUp shortcut in every up stage, leaving it out of the
+    transcription moves the decode far past the oracle's 1e-12."""
+    spec = synth.decoder_spec(small=True, dupup=True)
+    wts = synth.decoder_weights(spec, seed_config=4)
+    z = synth.decoder_latent(4, 6, zc=spec.zc)
+    good = O.decode(wts, z, guard_log2=8)
+    bad = Recipe(wts, 8, True, skip="dupup").decode(z).numpy()
+    assert _rel(bad, good) > 1e-3
 
 
 @pytest.mark.parametrize("skip", ["xna", "q", "k", "vt", "p", "o", "bp2"])
