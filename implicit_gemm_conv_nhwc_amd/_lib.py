@@ -242,11 +242,11 @@ class ConvW(ctypes.Structure):
 
 class ResnetW(ctypes.Structure):
     _fields_ = [("g1", _vp), ("c1", ConvW), ("g2", _vp), ("c2", ConvW), ("has_sc", _c_int),
-                ("sc", ConvW)]
+                ("sc", ConvW), ("beta1", _vp), ("beta2", _vp)]
 
 
 class AttnW(ctypes.Structure):
-    _fields_ = [("gamma", _vp), ("q", ConvW), ("k", ConvW), ("v", ConvW), ("proj", ConvW)]
+    _fields_ = [("gamma", _vp), ("q", ConvW), ("k", ConvW), ("v", ConvW), ("proj", ConvW), ("beta", _vp)]
 
 
 class UpW(ctypes.Structure):
@@ -257,7 +257,10 @@ class UpW(ctypes.Structure):
 class DecoderDesc(ctypes.Structure):
     _fields_ = [("zc", _c_int), ("conv_in", ConvW), ("mid", ResnetW * 2), ("attn", AttnW),
                 ("n_up", _c_int), ("ups", UpW * IG_MAX_UP), ("norm_out_gamma", _vp),
-                ("norm_out_c", _c_int), ("conv_out", ConvW)]
+                ("norm_out_c", _c_int), ("conv_out", ConvW), ("norm_kind", _c_int), ("norm_groups", _c_int),
+                ("norm_eps", _c_float), ("norm_out_beta", _vp)]
+
+IG_NORM_RMS, IG_NORM_GROUP = 0, 1
 
 
 _ws_bytes = _sig("ig_decoder_workspace_bytes", [ctypes.POINTER(DecoderDesc), _c_int, _c_int, _c_int],

@@ -96,12 +96,15 @@ struct Plan {
     int64_t max_xn = 0;  // f16 conv inputs
     int64_t max_xg = 0;  // f16 guarded shortcut input
     int64_t max_cp = 0;  // f32 up-stage input kept for its DupUp shortcut
+    int gn_groups = 0;   // GroupNorm's groups (0: RMS_norm)
+    float gn_eps = 0.f;
+    size_t max_gn = 0;   // bytes of GroupNorm's per-chunk statistics
     int m = 0, mp = 0, C = 0, qc = 0;
     bool flash = false;  // single-pass attention (else query chunks)
     int H = 0, W = 0;    // output frame
     int s = 0;           // up blocks s.. run in bands (s == n_up: none)
     int band_rows = 0;   // kept output rows per band
-    size_t off_x, off_xb, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, off_cp, total;
+    size_t off_x, off_xb, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, off_cp, off_gn, total;
 };
 
 int check_conv_w(const ig_conv_w &c, const char *name, int k)
@@ -130,10 +133,27 @@ inline void upd(int64_t &m, int64_t v)
 
 // Check one resnet against the incoming width (c, cp); returns the outgoing
 // width through c, cp.
-int check_resnet(const ig_resnet_w &r, const char *name, int &c, int &cp)
+// the decoder's norm kind and GroupNorm's groups (0 with RMS_norm)
+struct NormCfg {
+    int groups = 0;
+};
+
+// a GroupNorm site: its beta, and its widths within the kernel's reach
+int check_gn_site(const NormCfg &nc, const float *beta, int c, int cp, const char *name)
+{
+    if (!nc.groups) return IG_OK;
+    if (!beta || !aligned16(beta)) return fail(IG_EINVAL, "%s: GroupNorm beta NULL or not 16-byte aligned", name);
+    if (!gn_supported(cp, c, nc.groups))
+        return fail(IG_EUNSUPPORTED, "%s: GroupNorm(%d) over %d channels padded to %d", name, nc.groups, c, cp);
+    return IG_OK;
+}
+
+int check_resnet(const ig_resnet_w &r, const char *name, int &c, int &cp, const NormCfg &nc)
 {
     int e;
     if ((e = check_gamma(r.g1, name)) || (e = check_gamma(r.g2, name))) return e;
+    if ((e = check_gn_site(nc, r.beta1, c, cp, name))) return e;
+    if ((e = check_gn_site(nc, r.beta2, r.c1.cout, r.c1.cout_p, name))) return e;
     if ((e = check_conv_w(r.c1, name, 3)) || (e = check_conv_w(r.c2, name, 3))) return e;
     if (r.c1.cin != c || r.c1.cin_p != cp) return fail(IG_EINVAL, "%s: conv1 input %d/%d, stream is %d/%d", name, r.c1.cin, r.c1.cin_p, c, cp);
     if (r.c2.cin != r.c1.cout || r.c2.cin_p != r.c1.cout_p || r.c2.cout != r.c1.cout || r.c2.cout_p != r.c1.cout_p)
@@ -151,8 +171,19 @@ int check_resnet(const ig_resnet_w &r, const char *name, int &c, int &cp)
 }
 
 // the buffers one resnet on M pixels uses; xmax: the stream's maximum
+// GroupNorm's statistics for a site of M pixels, cp channels
+void size_gn(int64_t M, int cp, Plan &pl)
+{
+    if (pl.gn_groups && M > 0) {
+        const size_t b = gn_workspace_bytes((int)M, cp, pl.gn_groups);
+        if (b > pl.max_gn) pl.max_gn = b;
+    }
+}
+
 void size_resnet(const ig_resnet_w &r, int64_t M, int cp, int64_t &xmax, Plan &pl)
 {
+    size_gn(M, cp, pl);
+    size_gn(M, r.c1.cout_p, pl);
     if (r.has_sc) upd(pl.max_xg, M * cp);
     upd(pl.max_xn, M * cp);
     upd(pl.max_xn, M * r.c1.cout_p);
@@ -177,19 +208,28 @@ int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
     if ((e = check_conv_w(d->conv_in, "conv_in", 3))) return e;
     if (d->conv_in.cin != d->zc) return fail(IG_EINVAL, "conv_in takes %d channels, latent has %d", d->conv_in.cin, d->zc);
     int c = d->conv_in.cout, cp = d->conv_in.cout_p;
-    if ((e = check_resnet(d->mid[0], "mid.0", c, cp))) return e;
+    NormCfg nc;
+    if (d->norm_kind == IG_NORM_GROUP) {
+        if (d->norm_groups < 1 || d->norm_groups > 128) return fail(IG_EINVAL, "norm_groups=%d outside 1..128", d->norm_groups);
+        if (!(d->norm_eps >= 0.f) || d->norm_eps > 1.f) return fail(IG_EINVAL, "norm_eps=%g", (double)d->norm_eps);
+        nc.groups = d->norm_groups;
+    } else if (d->norm_kind != IG_NORM_RMS) {
+        return fail(IG_EINVAL, "norm_kind=%d", d->norm_kind);
+    }
+    if ((e = check_resnet(d->mid[0], "mid.0", c, cp, nc))) return e;
     const ig_attn_w &a = d->attn;
     if ((e = check_gamma(a.gamma, "attn"))) return e;
     const ig_conv_w *aw[4] = {&a.q, &a.k, &a.v, &a.proj};
     const char *an[4] = {"attn.q", "attn.k", "attn.v", "attn.proj"};
     if (cp != c || c % 64) return fail(IG_EUNSUPPORTED, "attention width %d must be unpadded and a multiple of 64", c);
+    if ((e = check_gn_site(nc, a.beta, c, cp, "attn"))) return e;
     for (int i = 0; i < 4; ++i) {
         if ((e = check_conv_w(*aw[i], an[i], 1))) return e;
         if (aw[i]->cin != c || aw[i]->cout != c || aw[i]->cin_p != c || aw[i]->cout_p != c)
             return fail(IG_EINVAL, "%s must map %d -> %d unpadded", an[i], c, c);
     }
     if ((int64_t)h0 * w0 >= (1LL << 30)) return fail(IG_EUNSUPPORTED, "latent too large for the attention");
-    if ((e = check_resnet(d->mid[1], "mid.1", c, cp))) return e;
+    if ((e = check_resnet(d->mid[1], "mid.1", c, cp, nc))) return e;
     int64_t H = h0, W = w0;
     for (int s = 0; s < d->n_up; ++s) {
         const ig_up_w &u = d->ups[s];
@@ -199,7 +239,7 @@ int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
         for (int r = 0; r < u.n_res; ++r) {
             char nm[32];
             snprintf(nm, sizeof nm, "ups.%d.res.%d", s, r);
-            if ((e = check_resnet(u.res[r], nm, c, cp))) return e;
+            if ((e = check_resnet(u.res[r], nm, c, cp, nc))) return e;
         }
         if (u.has_up) {
             char nm[32];
@@ -224,6 +264,7 @@ int check_decoder(const ig_decoder *d, int h0, int w0, Widths &wd, Plan &pl)
     }
     if ((e = check_gamma(d->norm_out_gamma, "norm_out"))) return e;
     if (d->norm_out_c != c) return fail(IG_EINVAL, "norm_out has %d channels, stream %d", d->norm_out_c, c);
+    if ((e = check_gn_site(nc, d->norm_out_beta, c, cp, "norm_out"))) return e;
     if ((e = check_conv_w(d->conv_out, "conv_out", 3))) return e;
     if (d->conv_out.cin != c || d->conv_out.cin_p != cp) return fail(IG_EINVAL, "conv_out input %d, stream %d", d->conv_out.cin, c);
     pl.H = (int)H;
@@ -260,6 +301,7 @@ void size_blocks(const ig_decoder &d, int s0, int s1, int rows, int W, const Spa
     if (fin) {
         const int64_t M = (int64_t)rows * W;
         upd(pl.max_xn, M * cp);
+        size_gn(M, cp, pl);
         if (d.conv_out.cout > 16) upd(pl.max_h, M * d.conv_out.cout_p);  // else straight to the frame
     }
 }
@@ -277,6 +319,12 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     Widths wd;
     int e = check_decoder(d, h0, w0, wd, pl);
     if (e) return e;
+    if (d->norm_kind == IG_NORM_GROUP) {
+        pl.gn_groups = d->norm_groups;
+        pl.gn_eps = d->norm_eps;
+        if (band_rows > 0 && band_from >= 0 && band_from < d->n_up)
+            return fail(IG_EUNSUPPORTED, "GroupNorm's statistics span the frame: a GroupNorm decoder does not run in bands");
+    }
     pl.s = (band_rows > 0 && band_from >= 0 && band_from < d->n_up) ? band_from : d->n_up;
     pl.band_rows = pl.s < d->n_up ? band_rows : 0;
     // conv_in, the mid block and its attention run on the latent grid
@@ -292,6 +340,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     pl.qc = q_chunk > 0 ? q_chunk : 16384;
     if (pl.qc > pl.m) pl.qc = pl.m;
     upd(pl.max_xn, (int64_t)pl.mp * c);
+    size_gn(pl.m, c, pl);
     if (!pl.flash && (uint64_t)pl.qc * pl.mp * 2 >= (3ULL << 30))
         return fail(IG_EUNSUPPORTED, "query chunk %d x %d keys: probabilities exceed 3 GiB; pass a smaller q_chunk", pl.qc, pl.mp);
     size_resnet(d->mid[1], M, c, pl.max_x, pl);
@@ -331,6 +380,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     pl.off_k = take(mp * C * 2);
     pl.off_vt = take(C * mp * 2);
     pl.off_cp = take(pl.max_cp * 4);
+    pl.off_gn = take(pl.max_gn);
     if (pl.flash) {
         // the single-pass kernel's key-range partials (if any)
         pl.off_o = take(0);
@@ -355,6 +405,17 @@ struct Run {
     float *x, *h, *o32, *S;
     _Float16 *xn, *xg, *q16, *k16, *vt16, *P;
     float *cpb = nullptr;  // an up stage's input, for its DupUp shortcut
+    void *gnws = nullptr;  // GroupNorm's statistics
+
+    // the decoder's norm of M pixels (+ bias on read, + SiLU) -> f16 y
+    void norm(const float *in, int M, int cp, int c_real, const float *bias, const float *gamma, const float *beta,
+              int silu, _Float16 *y)
+    {
+        if (pl.gn_groups)
+            launch_groupnorm(in, M, cp, c_real, pl.gn_groups, bias, gamma, beta, silu, pl.gn_eps, gnws, y, s);
+        else
+            launch_rmsnorm(in, M, cp, c_real, bias, gamma, silu, kEps, y, s);
+    }
 
     void conv(int mode, const _Float16 *in, int H, int W, const ig_conv_w &cw, const float *bias,
               float oscale, int acc, float *out, _Float16 *yg = nullptr)
@@ -467,7 +528,7 @@ struct Run {
                     launch_guard_cast(x + skip * cp, f.rows() * W, cp, nullptr, g, xg, s);
                     up_in = xg;
                 }
-                if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout && !dup) {
+                if (st == d.n_up - 1 && fusable(u.up) && d.norm_out_c == u.up.cout && !dup && !pl.gn_groups) {
                     // the last up conv's epilogue applies norm_out + SiLU; the
                     // f32 stream is not needed after it
                     conv_norm(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
@@ -495,7 +556,7 @@ struct Run {
     void output(const ig_decoder &d, Span cur, int W, int cp, bool normed, Span keep, int Hf, float *out)
     {
         const int H = cur.rows();
-        if (!normed) launch_rmsnorm(x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, 1, kEps, xn, s);
+        if (!normed) norm(x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, d.norm_out_beta, 1, xn);
         float *o = out + (int64_t)cur.first * W;
         const int64_t plane = (int64_t)Hf * W;
         if (d.conv_out.cout <= 16) {
@@ -517,15 +578,19 @@ struct Run {
     void resnet(const ig_resnet_w &r, int H, int W, int cp, _Float16 *cast = nullptr)
     {
         const int M = H * W;
-        if (r.has_sc) {
+        if (r.has_sc && !pl.gn_groups) {
             // one read of the stream gives the norm and the shortcut's
             // guarded input
             launch_rmsnorm(x, M, cp, r.c1.cin, nullptr, r.g1, 1, kEps, xn, s, xg, g);
             conv(kGemm, xg, H, W, r.sc, r.sc.b, ldexpf(1.f, g), 0, x);
         } else {
-            launch_rmsnorm(x, M, cp, r.c1.cin, nullptr, r.g1, 1, kEps, xn, s);
+            norm(x, M, cp, r.c1.cin, nullptr, r.g1, r.beta1, 1, xn);
+            if (r.has_sc) {
+                launch_guard_cast(x, M, cp, nullptr, g, xg, s);
+                conv(kGemm, xg, H, W, r.sc, r.sc.b, ldexpf(1.f, g), 0, x);
+            }
         }
-        if (fusable(r.c1)) {
+        if (fusable(r.c1) && !pl.gn_groups) {
             // conv1's epilogue normalises (h + b1) itself; the f16 result
             // goes to the h region (conv1 still reads xn)
             _Float16 *hn = reinterpret_cast<_Float16 *>(h);
@@ -533,7 +598,7 @@ struct Run {
             conv(kConv3x3, hn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast);
         } else {
             conv(kConv3x3, xn, H, W, r.c1, nullptr, 1.f, 0, h);
-            launch_rmsnorm(h, M, r.c1.cout_p, r.c1.cout, r.c1.b, r.g2, 1, kEps, xn, s);
+            norm(h, M, r.c1.cout_p, r.c1.cout, r.c1.b, r.g2, r.beta2, 1, xn);
             conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast);
         }
     }
@@ -542,7 +607,7 @@ struct Run {
     void attention(const ig_attn_w &a)
     {
         const int m = pl.m, mp = pl.mp, C = pl.C, qc = pl.qc;
-        launch_rmsnorm(x, m, C, C, nullptr, a.gamma, 0, kEps, xn, s);
+        norm(x, m, C, C, nullptr, a.gamma, a.beta, 0, xn);
         launch_zero_rows_f16(xn, m, mp, C, s);
         const _Float16 *wq = reinterpret_cast<const _Float16 *>(a.q.w);
         const _Float16 *wk = reinterpret_cast<const _Float16 *>(a.k.w);
@@ -646,6 +711,7 @@ int run_decoder(const ig_decoder *dec, const float *latent, int h0, int w0, int 
           reinterpret_cast<_Float16 *>(w + pl.off_q), reinterpret_cast<_Float16 *>(w + pl.off_k),
           reinterpret_cast<_Float16 *>(w + pl.off_vt), reinterpret_cast<_Float16 *>(w + pl.off_p)};
     r.cpb = reinterpret_cast<float *>(w + pl.off_cp);
+    r.gnws = w + pl.off_gn;
     hipStream_t s = r.s;
     (void)hipGetLastError();
     // latent -> f16 NHWC -> conv_in, x = conv + b

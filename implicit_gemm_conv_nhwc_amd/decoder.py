@@ -41,6 +41,16 @@ class DeviceDecoder:
         d.attn.k = self._conv(a["k"])
         d.attn.v = self._conv(a["v"])
         d.attn.proj = self._conv(a["proj"])
+        # the norm: RMS_norm, or GroupNorm with a beta at every site
+        nk = w.get("norm") or {"kind": "rms"}
+        self.group_norm = nk["kind"] == "group"
+        if self.group_norm:
+            d.norm_kind = L.IG_NORM_GROUP
+            d.norm_groups = int(nk["groups"])
+            d.norm_eps = float(nk["eps"])
+            d.attn.beta = self._vec(a["beta"], cpad(len(a["beta"])))
+        elif nk["kind"] != "rms":
+            raise ValueError("norm kind %r" % nk["kind"])
         if len(w["ups"]) > L.IG_MAX_UP:
             raise ValueError("too many up stages")
         d.n_up = len(w["ups"])
@@ -58,6 +68,8 @@ class DeviceDecoder:
                     d.ups[s].dupup_ft = int(st["dupup"].get("ft", 1))
         d.norm_out_gamma = self._vec(w["norm_out"], cpad(len(w["norm_out"])))
         d.norm_out_c = len(w["norm_out"])
+        if self.group_norm:
+            d.norm_out_beta = self._vec(w["norm_out_beta"], cpad(len(w["norm_out_beta"])))
         d.conv_out = self._conv(w["conv_out"])
         self.desc = d
         self.out_c = int(np.asarray(w["conv_out"]["b"]).shape[0])
@@ -101,6 +113,9 @@ class DeviceDecoder:
         if r.get("sc") is not None:
             rw.has_sc = 1
             rw.sc = self._conv(r["sc"])
+        if r.get("beta1") is not None:
+            rw.beta1 = self._vec(r["beta1"], cpad(len(r["beta1"])))
+            rw.beta2 = self._vec(r["beta2"], cpad(len(r["beta2"])))
         return rw
 
     # -- running -------------------------------------------------------------

@@ -49,6 +49,9 @@ extern "C" {
 
 #define IG_MAX_RES 4 /* resnet units per up stage */
 #define IG_MAX_UP 8  /* up stages */
+/* the decoder's norm (ig_decoder.norm_kind): */
+#define IG_NORM_RMS 0   /* RMS_norm, x / max(|x|, 1e-12) sqrt(C) gamma ([QI] RMSN_SRC) */
+#define IG_NORM_GROUP 1 /* GroupNorm(norm_groups, norm_eps) with gamma and beta ([VAE] GroupNorm) */
 
 /* Text of the last error on the calling thread ("" if none). */
 const char *ig_last_error(void);
@@ -331,11 +334,13 @@ typedef struct ig_resnet_w {
     ig_conv_w c2;    /* 3x3 cout -> cout */
     int has_sc;      /* 1: a 1x1 shortcut cin -> cout (guarded input) */
     ig_conv_w sc;
+    const float *beta1, *beta2; /* [cin_p], [cout_p]: GroupNorm's beta (IG_NORM_GROUP only) */
 } ig_resnet_w;
 
 typedef struct ig_attn_w {
     const float *gamma;      /* [c] RMS_norm gamma (no SiLU) */
     ig_conv_w q, k, v, proj; /* 1x1 c -> c; c % 64 == 0, unpadded */
+    const float *beta;       /* [c] GroupNorm's beta (IG_NORM_GROUP only) */
 } ig_attn_w;
 
 typedef struct ig_up_w {
@@ -361,6 +366,16 @@ typedef struct ig_decoder {
     const float *norm_out_gamma; /* [cp] */
     int norm_out_c;              /* real channels of norm_out */
     ig_conv_w conv_out;          /* 3x3 c -> out channels (<= 64) */
+    /* The norm of every norm site (the resnets' two, the attention's,
+     * norm_out): IG_NORM_RMS (0; eps 1e-12; betas unused) or IG_NORM_GROUP
+     * (a FLUX-class decoder, [VAE] `VaeDecoder::decode`: GroupNorm over
+     * norm_groups groups of the real channels, eps norm_eps, with the
+     * betas; each site's real width a multiple of norm_groups, padded
+     * width <= 1024, groups <= 128). GroupNorm's statistics span the frame,
+     * so a GroupNorm decoder does not run in bands (IG_EUNSUPPORTED). */
+    int norm_kind, norm_groups;
+    float norm_eps;
+    const float *norm_out_beta; /* [cp] */
 } ig_decoder;
 
 /* Workspace bytes decoder_forward needs for an h0 x w0 latent. q_chunk

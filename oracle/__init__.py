@@ -248,6 +248,15 @@ def group_norm(x, groups, gamma, beta, bias=None, silu=False, eps=1e-6):
     return y.reshape(x.shape)
 
 
+def norm_site(x, gamma, beta=None, bias=None, silu=False, norm=None):
+    """A norm site of the decoder: RMS_norm (norm None or kind "rms"), or,
+    for a FLUX-class decoder (vae.rs, `VaeDecoder::decode`), GroupNorm with
+    the site's beta (norm {"kind": "group", "groups", "eps"})."""
+    if norm is None or norm.get("kind", "rms") == "rms":
+        return rmsnorm(x, gamma, bias=bias, silu=silu)
+    return group_norm(x, norm["groups"], gamma, beta, bias=bias, silu=silu, eps=norm["eps"])
+
+
 # ---------------------------------------------------------------------------
 # attention (single head over the pixels)
 # ---------------------------------------------------------------------------
@@ -276,17 +285,18 @@ def attention_core(q, k, vt, bv=None):
     return o, p
 
 
-def attention(x, a, q_chunk=None, emulate_f16=True):
+def attention(x, a, q_chunk=None, emulate_f16=True, norm=None):
     """The mid attention on the stream x [C, m] (qi21_vae.rs, `attention`;
     vae.rs, `AttnBlock::apply`): xn = f16(RMS_norm(x; gamma_a)) (no SiLU);
     q = f16(Wq xn + bq); k = f16(Wk xn + bk); V^T = f16(Wv xn) with V's bias
     deferred past P.V; per block of query rows S = q k^T / sqrt(C),
     P = f16(softmax(S)), O = P V; then x + Wp f16(O + bv) + bp.
-    Query rows are independent, so the row blocks change nothing."""
+    Query rows are independent, so the row blocks change nothing. norm:
+    the decoder's norm kind (see ``norm_site``)."""
     rnd = f16 if emulate_f16 else _f64
     x = _f64(x)
     C, m = x.shape
-    xn = rnd(rmsnorm(x, a["gamma"], silu=False))
+    xn = rnd(norm_site(x, a["gamma"], a.get("beta"), silu=False, norm=norm))
 
     def w2(name):
         return _f64(a[name]["w"]).reshape(C, C), _f64(a[name]["b"])
@@ -325,15 +335,16 @@ class Trace:
         self.stages = {}
 
 
-def resnet(x, r, guard_log2, emulate_f16=True, trace=None):
+def resnet(x, r, guard_log2, emulate_f16=True, trace=None, norm=None):
     """One resnet unit on the stream x [cin, h, w] (qi21_vae.rs,
     `Rec::resnet`): xn = f16(RMSn(x; g1) -> SiLU); h = conv1(xn);
     xn = f16(RMSn(h + b1; g2) -> SiLU); h = conv2(xn); with a 1x1 shortcut
-    x = 2^g conv_sc(f16(x 2^-g)) + b_sc + h + b2, else x = x + h + b2."""
+    x = 2^g conv_sc(f16(x 2^-g)) + b_sc + h + b2, else x = x + h + b2.
+    norm: the decoder's norm kind (see ``norm_site``)."""
     rnd = f16 if emulate_f16 else _f64
-    xn = rnd(rmsnorm(x, r["g1"], silu=True))
+    xn = rnd(norm_site(x, r["g1"], r.get("beta1"), silu=True, norm=norm))
     h = conv2d(xn, r["c1"]["w"])
-    xn = rnd(rmsnorm(h, r["g2"], bias=r["c1"]["b"], silu=True))
+    xn = rnd(norm_site(h, r["g2"], r.get("beta2"), bias=r["c1"]["b"], silu=True, norm=norm))
     h = conv2d(xn, r["c2"]["w"])
     b2 = _bcast(r["c2"]["b"], h)
     if r.get("sc") is not None:
@@ -371,23 +382,25 @@ def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
     f16(latent) -> conv_in (+b) -> resnet -> attention -> resnet -> per up
     stage: resnets, then x = 2^g conv_up2(f16(x 2^-g)) + b (+ the DupUp
     shortcut of the stage's input, for stages that have one) -> f16(RMSn(x;
-    norm_out) -> SiLU) -> conv_out (+b). z: NCHW [zc, h0, w0]; returns
+    norm_out) -> SiLU) -> conv_out (+b); with wts["norm"] of kind "group",
+    GroupNorm (with the sites' betas) at every norm site instead. z: NCHW [zc, h0, w0]; returns
     [out_c, 2^s h0, 2^s w0] (qi21_vae.rs, `decode`, `run_blocks`,
     `output_rows`; vae.rs, `VaeDecoder::decode`)."""
     rnd = f16 if emulate_f16 else _f64
     g = int(guard_log2)
     gs = 2.0 ** g
+    nk = wts.get("norm")
     x = conv2d(rnd(z), wts["conv_in"]["w"], wts["conv_in"]["b"])
-    x = resnet(x, wts["mid"][0], g, emulate_f16, trace)
+    x = resnet(x, wts["mid"][0], g, emulate_f16, trace, nk)
     C, h, w = x.shape
-    x = attention(x.reshape(C, h * w), wts["attn"], q_chunk, emulate_f16).reshape(C, h, w)
-    x = resnet(x, wts["mid"][1], g, emulate_f16, trace)
+    x = attention(x.reshape(C, h * w), wts["attn"], q_chunk, emulate_f16, nk).reshape(C, h, w)
+    x = resnet(x, wts["mid"][1], g, emulate_f16, trace, nk)
     if trace is not None:
         trace.stages["mid"] = x.copy()
     for si, st in enumerate(wts["ups"]):
         x_in = x
         for r in st["res"]:
-            x = resnet(x, r, g, emulate_f16, trace)
+            x = resnet(x, r, g, emulate_f16, trace, nk)
         if trace is not None:
             trace.guard_max.append(float(np.max(np.abs(x))))
         xg = guard_cast(x, g) if emulate_f16 else x / gs
@@ -397,7 +410,7 @@ def decode(wts, z, guard_log2=8, q_chunk=None, emulate_f16=True, trace=None):
             x = x + dupup(x_in, x.shape[0], st["dupup"].get("ft", 1))
         if trace is not None:
             trace.stages["up%d" % si] = x.copy() if x.size <= (1 << 24) else None
-    xn = rnd(rmsnorm(x, wts["norm_out"], silu=True))
+    xn = rnd(norm_site(x, wts["norm_out"], wts.get("norm_out_beta"), silu=True, norm=nk))
     return conv2d(xn, wts["conv_out"]["w"], wts["conv_out"]["b"])
 
 

@@ -121,7 +121,8 @@ class DecoderSpec:
     """Shape of the synthetic decoder: latent channels, conv_in width, the
     channel count of each up stage, resnets per stage, output channels."""
 
-    def __init__(self, zc=16, c_in=512, stages=(512, 256, 128), n_res=2, out_c=3, dupup=False):
+    def __init__(self, zc=16, c_in=512, stages=(512, 256, 128), n_res=2, out_c=3, dupup=False, norm="rms",
+                 groups=32, eps=1e-6):
         self.zc = zc
         self.c_in = c_in
         self.stages = tuple(stages)
@@ -129,6 +130,12 @@ class DecoderSpec:
         self.out_c = out_c
         self.attn_c = c_in
         self.dupup = bool(dupup)  # every up stage adds the DupUp shortcut of its input (ft = 1)
+        # every norm site: RMS_norm, or GroupNorm(groups, eps) with a beta
+        # (a FLUX-class decoder)
+        assert norm in ("rms", "group")
+        self.norm = norm
+        self.groups = int(groups)
+        self.eps = float(eps)
 
     def as_dict(self):
         return {
@@ -138,17 +145,19 @@ class DecoderSpec:
             "n_res": self.n_res,
             "out_c": self.out_c,
             "dupup": self.dupup,
+            "norm": self.norm,
         }
 
 
-def decoder_spec(small=False, dupup=False):
+def decoder_spec(small=False, dupup=False, norm="rms"):
     """The decoder of the full-decode configurations, or a narrow copy with
     the same structure for CPU-sized tests; dupup: the up stages also add
     the DupUp shortcut of their input (stage channel pairs (in, out) then
-    take repeats 4 when in == out and 2 when in == 2 out)."""
+    take repeats 4 when in == out and 2 when in == 2 out); norm "group":
+    GroupNorm(32, 1e-6) at every norm site instead of RMS_norm."""
     if small:
-        return DecoderSpec(zc=4, c_in=128, stages=(128, 64, 64), n_res=2, out_c=3, dupup=dupup)
-    return DecoderSpec(dupup=dupup)
+        return DecoderSpec(zc=4, c_in=128, stages=(128, 64, 64), n_res=2, out_c=3, dupup=dupup, norm=norm)
+    return DecoderSpec(dupup=dupup, norm=norm)
 
 
 def _conv(cfg, idx, cout, cin, k, gain=1.0):
@@ -163,7 +172,7 @@ def _gamma(cfg, idx, c):
     return uniform(cfg, idx, (c,), 0.5, 1.5)
 
 
-def _resnet(cfg, idx, cin, cout):
+def _resnet(cfg, idx, cin, cout, group_norm=False):
     r = {
         "g1": _gamma(cfg, idx, cin),
         "c1": _conv(cfg, idx + 1, cout, cin, 3),
@@ -173,6 +182,9 @@ def _resnet(cfg, idx, cin, cout):
     }
     if cin != cout:
         r["sc"] = _conv(cfg, idx + 6, cout, cin, 1)
+    if group_norm:
+        r["beta1"] = normal(cfg, idx + 8, (cin,), 0.02)
+        r["beta2"] = normal(cfg, idx + 9, (cout,), 0.02)
     return r
 
 
@@ -180,31 +192,35 @@ def decoder_weights(spec: DecoderSpec, seed_config=4, conv_in_gain=1.0):
     """Weights of the synthetic decoder.
 
     3x3 convs ~ N(0, 1/(9 cin)), 1x1 convs and attention projections
-    ~ N(0, 1/cin), biases ~ N(0, 0.02), gammas ~ U(0.5, 1.5), every weight
-    rounded to f16. ``conv_in_gain`` (a power of two) scales conv_in's
+    ~ N(0, 1/cin), biases (and GroupNorm's betas) ~ N(0, 0.02), gammas
+    ~ U(0.5, 1.5), every weight rounded to f16. ``conv_in_gain`` (a power of two) scales conv_in's
     weights; the full-decode configuration uses it to push the residual
     stream past the f16 range.
     """
     cfg = seed_config
     idx = 100
     d = {"spec": spec.as_dict()}
+    gn = spec.norm == "group"
+    d["norm"] = {"kind": "group", "groups": spec.groups, "eps": spec.eps} if gn else {"kind": "rms"}
     d["conv_in"] = _conv(cfg, idx, spec.c_in, spec.zc, 3, conv_in_gain)
     idx += 10
     d["mid"] = []
     for _ in range(2):
-        d["mid"].append(_resnet(cfg, idx, spec.c_in, spec.c_in))
+        d["mid"].append(_resnet(cfg, idx, spec.c_in, spec.c_in, gn))
         idx += 10
     c = spec.attn_c
     d["attn"] = {"gamma": _gamma(cfg, idx, c)}
     for j, name in enumerate(("q", "k", "v", "proj")):
         d["attn"][name] = _conv(cfg, idx + 1 + 2 * j, c, c, 1)
+    if gn:
+        d["attn"]["beta"] = normal(cfg, idx + 9, (c,), 0.02)
     idx += 10
     d["ups"] = []
     prev = spec.c_in
     for cs in spec.stages:
         st = {"res": []}
         for r in range(spec.n_res):
-            st["res"].append(_resnet(cfg, idx, prev if r == 0 else cs, cs))
+            st["res"].append(_resnet(cfg, idx, prev if r == 0 else cs, cs, gn))
             idx += 10
         st["up"] = _conv(cfg, idx, cs, cs, 3)
         st["dupup"] = {"ft": 1} if spec.dupup else None
@@ -213,6 +229,8 @@ def decoder_weights(spec: DecoderSpec, seed_config=4, conv_in_gain=1.0):
         prev = cs
     d["norm_out"] = _gamma(cfg, idx, prev)
     d["conv_out"] = _conv(cfg, idx + 1, spec.out_c, prev, 3)
+    if gn:
+        d["norm_out_beta"] = normal(cfg, idx + 3, (prev,), 0.02)
     return d
 
 

@@ -180,6 +180,33 @@ def test_decoder_with_dupup(small, h0, w0):
         assert torch.equal(banded, whole), (band_rows, band_from)
 
 
+@pytest.mark.parametrize("small,h0,w0,dupup", [(True, 5, 7, False), (True, 8, 8, True), (False, 32, 32, False)])
+def test_group_norm_decoder(small, h0, w0, dupup):
+    """A FLUX-class decoder: GroupNorm(32, 1e-6) with betas at every norm
+    site instead of RMS_norm (the conv kernels unchanged; the epilogue norm
+    fusions are off, GroupNorm needs the frame's statistics). Against the
+    oracle's decode of the same weights."""
+    spec = synth.decoder_spec(small=small, dupup=dupup, norm="group")
+    w = synth.decoder_weights(spec, seed_config=4)
+    z = synth.decoder_latent(h0, w0, zc=spec.zc, config=4)
+    dd = ig.DeviceDecoder(w)
+    qc = 8 if small else 256
+    got = _run(dd, z, q_chunk=qc)
+    ref = O.decode(w, z, guard_log2=8, q_chunk=qc)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got))
+    assert _report("GroupNorm %s %dx%d%s" % ("small" if small else "full", h0, w0, " + DupUp" if dupup else ""),
+                   got, ref) >= PSNR_MIN
+
+
+def test_group_norm_decoder_refuses_bands():
+    spec = synth.decoder_spec(small=True, norm="group")
+    dd = ig.DeviceDecoder(synth.decoder_weights(spec, seed_config=4))
+    with pytest.raises(ig.IgError) as e:
+        dd.forward_bands(dev(synth.decoder_latent(4, 4, zc=spec.zc)), 4, 4, 8, 1, q_chunk=8)
+    assert "GroupNorm" in str(e.value)
+
+
 def test_decode_4096_in_bands_with_dupup():
     """A 4096x4096 frame (latent 512x512, 262144 attention tokens), the
     DupUp decoder with the guarded stream: up block 0 on the whole frame,

@@ -73,11 +73,23 @@ class Recipe:
         y = F.normalize(v, dim=0, eps=1e-12) * math.sqrt(v.shape[0]) * _t(gamma)[:, None, None]
         return F.silu(y) if silu else y
 
+    def norm(self, x, gamma, beta=None, bias=None, silu=False):
+        """The decoder's norm site: RMS_norm, or for a decoder whose norm
+        is "group" F.group_norm with the site's beta (vae.rs, GroupNorm;
+        the device recipe adds the conv bias on read), optional SiLU."""
+        nk = self.w.get("norm") or {"kind": "rms"}
+        if nk["kind"] == "rms":
+            return self.rmsn(x, gamma, bias, silu)
+        v = x if bias is None else x + _t(bias)[:, None, None]
+        bt = None if self.skip == "beta" else _t(beta)
+        y = F.group_norm(v[None], nk["groups"], _t(gamma), bt, eps=nk["eps"])[0]
+        return F.silu(y) if silu else y
+
     def resnet(self, x, r):
-        xn = self.site("xn1", self.rmsn(x, r["g1"], silu=True))
+        xn = self.site("xn1", self.norm(x, r["g1"], r.get("beta1"), silu=True))
         h = self.conv(xn, r["c1"])
         b1 = None if self.skip == "b1" else r["c1"]["b"]
-        xn = self.site("xn2", self.rmsn(h, r["g2"], bias=b1, silu=True))
+        xn = self.site("xn2", self.norm(h, r["g2"], r.get("beta2"), bias=b1, silu=True))
         h = self.conv(xn, r["c2"])
         b2 = _t(r["c2"]["b"])[:, None, None]
         if r.get("sc") is None:
@@ -92,7 +104,7 @@ class Recipe:
         a = self.w["attn"]
         C, H, W = x.shape
         m = H * W
-        xn = self.site("xna", self.rmsn(x, a["gamma"], silu=False)).reshape(C, m)
+        xn = self.site("xna", self.norm(x, a["gamma"], a.get("beta"), silu=False)).reshape(C, m)
 
         def lin(name):
             return _t(a[name]["w"]).reshape(C, C), _t(a[name]["b"])
@@ -142,12 +154,12 @@ class Recipe:
             x = gs * self.conv(u, st["up"]) + _t(st["up"]["b"])[:, None, None]
             if st.get("dupup") is not None and self.skip != "dupup":
                 x = x + self.dupup(x_in, x.shape[0], st["dupup"]["ft"])
-        xn = self.site("xno", self.rmsn(x, w["norm_out"], silu=True))
+        xn = self.site("xno", self.norm(x, w["norm_out"], w.get("norm_out_beta"), silu=True))
         return self.conv(xn, w["conv_out"], with_bias=True)
 
 
-def _wide_spec(dupup=False):
-    return synth.DecoderSpec(zc=4, c_in=256, stages=(256, 128, 64), n_res=2, out_c=3, dupup=dupup)
+def _wide_spec(dupup=False, norm="rms"):
+    return synth.DecoderSpec(zc=4, c_in=256, stages=(256, 128, 64), n_res=2, out_c=3, dupup=dupup, norm=norm)
 
 
 def _rel(a, b):
@@ -156,18 +168,19 @@ def _rel(a, b):
     return float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
 
 
+@pytest.mark.parametrize("norm", ["rms", "group"])
 @pytest.mark.parametrize("dupup", [False, True])
 @pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("emulate", [False, True])
-def test_decode_matches_the_recipe_transcription(wide, emulate, dupup):
-    spec = _wide_spec(dupup) if wide else synth.decoder_spec(small=True, dupup=dupup)
+def test_decode_matches_the_recipe_transcription(wide, emulate, dupup, norm):
+    spec = _wide_spec(dupup, norm) if wide else synth.decoder_spec(small=True, dupup=dupup, norm=norm)
     wts = synth.decoder_weights(spec, seed_config=4)
     z = synth.decoder_latent(4, 5 if wide else 6, zc=spec.zc)
     got = O.decode(wts, z, guard_log2=8, emulate_f16=emulate)
     want = Recipe(wts, 8, emulate).decode(z).numpy()
     assert got.shape == want.shape
     r = _rel(got, want)
-    print("decode vs transcription (wide %s, f16 sites %s, DupUp %s): %.2e" % (wide, emulate, dupup, r))
+    print("decode vs transcription (wide %s, f16 sites %s, DupUp %s, %s): %.2e" % (wide, emulate, dupup, norm, r))
     assert r <= 1e-12
 
 
@@ -226,6 +239,21 @@ def test_a_slip_in_the_recipe_is_caught(skip):
     bad = Recipe(wts, 8, True, skip=skip).decode(z).numpy()
     r = _rel(bad, good)
     print("slip %s: %.2e" % (skip, r))
+    assert r > 1e-9
+
+
+@pytest.mark.parametrize("skip", ["beta", "b1", "xn1", "xno"])
+def test_a_slip_in_the_group_norm_decoder_is_caught(skip):
+    """The GroupNorm decoder: its betas dropped, conv1's bias not added on
+    the second norm's read, or an f16 site skipped, each moves the decode
+    far past the oracle's 1e-12."""
+    spec = synth.decoder_spec(small=True, norm="group")
+    wts = synth.decoder_weights(spec, seed_config=4)
+    z = synth.decoder_latent(4, 6, zc=spec.zc)
+    good = O.decode(wts, z, guard_log2=8)
+    bad = Recipe(wts, 8, True, skip=skip).decode(z).numpy()
+    r = _rel(bad, good)
+    print("GroupNorm decoder slip %s: %.2e" % (skip, r))
     assert r > 1e-9
 
 
