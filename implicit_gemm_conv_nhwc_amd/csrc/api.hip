@@ -422,11 +422,12 @@ int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols,
 size_t ig_attention_workspace_bytes(int m, int C)
 {
     clear_error();
-    if (m <= 0 || C != 512) {
-        fail(C != 512 ? IG_EUNSUPPORTED : IG_EINVAL, "attention m=%d C=%d (C must be 512)", m, C);
+    const bool width_ok = C == 128 || C == 256 || C == 384 || C == 512;
+    if (m <= 0 || !width_ok) {
+        fail(!width_ok ? IG_EUNSUPPORTED : IG_EINVAL, "attention m=%d C=%d (C must be 128, 256, 384 or 512)", m, C);
         return 0;
     }
-    return flash_workspace_bytes(m);
+    return flash_workspace_bytes(m, C);
 }
 
 int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int m, int ld, int C,
@@ -434,7 +435,8 @@ int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int 
 {
     clear_error();
     if (m <= 0 || m >= (1 << 22)) return fail(IG_EINVAL, "attention m=%d outside 1..2^22-1", m);
-    if (C != 512) return fail(IG_EUNSUPPORTED, "attention width %d: the single-pass kernel takes 512", C);
+    if (C != 128 && C != 256 && C != 384 && C != 512)
+        return fail(IG_EUNSUPPORTED, "attention width %d: the single-pass kernel takes 128, 256, 384 or 512", C);
     if (!flash_supported(m, ld, C))
         return fail(IG_EINVAL, "ld=%d must be >= m rounded up to 32 (%d), a multiple of 8, and ld*C*2 below %lld bytes",
                     ld, (m + 31) / 32 * 32, (long long)kConvInMaxBytes);
@@ -443,7 +445,7 @@ int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int 
         (r = check_ptr(out, "out", true)))
         return r;
     if (bv && (r = check_ptr(bv, "bv", true))) return r;
-    const size_t need = flash_workspace_bytes(m);
+    const size_t need = flash_workspace_bytes(m, C);
     if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15)))
         return fail(IG_EWORKSPACE, "attention workspace of %zu bytes, %zu needed (16-byte aligned)", ws_bytes, need);
     FlashArgs a{};
@@ -452,6 +454,7 @@ int attention_f16(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int 
     a.vt = reinterpret_cast<const _Float16 *>(vt);
     a.ld = ld;
     a.m = m;
+    a.c = C;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)C));
     a.bv = bv;
     a.out = reinterpret_cast<_Float16 *>(out);

@@ -1,5 +1,6 @@
 // The mid attention's core in one pass over the keys, for gfx950:
-// out[i] = f16( sum_j softmax_j(q_i . k_j / sqrt(C)) v_j + bv ),  C = 512.
+// out[i] = f16( sum_j softmax_j(q_i . k_j / sqrt(C)) v_j + bv ),
+// C = 128, 256, 384 or 512.
 //
 // Page "cortiq-engine 0.8.3, src/gpu_wgpu/qi21_vae.rs", `attention`: S =
 // Q.K^T / sqrt(C) in f32, a row softmax to f16 P, O = P.V, V's bias added
@@ -13,11 +14,11 @@
 //
 // Design:
 //  * a workgroup of 4 wave64s (one per SIMD) owns 128 queries, a wave 32 of
-//    them. A wave keeps its queries' 512-wide rows in registers as the B
-//    operand of v_mfma_f32_32x32x16_f16 (128 VGPRs) and its output rows as
-//    16 f32 accumulator tiles (256 registers);
-//  * keys advance 32 per block: the block's K rows (32 x 512) and V^T
-//    columns (512 x 32) stream into double-buffered LDS by direct-to-LDS
+//    them. A wave keeps its queries' C-wide rows in registers as the B
+//    operand of v_mfma_f32_32x32x16_f16 (C / 4 VGPRs: 128 at C = 512) and
+//    its output rows as C / 32 f32 accumulator tiles (C / 2 registers);
+//  * keys advance 32 per block: the block's K rows (32 x C) and V^T
+//    columns (C x 32) stream into double-buffered LDS by direct-to-LDS
 //    buffer loads (rows past the buffers read zero);
 //  * scores are computed transposed, S^T = K . Q^T (keys as MFMA rows), and
 //    the output as O^T = V^T . P^T: a lane then holds one query's scores
@@ -37,8 +38,11 @@
 //    weights, so the softmax's VALU work overlaps the MFMAs of a single
 //    wave per SIMD; the score MFMAs are inline asm with the accumulator
 //    pinned to VGPRs, keeping every AGPR for the output;
-//  * K rows are padded to 65 units of 16 bytes in LDS and V^T units are
-//    swizzled (unit u of column c at u ^ ((c >> 2) & 3)), so every fragment
+//  * at C = 512 a K row (64 units of 16 bytes) is one wave's load and
+//    rows are padded to 65 units in LDS; narrower rows are packed, a load
+//    spanning several of them, and unit u of key row j sits at
+//    u ^ (j mod 16) within its group of 16. V^T units are swizzled too
+//    (unit u of column c at u ^ ((c >> 2) & 3)). Either way every fragment
 //    read touches 16 distinct bank groups per pass;
 //  * when the queries alone give fewer workgroups than the chip has CUs,
 //    the keys are split into ranges whose partial (max, sum, O) are merged
@@ -60,18 +64,24 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int C = 512;             // head width
 constexpr int NT = 256;            // 4 waves
 constexpr int BQ = 128;            // queries per workgroup
 constexpr int BK = 32;             // keys per block
-constexpr int KS = C / 16;         // K steps of the score product
-constexpr int CT = C / 32;         // output column tiles
-constexpr int KU = BK * C / 8;     // 16-byte units of a K block (2048)
-constexpr int KROW = C / 8 + 1;    // LDS units per K row: 64 + 1 of padding
-constexpr int KBUF = BK * KROW;    // LDS units per K buffer
-constexpr int VU = C * BK / 8;     // units of a V^T block (2048)
-constexpr int LPW = KU / 64 / 4;   // loads per wave per block, K and V^T each (8)
-constexpr int PD = 3;             // fragment reads in flight ahead of the MFMAs
+constexpr int PD = 3;              // fragment reads in flight ahead of the MFMAs
+// the geometry at head width C (a multiple of 128, at most 512)
+template <int C>
+struct FGeo {
+    static_assert(C % 128 == 0 && C >= 128 && C <= 512, "head width");
+    static constexpr int KS = C / 16;            // K steps of the score product
+    static constexpr int CT = C / 32;            // output column tiles
+    static constexpr int KUR = C / 8;            // 16-byte units of a K row
+    static constexpr bool KPAD = C == 512;       // a K row per wave load, rows padded
+    static constexpr int KROW = KPAD ? KUR + 1 : KUR;  // LDS units per K row
+    static constexpr int KBUF = BK * KROW;       // LDS units per K buffer
+    static constexpr int VU = C * BK / 8;        // units of a V^T block
+    static constexpr int LPW = BK * KUR / 64 / 4;  // loads per wave per block, K and V^T each (C / 64)
+    static constexpr int NH = CT / 2;            // softmax hooks per P.V phase
+};
 constexpr float kHeadroom = 15.f;  // log2 of the largest weight (f16 holds up to 2^16)
 constexpr float kNegBig = -1e30f;
 
@@ -130,9 +140,12 @@ __device__ __forceinline__ void mfma_last(f32x16 &acc, half8 a, half8 b)
     asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(acc) : "v"(a), "v"(b));
 }
 
+template <int C>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_flash(FlashArgs p)
 {
+    using G = FGeo<C>;
+    constexpr int KS = G::KS, CT = G::CT, KUR = G::KUR, KROW = G::KROW, KBUF = G::KBUF, VU = G::VU, LPW = G::LPW;
     __shared__ __attribute__((aligned(16))) u32x4 lds[2 * (KBUF + VU)];
 
     const int tid = threadIdx.x;
@@ -165,28 +178,53 @@ void k_flash(FlashArgs p)
                                               q_src, ((q0 + r) * C + 16 * s + 8 * h) * 2, 0, 0));
 
     // LDS: two K buffers (key rows KROW units apart), then two V^T
-    // buffers. The wave's i-th K load fills key row kr = wave + 4 i (64
-    // units from the lane's 16 bytes); its i-th V^T load fills columns
-    // 16 kc .. 16 kc + 15 (kc = wave + 4 i), 4 units each, unit u of column
-    // c at u ^ ((c >> 2) & 3). Per-lane source offsets are fixed; the load
-    // index and the block move the scalar offset.
+    // buffers. At C = 512 the wave's i-th K load fills key row kr = wave +
+    // 4 i (64 units from the lane's 16 bytes); narrower, it fills LDS units
+    // U = (wave + 4 i) 64 + lane, unit U mod KUR of key row U / KUR, read
+    // from the row's unit (U mod KUR) ^ (row mod 16). Its i-th V^T load
+    // fills columns 16 kc .. 16 kc + 15 (kc = wave + 4 i), 4 units each,
+    // unit u of column c at u ^ ((c >> 2) & 3). Per-lane source offsets
+    // are fixed; the load index and the block move the scalar offset.
     u32x4 *const ldv = lds + 2 * KBUF;
     const int kvoff = 16 * lane;
+    int kvo[G::KPAD ? 1 : LPW];
+    if constexpr (!G::KPAD) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int u = (wave + 4 * i) * 64 + lane, kr = u / KUR, ku = u % KUR;
+            kvo[i] = kr * C * 2 + 16 * (ku ^ (kr & 15));
+        }
+    }
     const int vvoff = (int)((uint32_t)(16 * wave + (lane >> 2)) * (uint32_t)p.ld * 2u +
                             16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)));
     auto issue_k = [&](int blk, int kbuf, int i) __attribute__((always_inline)) {
-        const int kr = wave + 4 * i;
-        dma16(k_src, lds + kbuf * KBUF + kr * KROW, kvoff, (blk * BK + kr) * C * 2);
+        if constexpr (G::KPAD) {
+            const int kr = wave + 4 * i;
+            dma16(k_src, lds + kbuf * KBUF + kr * KROW, kvoff, (blk * BK + kr) * C * 2);
+        } else {
+            dma16(k_src, lds + kbuf * KBUF + (wave + 4 * i) * 64, kvo[i], blk * BK * C * 2);
+        }
     };
     auto issue_v = [&](int blk, int vbuf, int i) __attribute__((always_inline)) {
         dma16(v_src, ldv + vbuf * VU + (wave + 4 * i) * 64, vvoff, (int)((uint32_t)i * 64u * (uint32_t)p.ld * 2u + (uint32_t)blk * BK * 2u));
     };
 
     // fragment reads (units): K step s of MFMA row r reads key row
-    // key_of_row(r), unit 2 s + h: with the padded rows, 16 consecutive
-    // lanes hit 16 distinct bank groups. V^T tile ct, K step t: column
-    // 32 ct + r, unit (2 t + h) ^ ((r >> 2) & 3)
+    // kr = key_of_row(r), unit 2 s + h: with padded rows at krd + 2 s, else
+    // at kr KUR + (2 s + h) ^ (kr mod 16) = kq[s mod 8] + 16 (s / 8); 16
+    // consecutive lanes hit 16 distinct bank groups. V^T tile ct, K step t:
+    // column 32 ct + r, unit (2 t + h) ^ ((r >> 2) & 3)
     const int krd = key_of_row(r) * KROW + h;
+    int kq[G::KPAD ? 1 : 8];
+    if constexpr (!G::KPAD) {
+        const int kr = key_of_row(r);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) kq[k] = kr * KUR + ((2 * k + h) ^ (kr & 15));
+    }
+    auto kunit = [&](int st) __attribute__((always_inline)) {
+        if constexpr (G::KPAD) return krd + 2 * st;
+        else return kq[st & 7] + 16 * (st >> 3);
+    };
     int voff[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) voff[t] = 4 * r + ((2 * t + h) ^ ((r >> 2) & 3));
@@ -211,12 +249,12 @@ void k_flash(FlashArgs p)
         const u32x4 *sk = lds + kbuf * KBUF;
         half8 kf[PD + 1];
 #pragma unroll
-        for (int i = 0; i < PD; ++i) kf[i] = __builtin_bit_cast(half8, sk[krd + 2 * i]);
+        for (int i = 0; i < PD; ++i) kf[i] = __builtin_bit_cast(half8, sk[kunit(i)]);
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
             if (st + PD < KS) {
                 const int s2 = st + PD;
-                kf[s2 % (PD + 1)] = __builtin_bit_cast(half8, sk[krd + 2 * s2]);
+                kf[s2 % (PD + 1)] = __builtin_bit_cast(half8, sk[kunit(s2)]);
             }
             const half8 a = kf[st % (PD + 1)];
             if (st == 0)
@@ -328,7 +366,17 @@ void k_flash(FlashArgs p)
             if (st % 4 == 3) issue_v(blk, cur, st / 4);
         });
         const int lim = p.m - blk * BK;
-        pv_phase(cur ^ 1, pprev, [&](int g) { softmax_step(g, sacc, lim, pcur, false); });
+        // the six softmax steps over the P.V phase's NH hooks: one per hook
+        // where there are six or more, else spread evenly (narrow heads)
+        pv_phase(cur ^ 1, pprev, [&](int g) __attribute__((always_inline)) {
+            if constexpr (G::NH >= 6) {
+                softmax_step(g, sacc, lim, pcur, false);
+            } else {
+#pragma unroll
+                for (int st = (6 * g + G::NH - 1) / G::NH; st < (6 * (g + 1) + G::NH - 1) / G::NH; ++st)
+                    softmax_step(st, sacc, lim, pcur, false);
+            }
+        });
         pprev[0] = pcur[0];
         pprev[1] = pcur[1];
     }
@@ -384,8 +432,9 @@ void k_flash(FlashArgs p)
     }
 }
 
-// merge the key ranges' partial results of one query row:
+// merge the key ranges' partial results of one query row (C / 4 threads):
 // out = f16( sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s + bv )
+template <int C>
 __global__ __launch_bounds__(128) void k_flash_merge(FlashArgs p)
 {
     const int q = blockIdx.x, t = threadIdx.x;
@@ -418,35 +467,47 @@ void flash_split(int m, int &nsplit, int &bps)
     nsplit = (nblocks + bps - 1) / bps;
 }
 
-}  // namespace
-
-// q, k and V^T are addressed with 32-bit byte offsets: each stays below
-// kConvInMaxBytes (ld < 2,096,960 rows at C = 512)
-bool flash_supported(int m, int ld, int c)
+template <int C>
+void launch_flash_t(FlashArgs a, void *ws, hipStream_t s)
 {
-    return c == C && m > 0 && ld >= ((m + BK - 1) / BK) * BK && ld % 8 == 0 &&
-           (int64_t)ld * C * 2 < kConvInMaxBytes;
-}
-
-size_t flash_workspace_bytes(int m)
-{
-    int ns, bps;
-    flash_split(m, ns, bps);
-    if (ns == 1) return 0;
-    return (size_t)ns * m * (C + 2) * sizeof(float) + 256;
-}
-
-void launch_flash(FlashArgs a, void *ws, hipStream_t s)
-{
-    if (a.m <= 0) return;
     flash_split(a.m, a.nsplit, a.bps);
     if (a.nsplit > 1) {
         a.opart = reinterpret_cast<float *>(ws);
         a.ml = a.opart + (int64_t)a.nsplit * a.m * C;
     }
     const int nqb = (a.m + BQ - 1) / BQ;
-    hipLaunchKernelGGL(k_flash, dim3(nqb * a.nsplit), dim3(NT), 0, s, a);
-    if (a.nsplit > 1) hipLaunchKernelGGL(k_flash_merge, dim3(a.m), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_flash<C>, dim3(nqb * a.nsplit), dim3(NT), 0, s, a);
+    if (a.nsplit > 1) hipLaunchKernelGGL(k_flash_merge<C>, dim3(a.m), dim3(C / 4), 0, s, a);
+}
+
+}  // namespace
+
+// head widths 128, 256, 384, 512; q, k and V^T are addressed with 32-bit
+// byte offsets: each stays below kConvInMaxBytes (ld < 2,096,960 rows at
+// C = 512)
+bool flash_supported(int m, int ld, int c)
+{
+    return (c == 128 || c == 256 || c == 384 || c == 512) && m > 0 && ld >= ((m + BK - 1) / BK) * BK &&
+           ld % 8 == 0 && (int64_t)ld * c * 2 < kConvInMaxBytes;
+}
+
+size_t flash_workspace_bytes(int m, int c)
+{
+    int ns, bps;
+    flash_split(m, ns, bps);
+    if (ns == 1) return 0;
+    return (size_t)ns * m * (c + 2) * sizeof(float) + 256;
+}
+
+void launch_flash(FlashArgs a, void *ws, hipStream_t s)
+{
+    if (a.m <= 0) return;
+    switch (a.c) {
+    case 128: launch_flash_t<128>(a, ws, s); break;
+    case 256: launch_flash_t<256>(a, ws, s); break;
+    case 384: launch_flash_t<384>(a, ws, s); break;
+    default: launch_flash_t<512>(a, ws, s); break;
+    }
 }
 
 }  // namespace ig

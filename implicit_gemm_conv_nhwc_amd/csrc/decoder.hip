@@ -384,7 +384,7 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     if (pl.flash) {
         // the single-pass kernel's key-range partials (if any)
         pl.off_o = take(0);
-        pl.off_s = take(flash_workspace_bytes(pl.m));
+        pl.off_s = take(flash_workspace_bytes(pl.m, pl.C));
         pl.off_p = take(0);
     } else {
         pl.off_o = take(mp * C * 4);
@@ -646,6 +646,7 @@ struct Run {
             f.vt = vt16;
             f.ld = mp;
             f.m = m;
+            f.c = C;
             f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)C));
             f.bv = a.v.b;
             f.out = xn;

@@ -114,12 +114,14 @@ int gemm2_stat_parts(int N);
 // rowstat[r] = (max, 1 / sum) from the partial statistics of row r
 void launch_rowstat(const float *stats, int nparts, int rows, float *rowstat, hipStream_t s);
 
-// single-pass attention core (C = 512): out = f16(softmax(q k^T / sqrt(C)) v + bv)
+// single-pass attention core (C = 128, 256, 384 or 512):
+// out = f16(softmax(q k^T / sqrt(C)) v + bv)
 struct FlashArgs {
     const _Float16 *q, *k;  // [ld][C] rows (rows >= m are read, never used)
     const _Float16 *vt;     // V^T [C][ld]
     int ld;                 // rows of q and k; row stride of V^T
     int m;                  // queries = keys
+    int c;                  // head width
     float scale_log2;       // log2(e) / sqrt(C)
     const float *bv;        // [C] or null
     _Float16 *out;          // [m][C]
@@ -127,7 +129,7 @@ struct FlashArgs {
     float *opart, *ml;      // per range: partial O [m][C] and (max, sum) [m] (workspace)
 };
 bool flash_supported(int m, int ld, int c);
-size_t flash_workspace_bytes(int m);
+size_t flash_workspace_bytes(int m, int c);
 void launch_flash(FlashArgs a, void *ws, hipStream_t s);
 
 // ---------------------------------------------------------------------

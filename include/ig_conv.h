@@ -263,7 +263,8 @@ int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols,
  *   ws:   device scratch of ws_bytes >= ig_attention_workspace_bytes(m, C)
  *         (0 bytes for small m: ws may then be NULL); its contents on
  *         entry do not matter.
- * C must be 512 (IG_EUNSUPPORTED otherwise); ld >= m rounded up to 32,
+ * C must be 128, 256, 384 or 512 (IG_EUNSUPPORTED otherwise: other
+ * widths take the chunked path of decoder_forward); ld >= m rounded up to 32,
  * ld % 8 == 0 and ld * C * 2 < 0x7fff0000 (the kernel addresses q, k and
  * V^T with 32-bit byte offsets); q, k, vt, out 16-byte aligned. m < 2^22.
  * --------------------------------------------------------------------- */
@@ -380,7 +381,7 @@ typedef struct ig_decoder {
 
 /* Workspace bytes decoder_forward needs for an h0 x w0 latent. q_chunk
  * selects the attention: q_chunk <= 0 takes the single-pass kernel of
- * attention_f16 when the attention width is 512 (else query chunks of
+ * attention_f16 when the attention width is 128, 256, 384 or 512 (else query chunks of
  * 16384 rows); q_chunk > 0 takes the chunked path (scores' row statistics,
  * then P, then P.V) over chunks of q_chunk query rows. Returns 0
  * if the descriptor or the sizes are invalid (see ig_last_error()). */

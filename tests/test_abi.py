@@ -118,6 +118,15 @@ def test_validation_rejects_before_enqueueing(ig):
     assert lib.attention_f16(fake, fake, fake, 1024, big + 8, 512, None, fake, 1 << 30, fake, None) == -1
     assert "ld" in ig.last_error()
     assert lib.attention_f16(fake, fake, fake, 1024, 1 << 22, 512, None, fake, 1 << 30, fake, None) == -1
+    # head widths: 128, 256, 384 and 512 run in one pass; others are refused
+    big256 = 0x7fff0000 // (256 * 2)
+    assert lib.attention_f16(fake, fake, fake, 1024, big256 + 8, 256, None, fake, 1 << 30, fake, None) == -1
+    for c in (64, 192, 320, 640, 1024):
+        assert lib.attention_f16(fake, fake, fake, 64, 64, c, None, fake, 1 << 30, fake, None) == -2, c
+        assert ig.attention_workspace_bytes(64, c) == 0
+    for c in (128, 256, 384, 512):
+        assert ig.attention_workspace_bytes(16384, c) > 0
+        assert ig.attention_workspace_bytes(64, c) == 0 and ig.last_error() == ""
     # groupnorm without a workspace: the same checks as with one
     lib.groupnorm_silu_f16_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

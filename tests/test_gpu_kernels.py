@@ -771,13 +771,12 @@ def test_rejected_call_leaves_output_untouched():
 # ---------------------------------------------------------------------------
 
 
-def _attn_inputs(m, kind, seed):
-    """q, k [m][512], V^T [512][m], bv: f16 operands with the decoder's
-    scale (entries ~ N(0, 1): scores q.k / sqrt(512) ~ N(0, 1)).
+def _attn_inputs(m, kind, seed, C=512):
+    """q, k [m][C], V^T [C][m], bv: f16 operands with the decoder's
+    scale (entries ~ N(0, 1): scores q.k / sqrt(C) ~ N(0, 1)).
     kind: 'flat'; 'growing' (key norms grow along the sequence, so the
     running max is raised block after block); 'self' (k = q: each query's
-    own key dominates by ~22 in the exponent)."""
-    C = 512
+    own key dominates by ~sqrt(C) in the exponent)."""
     q = synth.normal(7, seed, (m, C), 1.0, np.float16)
     k = synth.normal(7, seed + 1, (m, C), 1.0, np.float16)
     v = synth.normal(7, seed + 2, (m, C), 1.0, np.float16)
@@ -845,6 +844,31 @@ def test_attention_single_pass_large(m):
     _check_attn(got[rows], q[rows], k, vt, bv, "attention m=%d" % m)
 
 
+@pytest.mark.parametrize("C,m,kind", [(128, 1, "flat"), (128, 333, "growing"), (128, 2000, "self"),
+                                      (256, 100, "flat"), (256, 1500, "growing"), (256, 4096, "self"),
+                                      (384, 64, "flat"), (384, 1000, "growing"), (384, 2048, "self")])
+def test_attention_single_pass_other_widths(C, m, kind):
+    """Head widths below 512: K rows packed (several per load) with their
+    units swizzled in LDS, and the softmax steps spread over fewer P.V
+    hooks; the same bound against the plain definition."""
+    q, k, vt, bv = _attn_inputs(m, kind, seed=40 + C // 128 + m % 5, C=C)
+    got = _run_flash(q, k, vt, bv)
+    rows = np.arange(m) if m <= 2048 else np.unique(np.r_[0:64, m - 64:m, np.linspace(0, m - 1, 128).astype(int)])
+    _check_attn(got[rows], q[rows], k, vt, bv, "attention C=%d m=%d %s" % (C, m, kind))
+
+
+@pytest.mark.parametrize("C", [128, 256, 384])
+def test_attention_other_widths_with_key_ranges(C):
+    """16384 tokens: the keys split into ranges whose partial results the
+    merge kernel (C / 4 threads) combines."""
+    m = 16384
+    assert ig.attention_workspace_bytes(m, C) > 0
+    q, k, vt, bv = _attn_inputs(m, "flat", seed=5 + C // 128, C=C)
+    got = _run_flash(q, k, vt, bv)
+    rows = np.unique(np.r_[0:32, m - 32:m, np.linspace(0, m - 1, 64).astype(int)])
+    _check_attn(got[rows], q[rows], k, vt, bv, "attention C=%d m=%d" % (C, m))
+
+
 def test_attention_chunked_path_meets_the_same_bound():
     """The chunked path (statistics GEMM, row merge, probabilities GEMM,
     P.V) through the decoder's kernels: the same per-element bound against
@@ -868,9 +892,10 @@ def test_attention_chunked_path_meets_the_same_bound():
 
 
 def test_attention_rejects_other_widths_and_short_workspace():
-    with pytest.raises(ig.IgError) as e:
-        ig.attention_f16(None, None, None, 64, 64, 256, None, None, 0, None)
-    assert e.value.code == -2
+    for c in (192, 640):
+        with pytest.raises(ig.IgError) as e:
+            ig.attention_f16(None, None, None, 64, 64, c, None, None, 0, None)
+        assert e.value.code == -2
     m = 16384
     need = ig.attention_workspace_bytes(m, 512)
     assert need > 0
