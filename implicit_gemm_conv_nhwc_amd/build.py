@@ -66,14 +66,15 @@ def _check_isa(src: str) -> list:
     spec.loader.exec_module(mod)
     with open(out) as f:
         text = f.read()
-    return [(src,) + x for x in mod.scan(text) + mod.scan_m0(text)]
+    return [(src,) + x for x in mod.scan(text) + mod.scan_m0(text) + mod.scan_vmem(text)]
 
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libigconv.so; returns its path.
 
     Refuses to link when the device code of an asm-MFMA source reads an
-    MFMA result (or overwrites its accumulator) too early."""
+    MFMA result (or overwrites its accumulator) too early, uses M0 beyond
+    the patch loads, or touches the registers of a load still in flight."""
     os.makedirs(OUT_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(ASM_MFMA_SOURCES))) as ex:
         objs_f = [ex.submit(_compile, src) for src in SOURCES]
@@ -81,7 +82,7 @@ def build(verbose: bool = False) -> str:
         objs = [f.result() for f in objs_f]
         findings = [x for f in isa_f for x in f.result()]
     if findings:
-        raise RuntimeError("MFMA latency hazards in the device code:\n" +
+        raise RuntimeError("hazards in the device code (isa_check.py):\n" +
                            "\n".join("%s %s: %s -> %s" % f for f in findings[:20]))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]

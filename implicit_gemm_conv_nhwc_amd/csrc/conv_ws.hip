@@ -279,12 +279,20 @@ void k_conv_ws(IgemmArgs p)
     // vector-memory operations of the drain's items
     constexpr int OPS_L = ACC ? 4 : 0;                               // stream loads of a row
     constexpr int OPS_ROW = (WOUT ? 4 : 0) + (YG ? 4 : 0) + (NORM ? 2 : 0);  // stores of a row
-    // operations that may stay in flight at the wait in stage st (see the
-    // schedule): after the loads that must have landed come only these
-    constexpr int WAIT0 = APW;                                  // stream rows 0, 1 (staged in stage 3)
-    constexpr int WAIT1 = ACC ? OPS_ROW : 2 * OPS_ROW + APW;    // stream row 2, then row 1's stores
-    constexpr int WAIT2 = ACC ? OPS_ROW : OPS_ROW + APW;        // stream row 3, then row 2's stores
-    constexpr int WAIT3 = OPS_ROW + 2 * OPS_L + APW;            // nothing of the drain
+    // A wave issues APW patch loads per stage, or APW - 1 when its last
+    // one would lie wholly past the patch (the waves after the first, at
+    // both shapes here). The operations that may stay in flight at the wait
+    // in stage st (see the schedule) -- after the loads that must have
+    // landed come only these -- for a wave issuing L per stage; the waits
+    // take L = APW - 1 for every wave (stricter for a wave issuing APW):
+    constexpr int LPW_P = APW - 1;
+    static_assert(G::A_INSTR > NW * (APW - 1), "the first wave's last patch load carries data");
+    auto wait_count = [](int st, int L) constexpr {
+        return st == 0 ? L                                           // stream rows 0, 1 (staged in stage 3)
+             : st == 1 ? (ACC ? OPS_ROW : 2 * OPS_ROW + L)            // stream row 2, then row 1's stores
+             : st == 2 ? (ACC ? OPS_ROW : OPS_ROW + L)                // stream row 3, then row 2's stores
+             : OPS_ROW + 2 * OPS_L + L;                                // nothing of the drain
+    };
 
     __shared__ __attribute__((aligned(16))) u32x4 lds[ws_lds_bytes<MODE>() / 16];
     float *stg = reinterpret_cast<float *>(lds + NBUF * A_PAD);  // [TH][TW][SP]
@@ -300,6 +308,8 @@ void k_conv_ws(IgemmArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
+    // this wave issues all APW patch loads per stage (else APW - 1)
+    const bool lfull = wave + NW * (APW - 1) < G::A_INSTR;
     const int fx = lane & 31;  // tile column of this lane's B fragments and accumulators
     const int fh = lane >> 5;  // channel half (of a K-step's 16) in the fragments
 
@@ -378,7 +388,7 @@ void k_conv_ws(IgemmArgs p)
     // past the patch read zeros into the buffer's padding)
     auto issue_one = [&](const WTile &tl, int st, int buf, int k) __attribute__((always_inline)) {
         const int ii = wave + NW * k;
-        dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, tl.aoff[k], st * CK * 2);
+        if (k < APW - 1 || lfull) dma16(a_src, lds_base + (buf * A_PAD + ii * 64) * 16, tl.aoff[k], st * CK * 2);
     };
 
     // the wave's weights: fragment f = (2 s + ks) 9 + tap = output channel
@@ -553,7 +563,12 @@ void k_conv_ws(IgemmArgs p)
         item_norm(r, 1);
     };
     // the wait: all but the last n vector-memory operations have landed (and,
-    // after the barrier, every wave's); the stream values are ready
+    // after the barrier, every wave's); the stream values are ready. n counts
+    // the operations of a wave issuing APW - 1 patch loads per stage; a wave
+    // issuing APW waits for one more of them than it must. (One wait for
+    // every wave: with two, in the arms of a branch, the compiler may copy
+    // the stream values' registers before either wait, while their loads
+    // are still in flight.)
     auto wait_n = [&](auto n) __attribute__((always_inline)) {
         if constexpr (ACC)
             asm volatile("s_waitcnt vmcnt(%8)"
@@ -584,7 +599,7 @@ void k_conv_ws(IgemmArgs p)
 #pragma unroll
     for (int k = 0; k < APW; ++k) issue_one(cur, NST - 1, NST - 1, k);
     static_assert(18 + 3 * APW + 2 * OPS_L < 64, "vmcnt range");
-    wait_n(std::integral_constant<int, 18 + 3 * APW + 2 * OPS_L>{});
+    wait_n(std::integral_constant<int, 18 + 3 * LPW_P + 2 * OPS_L>{});
     if (tid < BN) {
         sbias[tid] = bias_v;
         sgam[tid] = gam_v;
@@ -683,10 +698,7 @@ void k_conv_ws(IgemmArgs p)
                     // the next stage's buffer has landed and every wave is
                     // past this stage's LDS reads; its first fragments load
                     // under group 5's MFMAs
-                    if constexpr (st == 0) wait_n(std::integral_constant<int, WAIT0>{});
-                    else if constexpr (st == 1) wait_n(std::integral_constant<int, WAIT1>{});
-                    else if constexpr (st == 2) wait_n(std::integral_constant<int, WAIT2>{});
-                    else wait_n(std::integral_constant<int, WAIT3>{});
+                    wait_n(std::integral_constant<int, wait_count(st, LPW_P)>{});
                     load_group(lds + ((st + 1) % NBUF) * A_PAD, 0, bf[0]);
                 } else {
                     // one wait per group: this group's fragments (loaded a

@@ -113,8 +113,56 @@ def scan_m0(text):
     return findings
 
 
+_VMCNT = re.compile(r"vmcnt\((\d+)\)")
+
+
+def scan_vmem(text):
+    """Registers of an asm load in flight. The conv's stream loads are asm
+    (hidden from the compiler's wait tracking) and land only by a later
+    s_waitcnt vmcnt(n) of the kernel's own; the compiler, which takes the
+    registers for written at issue, may place a copy or other access of
+    them before that wait and so read (or overwrite) data not yet landed.
+    Within each straight-line stretch of code (from a label to the next),
+    every vector-memory instruction is counted in layout order; a wait
+    with vmcnt(n) retires all but the last n; an access of a register that
+    an unretired load writes is a finding (a load into the same registers
+    included). Loads straight into LDS write no registers. A label starts
+    afresh: code reached by a branch has its own waits on every path (the
+    compiler's loads), and this check is about accesses placed between an
+    asm load and its wait in the same stretch."""
+    findings = []
+    for name, body in _FUNC.findall(text):
+        pending = []  # (registers, line) per vector-memory instruction in flight, oldest first
+        for l in body.split("\n"):
+            l = l.split(";")[0].strip()
+            if l.endswith(":"):
+                pending = []
+                continue
+            if not l or l.startswith("."):
+                continue
+            op = l.split()[0]
+            toks = l.split()[1:]
+            if op.startswith("s_waitcnt"):
+                m = _VMCNT.search(l)
+                if m:
+                    n = int(m.group(1))
+                    pending = pending[len(pending) - n:] if n < len(pending) else pending
+                continue
+            regs = set().union(*[_regs(t) for t in toks]) if toks else set()
+            busy = set().union(*[r for r, _ in pending]) if pending else set()
+            if regs & busy:
+                findings.append((name, [ln for r, ln in pending if r & regs][0], l))
+            if op.startswith(("buffer_", "global_", "flat_", "scratch_")):
+                dst = set()
+                if op.startswith(("buffer_load", "global_load", "flat_load", "scratch_load")) and " lds" not in " " + l:
+                    dst = _regs(toks[0])
+                pending.append((dst, l))
+    return findings
+
+
 if __name__ == "__main__":
-    bad = scan(open(sys.argv[1]).read()) + scan_m0(open(sys.argv[1]).read())
+    t = open(sys.argv[1]).read()
+    bad = scan(t) + scan_m0(t) + scan_vmem(t)
     for f in bad:
         print("%s: %s  ->  %s" % f)
     sys.exit(1 if bad else 0)

@@ -1,6 +1,7 @@
-"""The build's scan of inline-asm MFMAs for accesses inside their latency
-window (a CDNA XDL op of N passes needs N + 3 wait states before a VALU or
-memory access of its result registers)."""
+"""The build's scans of the asm-MFMA kernels: accesses inside an MFMA's
+latency window (a CDNA XDL op of N passes needs N + 3 wait states before a
+VALU or memory access of its result registers), uses of M0, and accesses of
+the registers of a load still in flight."""
 import importlib.util
 import os
 
@@ -64,3 +65,36 @@ def test_m0_rule():
     assert len(isa_check.scan_m0(_kernel(["v_readlane_b32 s0, v1, m0"]))) == 1
     assert len(isa_check.scan_m0(_kernel(["s_sendmsg sendmsg(MSG_DEALLOC_VGPRS)"]))) == 1
     assert len(isa_check.scan_m0(_kernel(["s_movrels_b32 s0, s1"]))) == 1
+
+
+LOAD = "buffer_load_dwordx4 v[2:5], v14, s[28:31], 0 offen"
+
+
+def test_copy_of_a_load_in_flight_is_found():
+    """The compiler takes an asm load's registers for written at issue: a
+    copy placed before the kernel's own wait reads data not yet landed."""
+    bad = _kernel([LOAD, "buffer_load_dwordx4 v[6:9], v14, s[28:31], 0 offen", "v_mov_b64_e32 v[40:41], v[4:5]",
+                   "s_waitcnt vmcnt(0)"])
+    f = isa_check.scan_vmem(bad)
+    assert len(f) == 1 and f[0][1] == LOAD
+
+
+def test_wait_retires_all_but_the_last_n():
+    later = "buffer_load_dwordx4 v[6:9], v14, s[28:31], 0 offen"
+    # vmcnt(1): the first load has landed, the second may not have
+    ok = _kernel([LOAD, later, "s_waitcnt vmcnt(1)", "v_mov_b64_e32 v[40:41], v[4:5]"])
+    assert isa_check.scan_vmem(ok) == []
+    bad = _kernel([LOAD, later, "s_waitcnt vmcnt(1)", "v_mov_b64_e32 v[40:41], v[8:9]"])
+    assert len(isa_check.scan_vmem(bad)) == 1
+    # stores and loads into LDS count in vmcnt but write no registers
+    ok2 = _kernel([LOAD, "buffer_store_dwordx4 v[10:13], v14, s[28:31], 0 offen",
+                   "buffer_load_dwordx4 v1, s[8:11], s6 offen lds", "s_waitcnt vmcnt(2)", "v_add_f32_e32 v40, v2, v3"])
+    assert isa_check.scan_vmem(ok2) == []
+    # a second load into the same registers before the first has landed
+    assert len(isa_check.scan_vmem(_kernel([LOAD, LOAD]))) == 1
+
+
+def test_a_label_starts_afresh():
+    """Code reached by a branch has its own waits on every path."""
+    ok = _kernel([LOAD, "s_cbranch_execz .LBB0_2", ".LBB0_2:", "v_mov_b32_e32 v2, 0"])
+    assert isa_check.scan_vmem(ok) == []
