@@ -6,7 +6,10 @@ One step = one whole decode (decoder_forward) of the synthetic decoder at
 stream passes the f16 range), guard 2^-8, every tensor resident in HBM.
 `value` is the decode's algorithmic TFLOP/s (real channels; 3x3 and 1x1
 convs at 2*M*cin*cout*k^2, attention at 2*m^2*C per product plus its four
-projections); `decode_s` is seconds per decode.
+projections); `decode_s` is seconds per decode. `decode_graph`: the same
+decode captured once into a HIP graph and replayed (every kernel still
+runs; no host launch per kernel), with a check that a replay's frame equals
+the eager decode's.
 
 Also measured, in the same process and on the stream the kernels run on:
   * roofline: the dominant kernel, the 3x3 implicit-GEMM conv at
@@ -152,7 +155,7 @@ def decode_flops(spec, h0, w0):
 # ---------------------------------------------------------------------------
 
 
-def bench_decode(steps, warmup, h0, q_chunk):
+def bench_decode(steps, warmup, h0, q_chunk, graph=False):
     import torch
 
     import implicit_gemm_conv_nhwc_amd as ig
@@ -184,9 +187,38 @@ def bench_decode(steps, warmup, h0, q_chunk):
     ev_ms = sum(per)
     finite = bool(torch.isfinite(out).all().item())
     flops = decode_flops(spec, h0, h0)
+    res = {"wall_s": wall, "event_ms": ev_ms, "median_ms": statistics.median(per), "flops": flops,
+           "finite": finite, "H": H, "spec": spec}
+    if graph:
+        # the same decode captured once into a HIP graph and replayed: every
+        # kernel still runs, without a host launch per kernel
+        ref = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dd.forward(zd, h0, h0, guard_log2=8, q_chunk=q_chunk, ws=ws, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dd.forward(zd, h0, h0, guard_log2=8, q_chunk=q_chunk, ws=ws, out=out)
+        for _ in range(max(warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out, ref))
+        gevs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        gevs[0].record()
+        for k in range(steps):
+            g.replay()
+            gevs[k + 1].record()
+        torch.cuda.synchronize()
+        gper = [gevs[k].elapsed_time(gevs[k + 1]) for k in range(steps)]
+        res["graph"] = {"median_s": round(statistics.median(gper) / 1000.0, 6),
+                        "mean_s": round(sum(gper) / steps / 1000.0, 6), "steps": steps,
+                        "equals_eager": same and bool(torch.equal(out, ref))}
+        del g
     del ws
-    return {"wall_s": wall, "event_ms": ev_ms, "median_ms": statistics.median(per), "flops": flops,
-            "finite": finite, "H": H, "spec": spec}
+    return res
 
 
 def bench_conv_roofline(reps, H=512, W=512, C=128):
@@ -694,12 +726,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log("device:", torch.cuda.get_device_name(0))
 
-    dec = bench_decode(args.steps, args.warmup, args.latent, args.q_chunk)
+    dec = bench_decode(args.steps, args.warmup, args.latent, args.q_chunk, graph=True)
     ms = dec["wall_s"] * 1000.0 / args.steps
     ev_ms = dec["event_ms"] / args.steps
     tflops = dec["flops"] / (ms / 1000.0) / 1e12
     log("decode %d^2: %.3f ms/step (events %.3f), %.1f TFLOP/s, finite=%s" % (
         dec["H"], ms, ev_ms, tflops, dec["finite"]))
+    log("decode %d^2 replayed from a HIP graph: median %.3f ms (equals eager: %s)" % (
+        dec["H"], dec["graph"]["median_s"] * 1000.0, dec["graph"]["equals_eager"]))
 
     conv = bench_conv_roofline(args.roof_reps)
     conv_tf = conv["flops"] / (conv["avg_ms"] / 1000.0) / 1e12
@@ -773,6 +807,7 @@ def main():
         },
         "decode_s": round(ms / 1000.0, 6),
         "decode_s_median": round(dec["median_ms"] / 1000.0, 6),
+        "decode_graph": dec["graph"],
         "decode_tflop": round(dec["flops"] / 1e12, 4),
         "output_finite": dec["finite"],
         "roofline": {

@@ -156,6 +156,42 @@ def test_banded_decode_full_size_1024(full_decoder):
     assert torch.equal(banded, whole)
 
 
+@pytest.mark.parametrize("small,h0,w0,dupup", [(True, 8, 8, True), (False, 16, 16, False)])
+def test_decode_replays_from_a_captured_graph(small, h0, w0, dupup):
+    """decoder_forward allocates nothing, synchronises nothing and enqueues
+    only kernels and device-to-device copies on its stream, so a caller can
+    capture a decode into a HIP graph (torch.cuda.CUDAGraph) and replay it.
+    Each replay, with new latents copied into the captured input and eager
+    decodes on the same workspace between replays, equals the eager decode
+    of that latent bit for bit."""
+    spec = synth.decoder_spec(small=small, dupup=dupup)
+    dd = ig.DeviceDecoder(synth.decoder_weights(spec, seed_config=4))
+    ws = dd.alloc_workspace(h0, w0, 0)
+    zs = [dev(synth.decoder_latent(h0, w0, zc=spec.zc, config=4 + i)) for i in range(3)]
+    refs = [dd.forward(z, h0, w0, ws=ws).clone() for z in zs]
+    zin = torch.empty_like(zs[0])
+    out = torch.empty_like(refs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        zin.copy_(zs[0])
+        dd.forward(zin, h0, w0, ws=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dd.forward(zin, h0, w0, ws=ws, out=out)
+    for i in (1, 0, 2, 1):
+        zin.copy_(zs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[i]), i
+        other = dd.forward(zs[(i + 1) % 3], h0, w0, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, refs[(i + 1) % 3])
+    print("graph replays equal the eager decodes (%s %dx%d)" % ("small" if small else "full", h0, w0), flush=True)
+
+
 @pytest.mark.parametrize("small,h0,w0", [(True, 5, 7), (True, 8, 8), (False, 32, 32)])
 def test_decoder_with_dupup(small, h0, w0):
     """Every up stage adds the DupUp shortcut of its input (the pages'
