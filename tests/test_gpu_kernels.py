@@ -547,6 +547,59 @@ def test_conv_weights_in_registers_sampled(H, W, mode, acc, write_y, g):
     assert err <= 1e-4 * rms + 1e-7 * float(np.max(np.abs(want)))
 
 
+@pytest.mark.parametrize("mode,H,W,cin,cout", [(1, 2048, 4095, 128, 128), (1, 4096, 4095, 64, 64),
+                                              (2, 2047, 4095, 128, 128)])
+def test_conv_at_the_largest_input(mode, H, W, cin, cout):
+    """The 3x3 kernels address their f16 input with 32-bit byte offsets:
+    the largest input they take is just below 0x7fff0000 bytes. At that
+    size (ragged width; the register-weight kernel at 128 channels, the
+    patch kernel at 64; the upsampling form writes a 17 GB frame) the f32
+    result at the borders, the last rows and columns and seeded picks
+    equals the oracle's conv. The input repeats a seeded block of R rows,
+    so the oracle sees each sampled pixel's 3x3 source window from it."""
+    R = 64
+    assert H * W * cin * 2 < 0x7fff0000 and H * W * cin * 2 > 0x7fff0000 - (W + 2) * cin * 4
+    seed = 1300 + mode + cin
+    blk = synth.normal(20, seed, (R, W, cin), 1.0, np.float16)
+    w = synth.normal(20, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
+    b = synth.normal(20, seed + 2, (cout,), 0.02)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    osc = 256.0 if mode == 2 else 1.0
+    xd = dev(blk.reshape(R * W, cin)).repeat((H + R - 1) // R, 1)[:H * W].contiguous()
+    y = torch.empty((Ho * Wo, cout), dtype=torch.float32, device="cuda")
+    y.fill_(float("nan"))
+    ig.conv_nhwc_ex(xd, H, W, cin, mode, packed(w), cout, dev(b), osc, 0, y)
+    torch.cuda.synchronize()
+    # corners, the last row and column (strided), the tail of the row above
+    # the last, and seeded picks
+    pix = np.unique(np.concatenate([
+        np.array([0, Wo - 1, (Ho - 1) * Wo, Ho * Wo - 1], np.int64),
+        (Ho - 1) * Wo + np.arange(0, Wo, 97), np.arange(0, Ho, 61) * Wo + Wo - 1,
+        (Ho - 2) * Wo + np.arange(Wo - 40, Wo), np.random.default_rng(seed).integers(0, Ho * Wo, 160)]))
+    got = host(y[torch.from_numpy(pix).cuda()])
+    assert not np.isnan(got).any()
+    want = np.empty((pix.size, cout))
+    for n, q in enumerate(pix):
+        r, c = divmod(int(q), Wo)
+        # the output pixel's source window in the input (rows and columns
+        # clamped to the frame, whose edges are the conv's zero padding)
+        sr = (lambda v: v >> 1) if mode == 2 else (lambda v: v)
+        r0, r1 = max(0, sr(max(r - 1, 0))), min(H - 1, sr(min(r + 1, Ho - 1)))
+        c0, c1 = max(0, sr(max(c - 1, 0))), min(W - 1, sr(min(c + 1, Wo - 1)))
+        win = blk[np.arange(r0, r1 + 1) % R][:, c0:c1 + 1, :]
+        xc = np.ascontiguousarray(win.transpose(2, 0, 1)).astype(np.float64)
+        rl, cl = r - (2 * r0 if mode == 2 else r0), c - (2 * c0 if mode == 2 else c0)
+        wl = (c1 - c0 + 1) * (2 if mode == 2 else 1)
+        want[n] = osc * O.conv2d_at(xc, w, np.array([rl * wl + cl], np.int64), up2=(mode == 2))[0] + b
+    err = float(np.max(np.abs(got - want)))
+    rms = float(np.sqrt(np.mean(want * want)))
+    print("largest input %dx%dx%d mode %d (%.3f GB in, %.2f GB out, %d px): max|d| %.3e rms %.3e" % (
+        H, W, cin, mode, H * W * cin * 2 / 1e9, Ho * Wo * cout * 4 / 1e9, pix.size, err, rms), flush=True)
+    assert err <= 1e-4 * rms
+    del y, xd
+    torch.cuda.empty_cache()
+
+
 def test_conv_fused_norm_needs_one_tile_per_pixel():
     with pytest.raises(ig.IgError) as e:
         z = dev(np.zeros((4, 64), np.float16))
