@@ -254,7 +254,10 @@ __device__ __forceinline__ float row16_sum(float v)
 // Schedule. A stage is six fragment groups of 12 MFMAs (72 slots). The wait
 // and barrier for the next stage sit between groups 4 and 5: every wave has
 // then read group 5's fragments into registers, so the stage's buffer is
-// free, and the next stage's first fragments load while group 5 runs. The
+// free, and the next stage's first fragments load while group 5 runs, two
+// after each of its first three MFMAs (the four waves leave the barrier
+// together, and six reads each at once held their MFMAs up: 1-1.5% of the
+// plain and fused-norm convs). The
 // epilogue of the tile staged before (the "staged" tile) runs as small
 // items between the MFMAs of the next tile's stages 1-3, and the patch
 // loads go out after the barrier, one per slot from slot 60:
@@ -689,6 +692,16 @@ void k_conv_ws(IgemmArgs p)
                     constexpr int d = h - 63 - 3 * r;
                     if constexpr (d >= 0 && d <= 6 && d % 2 == 0 && (st == NST - 1 || h > 71)) stage_part(acc[r], r, d / 2);
                 });
+                // after the barrier: the next stage's first fragments, two
+                // per slot (all four waves leave the barrier together)
+                if constexpr (i >= 60 && i < 60 + (PH + 1) / 2) {
+                    const u32x4 *sN = lds + ((st + 1) % NBUF) * A_PAD;
+                    const int pc = G::pcol(fx, 0);
+                    const half8 *sa = reinterpret_cast<const half8 *>(sN) + pc * 4 + (fh ^ ((pc >> 2) & 3));
+                    constexpr int p0 = 2 * (i - 60);
+                    bf[0][p0] = sa[p0 * PW * 4];
+                    if constexpr (p0 + 1 < PH) bf[0][p0 + 1] = sa[(p0 + 1) * PW * 4];
+                }
                 // after the barrier: the next tile's patch for this stage's buffer
                 if constexpr (i >= 60 && i < 60 + APW) issue_one(nxt, st, st, i - 60);
             };
@@ -697,9 +710,8 @@ void k_conv_ws(IgemmArgs p)
                 if constexpr (g == 5) {
                     // the next stage's buffer has landed and every wave is
                     // past this stage's LDS reads; its first fragments load
-                    // under group 5's MFMAs
+                    // under group 5's MFMAs (from the hook of slot 60 on)
                     wait_n(std::integral_constant<int, wait_count(st, LPW_P)>{});
-                    load_group(lds + ((st + 1) % NBUF) * A_PAD, 0, bf[0]);
                 } else {
                     // one wait per group: this group's fragments (loaded a
                     // group ago) and the items' LDS accesses have landed
@@ -719,6 +731,8 @@ void k_conv_ws(IgemmArgs p)
                     if constexpr (f < NST * 18 - NWF) mma<true>(acc[tr.r], wr[f], bf[g & 1][tr.pr], kind);
                     else mma<false>(acc[tr.r], wr[f], bf[g & 1][tr.pr], kind);
                     hook(std::integral_constant<int, g * 3 * TH + i>{});
+                    // those reads stay between group 5's first MFMAs
+                    if constexpr (g == 5 && i < 3) __builtin_amdgcn_sched_barrier(0);
                     // the norm's steps stay in their slots (left alone, the
                     // scheduler gathers them at the group's end)
                     if constexpr (NORM) __builtin_amdgcn_sched_barrier(0);
