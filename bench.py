@@ -21,6 +21,9 @@ Also measured, in the same process and on the stream the kernels run on:
   * roofline_cast: the guarded f16 cast at 512x512x128 (same 201 MB);
   * roofline_groupnorm: GroupNorm(32) + SiLU at 512x512x128, algorithmic
     201 MB (its statistics pass reads the input once more);
+  * roofline_groupnorm_gathered: the same GroupNorm when the producing conv
+    gathered the statistics in its epilogue (one read of the input), and
+    the gathering's cost to a 256x256x256 conv (without, with);
   * roofline_attention: the single-pass attention core at 16384 tokens x
     512 (the 1024^2 decode's mid block; 4 m^2 C = 550 GFLOP per launch:
     Q.K^T and P.V) against the f16 MFMA peak;
@@ -361,6 +364,58 @@ def bench_groupnorm_roofline(reps, H=512, W=512, C=128, groups=32):
         lambda st: ig.groupnorm_silu_f16(st[0], M, C, C, groups, None, gamma, beta, 1, 1e-6, ws, nbytes, st[1]),
         reps, M * C * 6, lambda: (x0.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
     return {"avg_ms": ms, "median_ms": med, "bytes": M * C * 6, "sets": nsets}
+
+
+def bench_groupnorm_fused(reps, H=512, W=512, C=128, groups=32):
+    """GroupNorm(32) + SiLU at 512x512x128 when the producing 3x3 conv has
+    gathered the group statistics in its epilogue: the final merge and one
+    read of the stream (201 MB algorithmic, 6 bytes per element). Also the
+    cost of the gathering to the conv: 256x256x256 -> 256 with and without
+    it (both the general-width conv kernel)."""
+    import torch
+
+    import implicit_gemm_conv_nhwc_amd as ig
+
+    M = H * W
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    gamma = torch.rand(C, device=dev, generator=g) + 0.5
+    beta = torch.randn(C, device=dev, generator=g) * 0.1
+
+    def conv_setup(h, w, c):
+        x16 = torch.randn((h * w, c), device=dev, generator=g).half()
+        wt = (torch.randn((c, c, 3, 3), device=dev, generator=g) / (3.0 * c ** 0.5)).half()
+        plane = torch.empty(ig.plane_shape(c, c, 3), dtype=torch.float16, device=dev)
+        ig.pack_conv_weights(wt, c, c, 3, c, c, plane)
+        nb = ig.conv_gn_partials_bytes(1, h, w, groups)
+        return x16, plane, nb, torch.empty(nb // 4, dtype=torch.float32, device=dev)
+
+    x16, plane, nbytes, part = conv_setup(H, W, C)
+    y32 = torch.empty((M, C), dtype=torch.float32, device=dev)
+    ig.conv3x3_gn_stats_nhwc(x16, H, W, C, 1, plane, C, None, 1.0, 0, y32, C, groups, part, nbytes)
+    nchunk = nbytes // (12 * groups)
+    tab = torch.empty(3 * C, dtype=torch.float32, device=dev)
+    ms, nsets, med = _pool_timed(
+        lambda st: ig.groupnorm_silu_f16_from_partials(st[0], M, C, C, groups, gamma, beta, 1, 1e-6, part, nchunk,
+                                                       tab, tab.numel() * 4, st[1]),
+        reps, M * C * 6, lambda: (y32.clone(), torch.empty((M, C), dtype=torch.float16, device=dev)))
+    # the gathering's cost: the same conv with and without it, interleaved
+    h2, c2 = 256, 256
+    x2, plane2, nb2, part2 = conv_setup(h2, h2, c2)
+    ys = [torch.empty((h2 * h2, c2), dtype=torch.float32, device=dev) for _ in range(6)]
+    plain = lambda i: ig.conv_nhwc_ex(x2, h2, h2, c2, 1, plane2, c2, None, 1.0, 0, ys[i % 6])  # noqa: E731
+    gath = lambda i: ig.conv3x3_gn_stats_nhwc(x2, h2, h2, c2, 1, plane2, c2, None, 1.0, 0, ys[i % 6], c2,  # noqa: E731
+                                              groups, part2, nb2)
+    _warm(plain)
+    pm, gm = [], []
+    for _ in range(3):
+        pm.append(_batches(plain, reps)[0])
+        gm.append(_batches(gath, reps)[0])
+    import statistics
+
+    return {"avg_ms": ms, "median_ms": med, "bytes": M * C * 6, "sets": nsets,
+            "conv_plain_us": statistics.median(pm) * 1000, "conv_gather_us": statistics.median(gm) * 1000}
 
 
 def bench_attention_roofline(reps, m=16384, C=512):
@@ -752,6 +807,11 @@ def main():
     gn_gbs = gn["bytes"] / (gn["avg_ms"] / 1000.0) / 1e9
     log("groupnorm 512^2x128 (32 groups): %.2f us, %.0f GB/s algorithmic (%.1f%% of HBM)" % (
         gn["avg_ms"] * 1000, gn_gbs, 100 * gn_gbs / HBM_PEAK_GBS))
+    gnf = bench_groupnorm_fused(args.roof_reps)
+    gnf_gbs = gnf["bytes"] / (gnf["avg_ms"] / 1000.0) / 1e9
+    log("groupnorm 512^2x128 from conv-gathered statistics: %.2f us, %.0f GB/s (%.1f%% of HBM); the gathering "
+        "in a 256^2x256 conv: %.2f -> %.2f us" % (gnf["avg_ms"] * 1000, gnf_gbs, 100 * gnf_gbs / HBM_PEAK_GBS,
+                                                 gnf["conv_plain_us"], gnf["conv_gather_us"]))
     att = bench_attention_roofline(max(5, args.roof_reps // 5))
     att_tf = att["flops"] / (att["avg_ms"] / 1000.0) / 1e12
     log("attention 16384 x 512: %.1f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (
@@ -856,6 +916,18 @@ def main():
             "frac": round(gn_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(gn["avg_ms"] * 1000, 3),
             "median_us": round(gn["median_ms"] * 1000, 3),
+        },
+        "roofline_groupnorm_gathered": {
+            "kernel": "groupnorm_silu_f16_from_partials 512x512x128, 32 groups (statistics gathered by the "
+                      "producing conv; finalize + apply)",
+            "bound": "hbm",
+            "achieved": round(gnf_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gnf_gbs / HBM_PEAK_GBS, 4),
+            "avg_us": round(gnf["avg_ms"] * 1000, 3),
+            "median_us": round(gnf["median_ms"] * 1000, 3),
+            "gathering_in_conv_256x256x256_us": [round(gnf["conv_plain_us"], 3), round(gnf["conv_gather_us"], 3)],
         },
         "roofline_attention": {
             "kernel": "attention_f16 single pass (k_flash + k_flash_merge), 16384 tokens x 512",

@@ -16,10 +16,12 @@ from ._lib import (  # noqa: F401
     UpW,
     combine,
     conv3x3_nhwc,
+    conv3x3_gn_stats_nhwc,
     conv3x3_guard_out_nhwc,
     conv3x3_norm_nhwc,
     conv3x3_out_nchw,
     conv3x3_up2_nhwc,
+    conv_gn_partials_bytes,
     conv_nhwc_ex,
     band_plan,
     set_clock_probe,
@@ -33,6 +35,7 @@ from ._lib import (  # noqa: F401
     attention_f16,
     attention_workspace_bytes,
     groupnorm_silu_f16,
+    groupnorm_silu_f16_from_partials,
     groupnorm_silu_f16_noalloc,
     groupnorm_workspace_bytes,
     guard_cast,

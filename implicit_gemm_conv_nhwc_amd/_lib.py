@@ -81,6 +81,11 @@ _gn = _sig("groupnorm_silu_f16", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                   ctypes.c_size_t, _vp, _vp])
 _gn_na = _sig("groupnorm_silu_f16_noalloc", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _c_float,
                                            _vp, _vp])
+_gn_pb = _sig("ig_conv_gn_partials_bytes", [_c_int, _c_int, _c_int, _c_int], ctypes.c_size_t)
+_conv_gn = _sig("ig_conv3x3_gn_stats_nhwc", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_float, _c_int,
+                                             _vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
+_gn_part = _sig("groupnorm_silu_f16_from_partials", [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_float,
+                                                     _vp, _c_int, _vp, ctypes.c_size_t, _vp, _vp])
 _attn_ws = _sig("ig_attention_workspace_bytes", [_c_int, _c_int], ctypes.c_size_t)
 _attn = _sig("attention_f16", [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, ctypes.c_size_t, _vp, _vp])
 _conv_out = _sig("ig_conv3x3_out_nchw", [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp])
@@ -214,6 +219,22 @@ def groupnorm_silu_f16(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, w
 def groupnorm_silu_f16_noalloc(x, M, cp, c_real, groups, bias, gamma, beta, silu, eps, y, stream=None):
     return _check(_gn_na(_ptr(x), M, cp, c_real, groups, _ptr(bias), _ptr(gamma), _ptr(beta), silu, eps, _ptr(y),
                          _stream(stream)))
+
+
+def conv_gn_partials_bytes(mode, H, W, groups):
+    return int(_gn_pb(mode, H, W, groups))
+
+
+def conv3x3_gn_stats_nhwc(x, H, W, cin_p, mode, w, cout_p, bias, oscale, accumulate, y, c_real, groups, part,
+                          part_bytes, stream=None):
+    return _check(_conv_gn(_ptr(x), H, W, cin_p, mode, _ptr(w), cout_p, _ptr(bias), float(oscale), int(accumulate),
+                           _ptr(y), c_real, groups, _ptr(part), part_bytes, _stream(stream)))
+
+
+def groupnorm_silu_f16_from_partials(x, M, cp, c_real, groups, gamma, beta, silu, eps, part, nchunk, ws, ws_bytes,
+                                     y, stream=None):
+    return _check(_gn_part(_ptr(x), M, cp, c_real, groups, _ptr(gamma), _ptr(beta), silu, eps, _ptr(part), nchunk,
+                           _ptr(ws), ws_bytes, _ptr(y), _stream(stream)))
 
 
 def conv3x3_out_nchw(x, H, W, cin_p, w, cout, cout_p, bias, out, stream=None):

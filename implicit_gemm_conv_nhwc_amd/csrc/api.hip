@@ -276,6 +276,72 @@ int ig_conv3x3_norm_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, c
     return check_launch("conv+norm launch");
 }
 
+size_t ig_conv_gn_partials_bytes(int mode, int H, int W, int groups)
+{
+    if ((mode != 1 && mode != 2) || H < 0 || W < 0 || groups <= 0) return 0;
+    return (size_t)groups * conv_gn_chunks(mode == 1 ? kConv3x3 : kConv3x3Up2, H, W) * 3 * sizeof(float);
+}
+
+int ig_conv3x3_gn_stats_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
+                             const float *bias, float oscale, int accumulate, float *y, int c_real, int groups,
+                             float *part, size_t part_bytes, void *stream)
+{
+    clear_error();
+    if (mode != 1 && mode != 2) return fail(IG_EINVAL, "mode %d is not a 3x3 mode", mode);
+    if (!conv_gn_stats_supported(cout_p, c_real, groups))
+        return fail(IG_EUNSUPPORTED, "GroupNorm(%d) statistics over %d of %d channels: groups of 4..64 channels "
+                                     "dividing 64 only", groups, c_real, cout_p);
+    bool empty;
+    int r = check_conv(x, H, W, cin_p, w, cout_p, bias, y, mode, &empty);
+    if (r || empty) return r;
+    const size_t need = ig_conv_gn_partials_bytes(mode, H, W, groups);
+    if (!part || part_bytes < need)
+        return fail(IG_EWORKSPACE, "GroupNorm partials of %zu bytes, %zu needed", part_bytes, need);
+    if ((r = check_ptr(part, "part"))) return r;
+    IgemmArgs a{};
+    a.a = reinterpret_cast<const _Float16 *>(x);
+    a.b = reinterpret_cast<const _Float16 *>(w);
+    a.bias = bias;
+    a.c = y;
+    a.M = H * W * (mode == 2 ? 4 : 1);
+    a.N = cout_p;
+    a.K = 9 * cin_p;
+    a.lda = cin_p;
+    a.ldb = a.K;
+    a.ldc = cout_p;
+    a.H = H;
+    a.W = W;
+    a.cin_p = cin_p;
+    a.oscale = oscale;
+    a.accumulate = accumulate ? 1 : 0;
+    a.gn_part = part;
+    a.gn_cpg = c_real / groups;
+    a.gn_creal = c_real;
+    a.gn_nchunk = conv_gn_chunks(mode == 1 ? kConv3x3 : kConv3x3Up2, H, W);
+    (void)hipGetLastError();
+    launch_conv_halo(mode == 1 ? kConv3x3 : kConv3x3Up2, a, reinterpret_cast<hipStream_t>(stream));
+    return check_launch("conv+GroupNorm statistics launch");
+}
+
+int groupnorm_silu_f16_from_partials(const float *x, int M, int cp, int c_real, int groups, const float *gamma,
+                                     const float *beta, int silu, float eps, const float *part, int nchunk,
+                                     void *ws, size_t ws_bytes, uint16_t *y, void *stream)
+{
+    clear_error();
+    int r = groupnorm_check(x, M, cp, c_real, groups, nullptr, gamma, beta, eps, y);
+    if (r || M == 0) return r;
+    if (nchunk <= 0) return fail(IG_EINVAL, "nchunk=%d", nchunk);
+    if ((r = check_ptr(part, "part"))) return r;
+    if (!ws || ((uintptr_t)ws & 15) || ws_bytes < (size_t)cp * 3 * sizeof(float))
+        return fail(IG_EWORKSPACE, "GroupNorm table of %zu bytes (16-byte aligned), %zu needed", ws_bytes,
+                    (size_t)cp * 3 * sizeof(float));
+    (void)hipGetLastError();
+    launch_groupnorm_partials(x, M, cp, c_real, groups, gamma, beta, silu, eps, part, nchunk,
+                              static_cast<float *>(ws), reinterpret_cast<_Float16 *>(y),
+                              reinterpret_cast<hipStream_t>(stream));
+    return check_launch("groupnorm (partials) launch");
+}
+
 int gemm1x1(const uint16_t *a, int M, int K, int lda, const uint16_t *b, int N, int ldb,
             const float *bias, float oscale, void *c, int ldc, int c_is_f16, void *stream)
 {

@@ -137,7 +137,36 @@ struct Tile {
     int8v aoff;
 };
 
-template <int MODE, int BN, int NW, bool NORM>
+// GroupNorm statistics in the epilogue: (n, mean, M2) of a thread's values
+// of one group, the batch of four channels of one pixel folded in by Chan,
+// Golub and LeVeque's update (the batch's own mean and squared deviations
+// first, so a large common offset does not cancel), and the merge of two
+// such figures (across lanes and waves)
+struct GnAcc {
+    float n = 0.f, m = 0.f, q = 0.f;
+    __device__ __forceinline__ void fold4(float4 v)
+    {
+        const float bm = 0.25f * ((v.x + v.y) + (v.z + v.w));
+        const float d0 = v.x - bm, d1 = v.y - bm, d2 = v.z - bm, d3 = v.w - bm;
+        const float bq = d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+        const float nn = n + 4.f, w = 4.f * __builtin_amdgcn_rcpf(nn), d = bm - m;
+        m += d * w;
+        q += bq + d * d * n * w;
+        n = nn;
+    }
+    __device__ __forceinline__ void merge(float nb, float mb, float qb)
+    {
+        const float nn = n + nb;
+        if (nb > 0.f) {
+            const float w = nb / nn, d = mb - m;
+            m += d * w;
+            q += qb + d * d * n * w;
+            n = nn;
+        }
+    }
+};
+
+template <int MODE, int BN, int NW, bool NORM, bool GNS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 void k_conv_halo(IgemmArgs p)
 {
@@ -168,6 +197,9 @@ void k_conv_halo(IgemmArgs p)
     // the fused norm's gamma, read from LDS in the epilogue (a tile spans
     // all N = BN channels, so n0 = 0)
     __shared__ __attribute__((aligned(16))) float gam[NORM ? BN : 4];
+    // the waves' GroupNorm partials of a tile: [wave][group of the tile][3]
+    __shared__ float gns[GNS ? NW * 16 * 3 : 1];
+    static_assert(!(GNS && (NORM || BN != 64)), "statistics from the plain 64-channel tiles");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -359,6 +391,10 @@ void k_conv_halo(IgemmArgs p)
 #pragma unroll
     for (int j = 0; j < FN; ++j) bv[j] = p.bias ? p.bias[n0 + wn * (BN / WN) + j * 32 + fx] : 0.f;
     float *out = reinterpret_cast<float *>(p.c);
+    // GroupNorm statistics: a thread's pieces all hold channel quad tid % 16
+    // (pieces tid + NT k, 16 quads per 64-channel pixel row), so one group
+    GnAcc gacc;
+    const bool gn_live = GNS && (n0 + 4 * (tid & 15)) < p.gn_creal;
 #pragma unroll
     for (int q = 0; q < FM; ++q) {
 #pragma unroll
@@ -393,6 +429,9 @@ void k_conv_halo(IgemmArgs p)
                         val.y += o.y;
                         val.z += o.z;
                         val.w += o.w;
+                    }
+                    if constexpr (GNS) {
+                        if (gn_live) gacc.fold4(val);
                     }
                     // streaming store: the tile is written once and not
                     // read again by this kernel
@@ -460,6 +499,35 @@ void k_conv_halo(IgemmArgs p)
         __syncthreads();
     }
     }
+    if constexpr (GNS) {
+        // the tile's partial per group: lanes l, l ^ 16, l ^ 32, l ^ 48 hold
+        // one channel quad, lanes of consecutive quads one group; then the
+        // waves' partials through LDS
+        const int qpg = p.gn_cpg >> 2;
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1)
+            gacc.merge(__shfl_xor(gacc.n, o), __shfl_xor(gacc.m, o), __shfl_xor(gacc.q, o));
+        for (int o = 1; o < qpg; o <<= 1)
+            gacc.merge(__shfl_xor(gacc.n, o), __shfl_xor(gacc.m, o), __shfl_xor(gacc.q, o));
+        if (lane < 16 && lane % qpg == 0) {
+            float *e = gns + (wave * 16 + lane / qpg) * 3;
+            e[0] = gacc.n;
+            e[1] = gacc.m;
+            e[2] = gacc.q;
+        }
+        __syncthreads();
+        const int g = n0 / p.gn_cpg + tid;
+        if (tid < 64 / p.gn_cpg && g * p.gn_cpg < p.gn_creal) {
+            GnAcc t0;
+            for (int w = 0; w < NW; ++w) t0.merge(gns[(w * 16 + tid) * 3], gns[(w * 16 + tid) * 3 + 1], gns[(w * 16 + tid) * 3 + 2]);
+            const int pt = t / n_tiles;  // the pixel tile
+            float *o = p.gn_part + ((int64_t)g * p.gn_nchunk + pt) * 3;
+            o[0] = t0.n;
+            o[1] = t0.m;
+            o[2] = t0.q;
+        }
+        // (the next tile's partials reuse gns only after its stages' barriers)
+    }
     cur = nxt;
     }
 }
@@ -479,7 +547,7 @@ int resident_slots(int per_cu)
     return cus[dev] * per_cu;
 }
 
-template <int MODE, int BN, int NW, bool NORM = false>
+template <int MODE, int BN, int NW, bool NORM = false, bool GNS = false>
 void launch_t(const IgemmArgs &a, hipStream_t s)
 {
     const int Hout = (MODE == kConv3x3Up2) ? 2 * a.H : a.H;
@@ -493,7 +561,7 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
         const int slots = resident_slots(8 / NW) & ~7;
         if (slots > 0 && slots < tiles) grid = slots;
     }
-    hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW, NORM>), dim3(grid), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW, NORM, GNS>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 
 }  // namespace
@@ -524,13 +592,34 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
     if (mode == kConv3x3) {
         const int tiles = ((a.H + TH - 1) / TH) * ((a.W + TW - 1) / TW) * (a.N / 64);
         const int cus = resident_slots(1);
-        if (cus > 0 && tiles <= cus)
+        const bool eight = cus > 0 && tiles <= cus;
+        if (a.gn_part) {
+            if (eight) launch_t<kConv3x3, 64, 8, false, true>(a, s);
+            else launch_t<kConv3x3, 64, 4, false, true>(a, s);
+        } else if (eight) {
             launch_t<kConv3x3, 64, 8>(a, s);
-        else
+        } else {
             launch_t<kConv3x3, 64, 4>(a, s);
+        }
+    } else if (a.gn_part) {
+        launch_t<kConv3x3Up2, 64, 4, false, true>(a, s);
     } else {
         launch_t<kConv3x3Up2, 64, 4>(a, s);
     }
+}
+
+int conv_gn_chunks(int mode, int H, int W)
+{
+    const int Hout = (mode == kConv3x3Up2) ? 2 * H : H;
+    const int Wout = (mode == kConv3x3Up2) ? 2 * W : W;
+    return ((Hout + TH - 1) / TH) * ((Wout + TW - 1) / TW);
+}
+
+bool conv_gn_stats_supported(int cout_p, int c_real, int groups)
+{
+    if (groups <= 0 || c_real <= 0 || c_real > cout_p || c_real % groups) return false;
+    const int cpg = c_real / groups;
+    return cout_p % 64 == 0 && cpg % 4 == 0 && 64 % cpg == 0;
 }
 
 }  // namespace ig

@@ -99,12 +99,14 @@ struct Plan {
     int gn_groups = 0;   // GroupNorm's groups (0: RMS_norm)
     float gn_eps = 0.f;
     size_t max_gn = 0;   // bytes of GroupNorm's per-chunk statistics
+    size_t gn_part = 0;  // bytes of one set of conv-gathered GroupNorm partials
     int m = 0, mp = 0, C = 0, qc = 0;
     bool flash = false;  // single-pass attention (else query chunks)
     int H = 0, W = 0;    // output frame
     int s = 0;           // up blocks s.. run in bands (s == n_up: none)
     int band_rows = 0;   // kept output rows per band
     size_t off_x, off_xb, off_h, off_xn, off_xg, off_q, off_k, off_vt, off_o, off_s, off_p, off_cp, off_gn, total;
+    size_t off_gpx = 0, off_gph = 0, off_gtab = 0;  // GroupNorm partials of x and h, the per-channel table
 };
 
 int check_conv_w(const ig_conv_w &c, const char *name, int k)
@@ -381,6 +383,14 @@ int make_plan(const ig_decoder *d, int h0, int w0, int q_chunk, int band_rows, i
     pl.off_vt = take(C * mp * 2);
     pl.off_cp = take(pl.max_cp * 4);
     pl.off_gn = take(pl.max_gn);
+    if (pl.gn_groups) {
+        // partials of the convs that feed a GroupNorm (the output frame
+        // has the most tiles), for the stream and for conv1's output
+        pl.gn_part = (size_t)pl.gn_groups * conv_gn_chunks(kConv3x3, pl.H, pl.W) * 3 * sizeof(float);
+        pl.off_gpx = take(pl.gn_part);
+        pl.off_gph = take(pl.gn_part);
+        pl.off_gtab = take((size_t)3 * kConvMaxChannels * sizeof(float));
+    }
     if (pl.flash) {
         // the single-pass kernel's key-range partials (if any)
         pl.off_o = take(0);
@@ -406,6 +416,28 @@ struct Run {
     _Float16 *xn, *xg, *q16, *k16, *vt16, *P;
     float *cpb = nullptr;  // an up stage's input, for its DupUp shortcut
     void *gnws = nullptr;  // GroupNorm's statistics
+    // GroupNorm decoders: the statistics of x and of h as gathered by the
+    // conv that last wrote them (chunk counts; 0 when x or h changed since
+    // or the conv could not gather them), and the per-channel table
+    float *gpx = nullptr, *gph = nullptr, *gtab = nullptr;
+    int gpx_n = 0, gph_n = 0;
+
+    // whether a conv of these widths can gather its output's GroupNorm
+    // statistics for the next norm
+    bool gn_gathers(const ig_conv_w &cw) const
+    {
+        return pl.gn_groups && conv_gn_stats_supported(cw.cout_p, cw.cout, pl.gn_groups);
+    }
+    // the norm of the stream x (no bias on read): from the statistics its
+    // producer gathered when it did, else the two-pass norm
+    void norm_x(int M, int cp, int c_real, const float *gamma, const float *beta, int silu, _Float16 *y)
+    {
+        if (gpx_n)
+            launch_groupnorm_partials(x, M, cp, c_real, pl.gn_groups, gamma, beta, silu, pl.gn_eps, gpx, gpx_n, gtab,
+                                      y, s);
+        else
+            norm(x, M, cp, c_real, nullptr, gamma, beta, silu, y);
+    }
 
     // the decoder's norm of M pixels (+ bias on read, + SiLU) -> f16 y
     void norm(const float *in, int M, int cp, int c_real, const float *bias, const float *gamma, const float *beta,
@@ -417,8 +449,10 @@ struct Run {
             launch_rmsnorm(in, M, cp, c_real, bias, gamma, silu, kEps, y, s);
     }
 
-    void conv(int mode, const _Float16 *in, int H, int W, const ig_conv_w &cw, const float *bias,
-              float oscale, int acc, float *out, _Float16 *yg = nullptr)
+    // returns the chunk count of the GroupNorm partials written to gpart
+    // (0 without gpart)
+    int conv(int mode, const _Float16 *in, int H, int W, const ig_conv_w &cw, const float *bias,
+             float oscale, int acc, float *out, _Float16 *yg = nullptr, float *gpart = nullptr)
     {
         IgemmArgs a{};
         a.a = in;
@@ -443,7 +477,16 @@ struct Run {
             a.gscale = ldexpf(1.f, -g);
             a.write_out = 0;
         }
+        int nch = 0;
+        if (gpart) {
+            nch = conv_gn_chunks(mode, H, W);
+            a.gn_part = gpart;
+            a.gn_cpg = cw.cout / pl.gn_groups;
+            a.gn_creal = cw.cout;
+            a.gn_nchunk = nch;
+        }
         launch_igemm(mode, a, s);
+        return nch;
     }
 
     // a 3x3 conv whose epilogue emits f16(RMS_norm(oscale*acc + bias; gamma) -> SiLU)
@@ -534,9 +577,11 @@ struct Run {
                     conv_norm(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, d.norm_out_gamma, d.norm_out_c, xn);
                     normed = true;
                 } else {
-                    conv(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, 0, x);
+                    gpx_n = conv(kConv3x3Up2, up_in, f.rows(), W, u.up, u.up.b, gs, 0, x, nullptr,
+                                 gn_gathers(u.up) && !dup ? gpx : nullptr);
                 }
                 if (dup) {
+                    gpx_n = 0;
                     // x[2y + sy][2x + sx] += the shuffled channels of the
                     // input's row y (the fed rows of the saved input)
                     const int factor = 4 * u.dupup_ft, repeats = u.up.cout * factor / c0;
@@ -556,7 +601,7 @@ struct Run {
     void output(const ig_decoder &d, Span cur, int W, int cp, bool normed, Span keep, int Hf, float *out)
     {
         const int H = cur.rows();
-        if (!normed) norm(x, H * W, cp, d.norm_out_c, nullptr, d.norm_out_gamma, d.norm_out_beta, 1, xn);
+        if (!normed) norm_x(H * W, cp, d.norm_out_c, d.norm_out_gamma, d.norm_out_beta, 1, xn);
         float *o = out + (int64_t)cur.first * W;
         const int64_t plane = (int64_t)Hf * W;
         if (d.conv_out.cout <= 16) {
@@ -584,22 +629,34 @@ struct Run {
             launch_rmsnorm(x, M, cp, r.c1.cin, nullptr, r.g1, 1, kEps, xn, s, xg, g);
             conv(kGemm, xg, H, W, r.sc, r.sc.b, ldexpf(1.f, g), 0, x);
         } else {
-            norm(x, M, cp, r.c1.cin, nullptr, r.g1, r.beta1, 1, xn);
+            norm_x(M, cp, r.c1.cin, r.g1, r.beta1, 1, xn);
             if (r.has_sc) {
                 launch_guard_cast(x, M, cp, nullptr, g, xg, s);
                 conv(kGemm, xg, H, W, r.sc, r.sc.b, ldexpf(1.f, g), 0, x);
+                gpx_n = 0;
             }
         }
+        // conv2 adds into the stream; with a GroupNorm next it gathers the
+        // new stream's statistics (not when it emits only the guarded cast)
+        float *g2 = (gn_gathers(r.c2) && !cast) ? gpx : nullptr;
         if (fusable(r.c1) && !pl.gn_groups) {
             // conv1's epilogue normalises (h + b1) itself; the f16 result
             // goes to the h region (conv1 still reads xn)
             _Float16 *hn = reinterpret_cast<_Float16 *>(h);
             conv_norm(kConv3x3, xn, H, W, r.c1, r.c1.b, 1.f, r.g2, r.c1.cout, hn);
-            conv(kConv3x3, hn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast);
+            gpx_n = conv(kConv3x3, hn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast, g2);
+        } else if (gn_gathers(r.c1)) {
+            // GroupNorm of (h + b1) from conv1's own statistics: conv1 adds
+            // b1 in its epilogue (the same f32 sum the norm would form on
+            // read) and gathers the statistics of what it stores
+            gph_n = conv(kConv3x3, xn, H, W, r.c1, r.c1.b, 1.f, 0, h, nullptr, gph);
+            launch_groupnorm_partials(h, M, r.c1.cout_p, r.c1.cout, pl.gn_groups, r.g2, r.beta2, 1, pl.gn_eps, gph,
+                                      gph_n, gtab, xn, s);
+            gpx_n = conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast, g2);
         } else {
             conv(kConv3x3, xn, H, W, r.c1, nullptr, 1.f, 0, h);
             norm(h, M, r.c1.cout_p, r.c1.cout, r.c1.b, r.g2, r.beta2, 1, xn);
-            conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast);
+            gpx_n = conv(kConv3x3, xn, H, W, r.c2, r.c2.b, 1.f, 1, x, cast, g2);
         }
     }
 
@@ -607,7 +664,8 @@ struct Run {
     void attention(const ig_attn_w &a)
     {
         const int m = pl.m, mp = pl.mp, C = pl.C, qc = pl.qc;
-        norm(x, m, C, C, nullptr, a.gamma, a.beta, 0, xn);
+        norm_x(m, C, C, a.gamma, a.beta, 0, xn);
+        gpx_n = 0;  // the projection adds into the stream
         launch_zero_rows_f16(xn, m, mp, C, s);
         const _Float16 *wq = reinterpret_cast<const _Float16 *>(a.q.w);
         const _Float16 *wk = reinterpret_cast<const _Float16 *>(a.k.w);
@@ -713,11 +771,17 @@ int run_decoder(const ig_decoder *dec, const float *latent, int h0, int w0, int 
           reinterpret_cast<_Float16 *>(w + pl.off_vt), reinterpret_cast<_Float16 *>(w + pl.off_p)};
     r.cpb = reinterpret_cast<float *>(w + pl.off_cp);
     r.gnws = w + pl.off_gn;
+    if (pl.gn_groups) {
+        r.gpx = reinterpret_cast<float *>(w + pl.off_gpx);
+        r.gph = reinterpret_cast<float *>(w + pl.off_gph);
+        r.gtab = reinterpret_cast<float *>(w + pl.off_gtab);
+    }
     hipStream_t s = r.s;
     (void)hipGetLastError();
     // latent -> f16 NHWC -> conv_in, x = conv + b
     launch_latent_ingest(latent, d.zc, h0 * w0, d.conv_in.cin_p, r.xn, s);
-    r.conv(kConv3x3, r.xn, h0, w0, d.conv_in, d.conv_in.b, 1.f, 0, r.x);
+    r.gpx_n = r.conv(kConv3x3, r.xn, h0, w0, d.conv_in, d.conv_in.b, 1.f, 0, r.x, nullptr,
+                     r.gn_gathers(d.conv_in) ? r.gpx : nullptr);
     r.resnet(d.mid[0], h0, w0, d.conv_in.cout_p);
     r.attention(d.attn);
     r.resnet(d.mid[1], h0, w0, d.mid[0].c2.cout_p);

@@ -333,4 +333,22 @@ void launch_groupnorm(const float *x, int M, int cp, int c_real, int groups, con
     hipLaunchKernelGGL(k_gn_apply, dim3((unsigned)blocks), dim3(nt), 0, s, x, M, cp, offset, scale, shift, silu, y);
 }
 
+// The statistics arrive as partials from the producing conv's epilogue
+// (one per pixel tile and group, of the values as stored: no bias on read),
+// so the stream is read once, by the apply pass.
+void launch_groupnorm_partials(const float *x, int M, int cp, int c_real, int groups, const float *gamma,
+                               const float *beta, int silu, float eps, const float *part, int nchunk, float *tab,
+                               _Float16 *y, hipStream_t s)
+{
+    if (M <= 0) return;
+    const int nt = stats_threads(cp);
+    float *offset = tab, *scale = offset + cp, *shift = scale + cp;
+    const int cpg = c_real / groups;
+    hipLaunchKernelGGL(k_gn_final, dim3(groups), dim3(256), 0, s, part, nchunk, cp, c_real, cpg, eps,
+                       static_cast<const float *>(nullptr), gamma, beta, offset, scale, shift);
+    const int rl = nt / (cp / 4);
+    const int64_t blocks = ((int64_t)M + (int64_t)rl * AU - 1) / ((int64_t)rl * AU);
+    hipLaunchKernelGGL(k_gn_apply, dim3((unsigned)blocks), dim3(nt), 0, s, x, M, cp, offset, scale, shift, silu, y);
+}
+
 }  // namespace ig

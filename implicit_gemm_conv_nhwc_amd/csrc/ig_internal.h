@@ -57,6 +57,14 @@ struct IgemmArgs {
     // yg [M][ldc] -- the cast of the stream before an up conv
     _Float16 *yg = nullptr;
     float gscale = 1.f;
+    // 3x3 convs without the norm: with gn_part set, the epilogue also
+    // writes GroupNorm statistics of the (accumulated) f32 result v: for
+    // every pixel tile pt (16 x 32 output pixels, row-major over the frame)
+    // and group g of gn_cpg consecutive real channels (< gn_creal), the
+    // tile's (count, mean, M2) at gn_part[(g * gn_nchunk + pt) * 3]; gn_cpg
+    // divides 64 and is a multiple of 4 (conv_gn_stats_supported)
+    float *gn_part = nullptr;
+    int gn_cpg = 0, gn_creal = 0, gn_nchunk = 0;
     // measurement: when set, the weight-stationary conv's first wave
     // writes the shader-clock and real-time counters at its start and end
     // (clk[0], clk[1], clk[2], clk[3])
@@ -74,6 +82,11 @@ void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s);
 // registers; true when the shape fits (it depends on the channels and the
 // output width, not the height, so bands and whole frames agree).
 bool conv_ws_supported(int mode, const IgemmArgs &a);
+// GroupNorm statistics from the conv's epilogue: the pixel tiles of a 3x3
+// conv's output (the partials' chunk count), and whether groups of cpg
+// channels out of c_real, padded to cout_p, can be gathered there
+int conv_gn_chunks(int mode, int H, int W);
+bool conv_gn_stats_supported(int cout_p, int c_real, int groups);
 void launch_conv_ws(int mode, const IgemmArgs &a, hipStream_t s);
 // The buffer later launches of the weight-stationary conv record their
 // clock counters in (null: none).
@@ -150,6 +163,13 @@ size_t gn_scratch_bytes();
 void launch_groupnorm(const float *x, int M, int cp, int c_real, int groups, const float *bias,
                       const float *gamma, const float *beta, int silu, float eps, void *ws, _Float16 *y,
                       hipStream_t s);
+// GroupNorm of x whose group statistics came as nchunk partial (count,
+// mean, M2) per group in part [groups][nchunk][3] (a conv epilogue's): the
+// final merge and the apply pass only (x is read once). tab: 3 cp floats,
+// 16-byte aligned, for the per-channel offset, scale and shift.
+void launch_groupnorm_partials(const float *x, int M, int cp, int c_real, int groups, const float *gamma,
+                               const float *beta, int silu, float eps, const float *part, int nchunk, float *tab,
+                               _Float16 *y, hipStream_t s);
 void launch_guard_cast(const float *x, int M, int C, const float *bias, int guard_log2,
                        _Float16 *y, hipStream_t s);
 void launch_combine(float *x, const float *h, const float *hb, const float *sv, const float *sb,

@@ -218,6 +218,39 @@ int groupnorm_silu_f16_noalloc(const float *x, int M, int cp, int c_real, int gr
                                const float *gamma, const float *beta, int silu, float eps, uint16_t *y,
                                void *stream);
 
+/* GroupNorm with one read of its input: the producing 3x3 conv gathers the
+ * group statistics in its epilogue, the norm merges them and applies
+ * ([VAE] `GroupNorm::apply` for the definition; page "cortiq-engine
+ * 0.8.72, src/gpu_wgpu/s2v_vae.rs", GN_PART_SRC, whose per-workgroup
+ * partial sums here come from the conv's output tiles instead of a pass of
+ * their own).
+ *
+ * ig_conv3x3_gn_stats_nhwc: ig_conv_nhwc_ex (mode 1 or 2, y written) that
+ * also writes, for each 16 x 32-pixel tile pt of the output frame
+ * (row-major; nchunk = ig_conv_gn_partials_bytes / (12 groups) of them) and each
+ * group g of cpg = c_real / groups consecutive real channels, the tile's
+ * (count, mean, M2 = sum of squared deviations) of the stored values
+ * (after the accumulation, if any) as three floats at
+ * part[(g * nchunk + pt) * 3]. The partials are f32, each tile's folded
+ * four values at a time with Chan, Golub and LeVeque's update.
+ *   part: f32, ig_conv_gn_partials_bytes(mode, H, W, groups) bytes.
+ * cpg must be a multiple of 4 that divides 64 and cout_p a multiple of 64
+ * (IG_EUNSUPPORTED otherwise); IG_EWORKSPACE when part_bytes is short.
+ *
+ * groupnorm_silu_f16_from_partials: groupnorm_silu_f16 of x (no bias on
+ * read: the statistics are of x as stored) with the statistics merged, in
+ * f64, from nchunk such partials per group (part [groups][nchunk][3]);
+ * x is read once. ws: 16-byte-aligned device scratch of at least
+ * 3 cp floats (per-channel offset, scale and shift). Errors as
+ * groupnorm_silu_f16. */
+size_t ig_conv_gn_partials_bytes(int mode, int H, int W, int groups);
+int ig_conv3x3_gn_stats_nhwc(const uint16_t *x, int H, int W, int cin_p, int mode, const uint16_t *w, int cout_p,
+                             const float *bias, float oscale, int accumulate, float *y, int c_real, int groups,
+                             float *part, size_t part_bytes, void *stream);
+int groupnorm_silu_f16_from_partials(const float *x, int M, int cp, int c_real, int groups, const float *gamma,
+                                     const float *beta, int silu, float eps, const float *part, int nchunk,
+                                     void *ws, size_t ws_bytes, uint16_t *y, void *stream);
+
 /* ---------------------------------------------------------------------
  * The range-guarded f16 cast of the raw residual stream ([QI] `guard`,
  * CAST_SRC, `Rec::cast`): y = f16((x + bias) * 2^-guard_log2); the

@@ -137,6 +137,32 @@ def test_validation_rejects_before_enqueueing(ig):
                                           None) == -2
     assert lib.groupnorm_silu_f16_noalloc(fake, 8, 128, 128, 32, None, None, fake, 1, ctypes.c_float(1e-6), fake,
                                           None) == -1
+    # GroupNorm statistics from a conv's epilogue: 3x3 modes only, groups
+    # of 4..64 channels dividing 64, a partials buffer of the stated size
+    assert ig.conv_gn_partials_bytes(1, 64, 64, 32) == 2 * 4 * 32 * 12  # 16 x 32-pixel tiles
+    assert ig.conv_gn_partials_bytes(2, 32, 32, 32) == 2 * 4 * 32 * 12
+    assert ig.conv_gn_partials_bytes(1, 65, 33, 32) == 5 * 2 * 32 * 12  # ragged tiles count
+    assert ig.conv_gn_partials_bytes(0, 64, 64, 32) == 0
+    sz = ig.conv_gn_partials_bytes(1, 16, 32, 32)
+    C = ctypes.c_size_t
+    f = lib.ig_conv3x3_gn_stats_nhwc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(fake, 16, 32, 64, 0, fake, 128, None, 1.0, 0, fake, 128, 32, fake, C(sz), None) == -1  # not 3x3
+    assert f(fake, 16, 32, 64, 1, fake, 320, None, 1.0, 0, fake, 288, 32, fake, C(1 << 20), None) == -2  # 9 per group
+    assert f(fake, 16, 32, 64, 1, fake, 64, None, 1.0, 0, fake, 64, 32, fake, C(1 << 20), None) == -2  # 2 per group
+    assert f(fake, 16, 32, 64, 1, fake, 128, None, 1.0, 0, fake, 128, 32, fake, C(sz - 4), None) == -3
+    assert "partials" in ig.last_error()
+    g = lib.groupnorm_silu_f16_from_partials
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(fake, 8, 128, 128, 32, fake, fake, 1, 1e-6, fake, 0, fake, C(1536), fake, None) == -1
+    assert g(fake, 8, 128, 128, 32, fake, fake, 1, 1e-6, fake, 4, fake, C(1535), fake, None) == -3
+    assert g(fake, 8, 128, 128, 32, fake, fake, 1, 1e-6, fake, 4, ctypes.c_void_p((1 << 20) + 4), C(4096), fake,
+             None) == -3
+    assert g(fake, 8, 128, 128, 3, fake, fake, 1, 1e-6, fake, 4, fake, C(4096), fake, None) == -2
 
 
 def test_decoder_descriptor_validation(ig):

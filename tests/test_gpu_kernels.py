@@ -172,6 +172,101 @@ def test_groupnorm_many_batches_per_workgroup():
     assert np.all((u <= 1) | (d <= bound)) and exact >= 0.97
 
 
+def _merge_partials(part, groups, nchunk):
+    """Per-group (count, mean, M2) from a conv's per-tile partials: the
+    exact parallel combination (sums of counts, count-weighted means, M2s
+    plus the spread of the tile means), in float64."""
+    p = part.reshape(groups, nchunk, 3).astype(np.float64)
+    n = p[..., 0].sum(axis=1)
+    mean = (p[..., 0] * p[..., 1]).sum(axis=1) / n
+    m2 = p[..., 2].sum(axis=1) + (p[..., 0] * (p[..., 1] - mean[:, None]) ** 2).sum(axis=1)
+    return n, mean, m2
+
+
+def _gn_stats_conv(H, W, cin, cout, groups, mode, acc, seed, offset=0.0):
+    """A 3x3 conv that gathers its output's GroupNorm statistics; returns
+    the stored f32 output, the partials, their chunk count and the oracle's
+    conv of the same f16 input (plus the stream it was added to)."""
+    d = {"x": synth.normal(20, 4 * seed, (H, W, cin), 1.0),
+         "w": synth.normal(20, 4 * seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16),
+         "b": synth.normal(20, 4 * seed + 2, (cout,), 0.02).astype(np.float32)}
+    x16 = d["x"].astype(np.float16)
+    Ho, Wo = (2 * H, 2 * W) if mode == 2 else (H, W)
+    y0 = (synth.normal(20, 4 * seed + 3, (Ho * Wo, cout), 1.0) + offset).astype(np.float32) if acc else None
+    y = dev(y0) if acc else nan_f32((Ho * Wo, cout))
+    nbytes = ig.conv_gn_partials_bytes(mode, H, W, groups)
+    nchunk = nbytes // (12 * groups)
+    part = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    ig.conv3x3_gn_stats_nhwc(dev(x16.reshape(H * W, cin)), H, W, cin, mode, packed(d["w"]), cout, dev(d["b"]), 1.0,
+                             acc, y, cout, groups, part, nbytes)
+    xc = nhwc_to_chw(x16.astype(np.float64), H, W)
+    ref = (O.conv2d_up2 if mode == 2 else O.conv2d)(xc, d["w"], d["b"])
+    ref = ref.transpose(1, 2, 0).reshape(Ho * Wo, cout)
+    if acc:
+        ref = ref + y0
+    return host(y), host(part), nchunk, ref
+
+
+@pytest.mark.parametrize("H,W,cin,cout,groups,mode,acc", [
+    (40, 52, 128, 128, 32, 1, 0), (33, 70, 64, 256, 32, 1, 1), (12, 20, 128, 512, 32, 2, 0),
+    (20, 36, 64, 128, 16, 2, 1), (16, 40, 64, 128, 2, 1, 0), (9, 150, 64, 256, 8, 1, 1)])
+def test_conv_gathers_group_statistics(H, W, cin, cout, groups, mode, acc):
+    """The conv's epilogue gathers per-tile GroupNorm statistics of what it
+    stores (after adding into the stream). The output meets the per-conv
+    bar against the oracle; the merged partials give every group's exact
+    count, and mean and variance within f32 folding error of the float64
+    statistics of the stored values (groups of 4 to 64 channels, ragged
+    tiles, plain and upsampled, stored and accumulated)."""
+    got, part, nchunk, ref = _gn_stats_conv(H, W, cin, cout, groups, mode, acc, seed=H + cout)
+    err, rms, ratio = conv_err(got, ref)
+    assert ratio <= CONV_TOL, (err, rms)
+    assert np.all(np.isfinite(part))
+    M, cpg = got.shape[0], cout // groups
+    n, mean, m2 = _merge_partials(part, groups, nchunk)
+    v = got.astype(np.float64).reshape(M, groups, cpg)
+    rmean = v.mean(axis=(0, 2))
+    rvar = v.var(axis=(0, 2))
+    dm = np.abs(mean - rmean) / (np.abs(rmean) + np.sqrt(rvar))
+    dv = np.abs(m2 / n - rvar) / rvar
+    print("gn stats %dx%d %d->%d g=%d mode %d acc %d: %d tiles, mean rel %.2e, var rel %.2e" % (
+        H, W, cin, cout, groups, mode, acc, nchunk, dm.max(), dv.max()))
+    assert np.all(n == M * cpg)
+    assert dm.max() <= 2e-6 and dv.max() <= 2e-5
+
+
+@pytest.mark.parametrize("offset", [0.0, 100.0])
+def test_groupnorm_from_conv_statistics(offset):
+    """GroupNorm of a conv's output from the statistics its epilogue
+    gathered (one read of the stream) against the oracle's GroupNorm of
+    the same stored values, at the standalone GroupNorm's bars: 1 ulp or
+    1e-5 and 99.9% exact; with the stream at mean 100 (the conv adds into
+    it), the mean-dependent bound of the large-mean standalone case and
+    97% exact."""
+    H, W, cin, cout, groups = 48, 64, 64, 256, 32
+    got, part, nchunk, _ = _gn_stats_conv(H, W, cin, cout, groups, 1, 1, seed=5, offset=offset)
+    M = H * W
+    gamma = synth.uniform(18, 90, (cout,), 0.5, 1.5)
+    beta = synth.normal(18, 91, (cout,), 0.1)
+    tab = torch.empty(3 * cout, dtype=torch.float32, device="cuda")
+    y = nan_f16((M, cout))
+    ig.groupnorm_silu_f16_from_partials(dev(got), M, cout, cout, groups, dev(gamma), dev(beta), 1, 1e-6,
+                                        dev(part), nchunk, tab, tab.numel() * 4, y)
+    gy = host(y)
+    ref = O.group_norm(got.T.astype(np.float64), groups, gamma, beta, silu=True).T
+    u = f16_ulps(gy, ref.astype(np.float16))
+    d = np.abs(gy.astype(np.float64) - ref)
+    exact = float(np.mean(u == 0))
+    xg = got.astype(np.float64).reshape(M, groups, cout // groups)
+    mean = xg.mean(axis=(0, 2))
+    inv = 1.0 / np.sqrt(xg.var(axis=(0, 2)) + 1e-6)
+    bound = 1e-5 + 2.0 ** -21 * np.repeat(np.abs(mean) * inv, cout // groups)[None, :] * np.abs(gamma)[None, :]
+    print("groupnorm from conv statistics (stream mean %g): max ulp %d, exact %.5f" % (offset, u.max(), exact))
+    if offset == 0.0:
+        assert np.all((u <= 1) | (d <= 1e-5)) and exact >= 0.999
+    else:
+        assert np.all((u <= 1) | (d <= bound)) and exact >= 0.97
+
+
 def test_groupnorm_workspace_too_small():
     M, cp = 64, 128
     y = nan_f16((M, cp))
