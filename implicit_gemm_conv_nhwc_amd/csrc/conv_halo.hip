@@ -48,6 +48,11 @@
 //    epilogue can instead emit the pixel's RMS_norm (+ SiLU) as f16 from the
 //    staged rows -- the next step of the pages' resnet and output recipes --
 //    so the f32 result is neither stored nor read back;
+//  * for a GroupNorm that follows, the epilogue can also gather the group
+//    statistics of what it stores (per tile and group: count, mean and
+//    sum of squared deviations), so the norm reads its input once
+//    (page "cortiq-engine 0.8.72, src/gpu_wgpu/s2v_vae.rs", GN_PART_SRC,
+//    whose per-workgroup partials come from a pass of their own);
 //  * workgroups are dealt round robin to the 8 XCDs; the tile order is
 //    remapped so each XCD works on a contiguous band of rows (shared halos
 //    and weights stay in its L2).
@@ -569,7 +574,8 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
 void launch_conv_halo(int mode, const IgemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return;
-    if (conv_ws_supported(mode, a)) {
+    // (GroupNorm statistics are gathered by this kernel's epilogue only)
+    if (!a.gn_part && conv_ws_supported(mode, a)) {
         launch_conv_ws(mode, a, s);
         return;
     }

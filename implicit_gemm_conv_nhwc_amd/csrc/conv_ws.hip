@@ -831,7 +831,6 @@ bool conv_ws_supported(int mode, const IgemmArgs &a)
     if (mode != kConv3x3 && mode != kConv3x3Up2) return false;
     if (a.cin_p != 128 || a.N != 128 || a.ldc != 128) return false;
     if (a.ngamma && a.accumulate) return false;
-    if (a.gn_part) return false;  // GroupNorm statistics come from the general conv's epilogue
     const int64_t Hout = (mode == kConv3x3Up2) ? 2LL * a.H : a.H;
     const int64_t Wout = (mode == kConv3x3Up2) ? 2LL * a.W : a.W;
     (void)Hout;
