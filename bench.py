@@ -645,7 +645,11 @@ def digest_counters(path, roof_launches, n_xcd=8, n_simd=1024):
 
     rows = list(csv.DictReader(open(path)))
     kernels = [("conv3x3 512^2x128 (%s)" % ROOF_KERNEL, _is_roof, roof_launches, None, None),
-               ("attention 16384 x 512 (k_flash)", lambda n: "k_flash(" in n or "k_flashEN" in n, 10, None, None)]
+               # the single-pass kernel at 16384 tokens (128 queries per
+               # workgroup, key ranges split over 256 workgroups): the
+               # roofline's grid; the 256^2 and 2048^2 decodes after it
+               # run other grids
+               ("attention 16384 x 512 (k_flash)", lambda n: "k_flash<" in n or "k_flashILi" in n, 10, "65536", None)]
     # the 1024^2 decode's convs: every dispatch before the roofline region
     # (the decodes run first), the last 10 of each conv kernel and grid
     t_roof = min([int(r["Start_Timestamp"]) for r in rows if _is_roof(r["Kernel_Name"])] or [1 << 62])
