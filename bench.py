@@ -158,13 +158,13 @@ def decode_flops(spec, h0, w0):
 # ---------------------------------------------------------------------------
 
 
-def bench_decode(steps, warmup, h0, q_chunk, graph=False):
+def bench_decode(steps, warmup, h0, q_chunk, graph=False, norm="rms"):
     import torch
 
     import implicit_gemm_conv_nhwc_amd as ig
     import synth
 
-    spec = synth.decoder_spec()
+    spec = synth.decoder_spec(norm=norm)
     w = synth.decoder_weights(spec, seed_config=4, conv_in_gain=2.0 ** 11)
     z = synth.decoder_latent(h0, h0, zc=spec.zc, config=5, scale=8.0)
     dd = ig.DeviceDecoder(w)
@@ -823,13 +823,13 @@ def main():
 
     # the other configurations' figures
     decodes = {}
-    for lat, st, wu in ((32, 10, 3), (256, 3, 1)):
-        dx = bench_decode(st, wu, lat, args.q_chunk)
-        decodes["%dx%d" % (dx["H"], dx["H"])] = {
+    for lat, st, wu, nm in ((32, 10, 3, "rms"), (256, 3, 1, "rms"), (128, 10, 3, "group")):
+        dx = bench_decode(st, wu, lat, args.q_chunk, norm=nm)
+        decodes["%dx%d%s" % (dx["H"], dx["H"], "" if nm == "rms" else "_groupnorm")] = {
             "median_s": round(dx["median_ms"] / 1000.0, 6), "mean_s": round(dx["event_ms"] / st / 1000.0, 6),
             "steps": st, "tflop": round(dx["flops"] / 1e12, 4),
             "tflops": round(dx["flops"] / (dx["median_ms"] / 1000.0) / 1e12, 2), "output_finite": dx["finite"]}
-        log("decode %d^2: median %.3f ms" % (dx["H"], dx["median_ms"]))
+        log("decode %d^2 (%s): median %.3f ms" % (dx["H"], nm, dx["median_ms"]))
     cfg2 = bench_cfg2(args.roof_reps)
     log("config 2:", json.dumps(cfg2))
     cfg3p = {}
