@@ -43,7 +43,9 @@
 //    32 on the other half) then touches 16 distinct bank groups in each
 //    pass, where the plain 32-byte pitch would conflict two ways;
 //  * the f32 tile leaves through LDS: every tile row goes out as one
-//    contiguous run of 16-byte stores;
+//    contiguous run of 16-byte stores; a conv that adds into the stream
+//    (a template instantiation of its own) loads a pass's stream values
+//    all together under the staging barrier;
 //  * when the tile spans all of a pixel's channels (N = 64 or 128) the
 //    epilogue can instead emit the pixel's RMS_norm (+ SiLU) as f16 from the
 //    staged rows -- the next step of the pages' resnet and output recipes --
@@ -171,7 +173,7 @@ struct GnAcc {
     }
 };
 
-template <int MODE, int BN, int NW, bool NORM, bool GNS = false>
+template <int MODE, int BN, int NW, bool NORM, bool GNS = false, bool ACC = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 void k_conv_halo(IgemmArgs p)
 {
@@ -390,7 +392,7 @@ void k_conv_halo(IgemmArgs p)
     // stage in the last stage's buffer only (the launcher keeps tiles too
     // wide for one buffer to one tile per workgroup).
     const float osc = p.oscale;
-    const bool accum = p.accumulate != 0;
+    static_assert(!(ACC && NORM), "the fused norm does not accumulate");
     float *stg = reinterpret_cast<float *>(lds + (has_next ? ((gs - 1) & 1) * STAGE : 0));
     float bv[FN];
 #pragma unroll
@@ -404,6 +406,8 @@ void k_conv_halo(IgemmArgs p)
     for (int q = 0; q < FM; ++q) {
 #pragma unroll
     for (int h = 0; h < 4 / RS; ++h) {
+        constexpr int V4 = RS * TW * BN / 4;  // 16-byte pieces staged per pass
+        constexpr int NPT = (V4 + NT - 1) / NT;  // pieces per thread
         // pass (q, h): wave row groups h RS .. h RS + RS - 1 stage their row q
         if (wm / RS == h) {
 #pragma unroll
@@ -414,45 +418,73 @@ void k_conv_halo(IgemmArgs p)
                     stg[((wm % RS) * TW + px) * SP + wn * (BN / WN) + j * 32 + fx] = osc * acc[q][j][r] + bv[j];
                 }
         }
-        __syncthreads();
-        constexpr int V4 = RS * TW * BN / 4;  // 16-byte pieces staged per pass
-        if ((!NORM && p.yg) || p.write_out) {
+        // an accumulating pass loads the stream values it adds to all at
+        // once, under the staging barrier: one piece's load after the
+        // previous piece's store (the compiler cannot tell they never
+        // overlap) waited a full memory round trip each
+        // (with 8 waves a thread has only half the pieces, and loading them
+        // in the loop below measured faster; with the GroupNorm statistics
+        // as well, the 4-wave kernel has no registers left for them)
+        constexpr bool HOIST = ACC && NW == 4 && !GNS;
+        f32x4 res[HOIST ? NPT : 1];
+        if constexpr (HOIST) {
 #pragma unroll
-            for (int v = tid; v < V4; v += NT) {
-                const int e = v * 4;
-                const int wr = e / (TW * BN);  // staged row: tile row FM (h RS + wr) + q
-                const int px = (e / BN) % TW;
-                const int ch = e % BN;
-                const int oy = y0 + FM * (h * RS + wr) + q, ox = x0 + px;
-                if (oy < Hout && ox < Wout) {
-                    float4 val = (SP == BN) ? reinterpret_cast<const float4 *>(stg)[v]
-                                            : *reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + ch);
-                    float *dst = out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch;
-                    if (accum) {
-                        const float4 o = *reinterpret_cast<const float4 *>(dst);
-                        val.x += o.x;
-                        val.y += o.y;
-                        val.z += o.z;
-                        val.w += o.w;
-                    }
-                    if constexpr (GNS) {
-                        if (gn_live) gacc.fold4(val);
-                    }
-                    // streaming store: the tile is written once and not
-                    // read again by this kernel
-                    if (p.write_out)
-                        __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w},
-                                                    reinterpret_cast<f32x4 *>(dst));
-                    if (!NORM && p.yg) {
-                        const float gs = p.gscale;
-                        half4v h;
-                        h[0] = (_Float16)(val.x * gs);
-                        h[1] = (_Float16)(val.y * gs);
-                        h[2] = (_Float16)(val.z * gs);
-                        h[3] = (_Float16)(val.w * gs);
-                        *reinterpret_cast<half4v *>(p.yg + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch) = h;
-                    }
+            for (int k = 0; k < NPT; ++k) {
+                // piece tid + NT k: staged row, pixel and channel as below
+                const int e = (tid + NT * k) * 4;
+                const int oy = y0 + FM * (h * RS + e / (TW * BN)) + q, ox = x0 + (e / BN) % TW, ch = e % BN;
+                const bool in = oy < Hout && ox < Wout;
+                res[k] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+                                  out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch))
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        __syncthreads();
+        static_assert(V4 % NT == 0, "whole pieces per thread");
+        // piece v: its staged value (plus the stream value r when
+        // accumulating) to the f32 output, the guarded cast, the statistics
+        auto emit = [&](int v, const f32x4 &r) __attribute__((always_inline)) {
+            const int e = v * 4;
+            const int wr = e / (TW * BN);  // staged row: tile row FM (h RS + wr) + q
+            const int px = (e / BN) % TW;
+            const int ch = e % BN;
+            const int oy = y0 + FM * (h * RS + wr) + q, ox = x0 + px;
+            if (oy < Hout && ox < Wout) {
+                float4 val = (SP == BN) ? reinterpret_cast<const float4 *>(stg)[v]
+                                        : *reinterpret_cast<const float4 *>(stg + (wr * TW + px) * SP + ch);
+                float *dst = out + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch;
+                if constexpr (ACC) {
+                    const f32x4 o = HOIST ? r : *reinterpret_cast<const f32x4 *>(dst);
+                    val.x += o[0];
+                    val.y += o[1];
+                    val.z += o[2];
+                    val.w += o[3];
                 }
+                if constexpr (GNS) {
+                    if (gn_live) gacc.fold4(val);
+                }
+                // streaming store: the tile is written once and not read
+                // again by this kernel
+                if (p.write_out)
+                    __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w}, reinterpret_cast<f32x4 *>(dst));
+                if (!NORM && p.yg) {
+                    const float gs = p.gscale;
+                    half4v hv;
+                    hv[0] = (_Float16)(val.x * gs);
+                    hv[1] = (_Float16)(val.y * gs);
+                    hv[2] = (_Float16)(val.z * gs);
+                    hv[3] = (_Float16)(val.w * gs);
+                    *reinterpret_cast<half4v *>(p.yg + ((int64_t)oy * Wout + ox) * p.ldc + n0 + ch) = hv;
+                }
+            }
+        };
+        if ((!NORM && p.yg) || p.write_out) {
+            if constexpr (HOIST) {
+#pragma unroll
+                for (int k = 0; k < NPT; ++k) emit(tid + NT * k, res[k]);
+            } else {
+#pragma unroll
+                for (int v = tid; v < V4; v += NT) emit(v, f32x4{0.f, 0.f, 0.f, 0.f});
             }
         }
         if constexpr (NORM) {
@@ -565,6 +597,12 @@ void launch_t(const IgemmArgs &a, hipStream_t s)
     if (can_walk<MODE, BN, NORM>()) {
         const int slots = resident_slots(8 / NW) & ~7;
         if (slots > 0 && slots < tiles) grid = slots;
+    }
+    if constexpr (!NORM) {
+        if (a.accumulate) {
+            hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW, NORM, GNS, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+            return;
+        }
     }
     hipLaunchKernelGGL((k_conv_halo<MODE, BN, NW, NORM, GNS>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
