@@ -717,6 +717,15 @@ def digest_trace(path, roof_launches):
         avg = sum(x[2] for x in last) / len(last)
         print("roofline region: last %d dispatches of %s (grid %s): avg %.2f us" % (
             len(last), ROOF_KERNEL, last[-1][3], avg))
+    # the roofline's timed launches in order: roof_launches for the average,
+    # roof_launches in batches of 10 for the median, then 5 with the clock
+    # probe set (bench_conv_roofline)
+    n_probe = 5
+    if len(roof) >= 2 * roof_launches + n_probe:
+        a = roof[-(2 * roof_launches + n_probe):-(roof_launches + n_probe)]
+        b = roof[-(roof_launches + n_probe):-n_probe]
+        print("  the bench's average launches: avg %.2f us; its median batches: avg %.2f us, median %.2f us" % (
+            sum(x[2] for x in a) / len(a), sum(x[2] for x in b) / len(b), sorted(x[2] for x in b)[len(b) // 2]))
     # the last 1024^2 decode alone (the decodes before the roofline region):
     # from its latent cast (k_latent) to its output conv (k_conv_out), by
     # kernel and grid
