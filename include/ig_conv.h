@@ -285,11 +285,14 @@ int ig_softmax_rows_f16(const float *S, int rows, int lds, int valid, int ncols,
  * S = q.k^T / sqrt(C), row softmax, O = P.V, V's bias after the product;
  * [VAE] `AttnBlock::apply`: max-subtracted softmax):
  *   out[i][c] = f16( sum_{j<m} softmax_j(q_i . k_j / sqrt(C)) vt[c][j] + bv[c] )
- * The softmax is taken online over blocks of 32 keys (a running max and
- * sum per query); no score or probability matrix is stored. Each block's
- * weights are rounded to f16 relative to the running max (the chunked
- * path rounds the normalised probabilities instead), so the two agree
- * to f16 rounding, not bit for bit.
+ * The softmax is taken online over blocks of 32 keys (a running sum per
+ * query); no score or probability matrix is stored. Each block's weights
+ * exp(s - ref) are rounded to f16 against a per-query reference ref fixed
+ * for the pass (the first block's max; a later block more than 2^15 above
+ * it makes the kernel redo the pass with the true max), and divided by
+ * their sum at the end (the chunked path rounds the normalised
+ * probabilities instead), so the two agree to f16 rounding, not bit for
+ * bit.
  *   q, k: f16 [ld][C] row-major; rows m..ld-1 are read, never used.
  *   vt:   f16 V^T [C][ld].
  *   bv:   f32 [C] or NULL.      out: f16 [m][C].

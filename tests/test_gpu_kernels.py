@@ -922,8 +922,8 @@ def test_rejected_call_leaves_output_untouched():
 def _attn_inputs(m, kind, seed, C=512):
     """q, k [m][C], V^T [C][m], bv: f16 operands with the decoder's
     scale (entries ~ N(0, 1): scores q.k / sqrt(C) ~ N(0, 1)).
-    kind: 'flat'; 'growing' (key norms grow along the sequence, so the
-    running max is raised block after block); 'self' (k = q: each query's
+    kind: 'flat'; 'growing' (key norms grow along the sequence, so later
+    blocks' maxima pass the first block's, the kernel's reference); 'self' (k = q: each query's
     own key dominates by ~sqrt(C) in the exponent)."""
     q = synth.normal(7, seed, (m, C), 1.0, np.float16)
     k = synth.normal(7, seed + 1, (m, C), 1.0, np.float16)
@@ -939,7 +939,7 @@ def _attn_inputs(m, kind, seed, C=512):
 def _attn_tol(o_ref, p, vt):
     """Per-element bound: f16 rounding of the output (half an ulp, 2^-11
     relative) and of every weight (2^-11 relative, the weights' f16 grid
-    relative to a running max or to the row sum), each doubled, plus f32
+    relative to the kernel's reference max or to the row sum), each doubled, plus f32
     accumulation slack."""
     pv = np.matmul(p, np.abs(vt.astype(np.float64)).T)
     return 2.0 ** -10 * (np.abs(o_ref) + pv) + 1e-6
