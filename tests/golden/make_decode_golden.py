@@ -16,6 +16,10 @@ Only ``oracle`` and ``synth`` are used; no value comes from the GPU path.
 
     python tests/golden/make_decode_golden.py --size 1024
     python tests/golden/make_decode_golden.py --size 2048
+    python tests/golden/make_decode_golden.py --size 1024 --norm group
+
+``--norm group`` stores the GroupNorm (FLUX-class) decoder of the same
+seeds: every norm site GroupNorm(32, 1e-6) with its beta.
 """
 
 from __future__ import annotations
@@ -42,13 +46,17 @@ LATENT_SCALE = 8.0
 GUARD_LOG2 = 8
 
 
-def golden_path(size: int) -> str:
-    return os.path.join(HERE, "decode_%d_rows.npz" % size)
+def _stem(size: int, norm: str = "rms") -> str:
+    return "decode_%d%s_rows" % (size, "" if norm == "rms" else "_" + norm)
 
 
-def inputs(size: int):
+def golden_path(size: int, norm: str = "rms") -> str:
+    return os.path.join(HERE, _stem(size, norm) + ".npz")
+
+
+def inputs(size: int, norm: str = "rms"):
     """The seeded weights and latent of the full-size decode."""
-    spec = synth.decoder_spec()
+    spec = synth.decoder_spec(norm=norm)
     w = synth.decoder_weights(spec, seed_config=4, conv_in_gain=2.0 ** GAIN_LOG2)
     h0 = size // 8
     z = synth.decoder_latent(h0, h0, zc=spec.zc, config=5, scale=LATENT_SCALE)
@@ -76,9 +84,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--size", type=int, choices=sorted(STRIDE), default=1024)
     ap.add_argument("--q-chunk", type=int, default=4096)
+    ap.add_argument("--norm", choices=("rms", "group"), default="rms")
     a = ap.parse_args()
     O.build()
-    w, z = inputs(a.size)
+    w, z = inputs(a.size, a.norm)
     t0 = time.time()
     tr = O.Trace()
     out = O.decode(w, z, guard_log2=GUARD_LOG2, q_chunk=a.q_chunk, trace=tr)
@@ -89,7 +98,7 @@ def main():
     frows = np.arange(0, a.size, 8 * stride)
     u8 = O.to_u8(out).astype(np.uint8)
     np.savez_compressed(
-        golden_path(a.size),
+        golden_path(a.size, a.norm),
         rows=rows.astype(np.int32),
         u8=np.ascontiguousarray(u8[:, rows, :]),
         frows=frows.astype(np.int32),
@@ -98,6 +107,7 @@ def main():
     )
     meta = {
         "size": a.size,
+        "norm": a.norm,
         "latent": [16, a.size // 8, a.size // 8],
         "latent_scale": LATENT_SCALE,
         "conv_in_gain_log2": GAIN_LOG2,
@@ -110,9 +120,10 @@ def main():
         "clipped_fraction": float(np.mean(np.abs(out) > 1.0)),
         "guard_max": tr.guard_max,
         "oracle_seconds": round(secs, 1),
-        "command": "python tests/golden/make_decode_golden.py --size %d" % a.size,
+        "command": "python tests/golden/make_decode_golden.py --size %d%s" % (
+            a.size, "" if a.norm == "rms" else " --norm " + a.norm),
     }
-    with open(os.path.join(HERE, "decode_%d_rows.json" % a.size), "w") as f:
+    with open(os.path.join(HERE, _stem(a.size, a.norm) + ".json"), "w") as f:
         json.dump(meta, f, indent=1)
     print(json.dumps(meta, indent=1))
 

@@ -291,26 +291,28 @@ def test_workspace_too_small_leaves_output_untouched(full_decoder):
     assert torch.isnan(out).all()
 
 
-def _load_golden(size):
+def _load_golden(size, norm="rms"):
     sys.path.insert(0, GOLDEN)
     import make_decode_golden as mg
 
-    path = mg.golden_path(size)
+    path = mg.golden_path(size, norm)
     if not os.path.exists(path):
         pytest.skip("no stored oracle rows for %d^2 (tests/golden/make_decode_golden.py)" % size)
     with np.load(path) as g:
         return mg, {k: g[k] for k in g.files}
 
 
-@pytest.mark.parametrize("size,q_chunk", [(1024, 0), (1024, 16384), (2048, 0)])
-def test_full_size_decode_against_stored_oracle_rows(size, q_chunk):
+@pytest.mark.parametrize("size,q_chunk,norm", [(1024, 0, "rms"), (1024, 16384, "rms"), (2048, 0, "rms"),
+                                             (1024, 0, "group")])
+def test_full_size_decode_against_stored_oracle_rows(size, q_chunk, norm):
     """The full-size decode, launched as the benchmark launches it (guard 8,
     latent N(0,1)*8, conv_in gain 2^11; q_chunk 0 = the single-pass
     attention, > 0 = the chunked path), against the oracle's stored rows:
     u8 PSNR >= 60 dB over every sampled row, plus the float rows' max |d|
-    relative to their RMS (reported)."""
-    mg, g = _load_golden(size)
-    w, z = mg.inputs(size)
+    relative to their RMS (reported). norm "group": the GroupNorm decoder of
+    the same seeds, its norms from the statistics the convs gather."""
+    mg, g = _load_golden(size, norm)
+    w, z = mg.inputs(size, norm)
     assert float(np.max(g["guard_max"])) > 65504.0  # the guard is exercised
     dd = ig.DeviceDecoder(w)
     h0 = size // 8
@@ -329,8 +331,8 @@ def test_full_size_decode_against_stored_oracle_rows(size, q_chunk):
     unclipped = np.abs(ref_f) <= 1.0
     p_unclipped = O.psnr_u8(got_f[unclipped], ref_f[unclipped])
     rel = float(np.max(np.abs(got_f - ref_f)) / np.sqrt(np.mean(ref_f ** 2)))
-    print("%d^2 (q_chunk %d): sampled-row PSNR %.2f dB (unclipped float rows %.2f dB), max|d|/RMS %.3e, "
-          "u8 levels off: %d of %d" % (size, q_chunk, p, p_unclipped, rel, int(np.count_nonzero(d)), d.size),
+    print("%d^2 %s (q_chunk %d): sampled-row PSNR %.2f dB (unclipped float rows %.2f dB), max|d|/RMS %.3e, "
+          "u8 levels off: %d of %d" % (size, norm, q_chunk, p, p_unclipped, rel, int(np.count_nonzero(d)), d.size),
           flush=True)
     assert p >= PSNR_MIN
     assert p_unclipped >= PSNR_MIN
