@@ -87,13 +87,8 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
     constexpr int PER_WAVE = T_INSTR / 8;
     constexpr int STAGE = (BM + BN) * UPR;
     static_assert(T_INSTR % 8 == 0 && FM >= 1 && FN >= 1, "tile shape");
-    // stage buffers: three (the loads of stage st + 2 stream in during
-    // stage st) when they fit in 144 KB and leave as many workgroups per
-    // CU (of 160 KB) as two do, else two
-    constexpr int SB = STAGE * 16;
-    constexpr int NBUF = (3 * SB <= 144 * 1024 && 160 * 1024 / (3 * SB) >= 160 * 1024 / (2 * SB)) ? 3 : 2;
 
-    __shared__ __attribute__((aligned(16))) u32x4 lds[NBUF * STAGE];
+    __shared__ __attribute__((aligned(16))) u32x4 lds[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -167,21 +162,11 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
 
     const int nst = p.K / KST;
     const int swz = (fx >> 1) & 7;  // rows wm*TM + 32i + fx share bits 1..3 with fx
-    // wait for every stage but the newest one in flight (this wave's
-    // PER_WAVE loads, issued last), then a barrier with no drain of the
-    // loads still streaming
-    auto stage_wait = [&](bool newest_in_flight) __attribute__((always_inline)) {
-        if (NBUF == 3 && newest_in_flight)
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(PER_WAVE) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    };
     issue(0, 0, 0, PER_WAVE);
-    if (NBUF == 3 && nst > 1) issue(1, 1, 0, PER_WAVE);
-    stage_wait(nst > 1);
-    int buf = 0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     for (int st = 0; st < nst; ++st) {
-        const int nbuf = buf == 0 ? NBUF - 1 : buf - 1;  // (st + NBUF - 1) mod NBUF
+        const int buf = st & 1;
         const u32x4 *sA = lds + buf * STAGE;
         const u32x4 *sB = sA + BM * UPR;
         // each K step reads the next step's fragments before its MFMAs, so
@@ -197,7 +182,7 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
         frags(0, af[0], bf[0]);
 #pragma unroll
         for (int ks = 0; ks < KST / 16; ++ks) {
-            if (st + NBUF - 1 < nst) issue(st + NBUF - 1, nbuf, ks * PER_WAVE / 4, (ks + 1) * PER_WAVE / 4);
+            if (st + 1 < nst) issue(st + 1, buf ^ 1, ks * PER_WAVE / 4, (ks + 1) * PER_WAVE / 4);
             if (ks + 1 < KST / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -206,8 +191,8 @@ __global__ __launch_bounds__(NT) void k_gemm2(Gemm2Args p)
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
         }
-        stage_wait(st + NBUF - 1 < nst);
-        buf = buf + 1 == NBUF ? 0 : buf + 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     }
 
     // epilogue: accumulator (i, j) register 4q + e of this lane is C[m][n]
