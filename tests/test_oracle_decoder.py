@@ -1,9 +1,11 @@
 """The oracle's synthetic decoder: shapes, the guard's effect, and agreement
-between its f16-emulating and pure-float64 modes. The decoder as a whole has
-no values printed on the pages, so its parity is unpinned; these tests pin
-the composition's plumbing and the guard's behaviour (page "cortiq-engine
-0.8.3, src/gpu_wgpu/qi21_vae.rs", `guard`: unguarded f16 casts of a stream
-past the f16 range turned most of an image into NaN)."""
+between its f16-emulating and pure-float64 modes. The pages print no decoder
+output values; the composition itself (order, bias sites, shortcut, guard,
+attention, DupUp, GroupNorm) is pinned in test_oracle_composition.py against
+an independent float64 transcription of the recipe. These tests cover the
+plumbing and the guard's behaviour (page "cortiq-engine 0.8.3,
+src/gpu_wgpu/qi21_vae.rs", `guard`: unguarded f16 casts of a stream past the
+f16 range turned most of an image into NaN)."""
 
 import os
 import sys
