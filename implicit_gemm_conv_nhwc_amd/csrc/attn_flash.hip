@@ -118,6 +118,15 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, const void *lds_dst, int voff,
                  : "memory");
 }
 
+// max(a, b, c) of finite scores, as one v_max3_f32 (fmaxf on values the
+// compiler cannot prove canonical adds a canonicalizing max per operand)
+__device__ __forceinline__ float max3_raw(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // MFMA row -> key within a block: bits 2 and 3 swapped
 __device__ __forceinline__ int key_of_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -291,18 +300,17 @@ void k_flash(FlashArgs p)
         }
     };
 
-    // softmax step g of a block whose scores are in sacc (lane (r, h)
+    // softmax step g of a block whose raw scores are in sacc (lane (r, h)
     // register j: query q0 + r, key 8 h + j (j < 8) or 16 + 8 h + (j - 8)
-    // of the block), turned in place into log2-domain scores, then into
-    // the weights 2^(t - ref) of the keys below lim. ref is the query's
+    // of the block): the block's max of the raw scores, taken to the log2
+    // domain afterwards (the scale sl2 > 0 commutes with the max), then the
+    // weights 2^(t sl2 - ref) of the keys below lim. ref is the query's
     // reference max, fixed for the pass (first: the range's first block's
     // max); a block whose max exceeds it by more than the headroom marks
     // the wave for a second pass with ref = the range's max.
     auto softmax_step = [&](int g, f32x16 &t, int lim, half8 (&pk)[2], bool first) __attribute__((always_inline)) {
         if (g == 0 || g == 1) {
-#pragma unroll
-            for (int j = 8 * g; j < 8 * g + 8; ++j) t[j] *= sl2;
-            if (g == 1 && lim < BK) {
+            if (g == 0 && lim < BK) {
                 // the sequence's last, partial block: keys >= m weigh 0
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
@@ -310,14 +318,13 @@ void k_flash(FlashArgs p)
                     if (key >= lim) t[j] = kNegBig;
                 }
             }
-        } else if (g == 2) {
-            const float m0 = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-            const float m1 = fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7]));
-            const float m2 = fmaxf(fmaxf(t[8], t[9]), fmaxf(t[10], t[11]));
-            const float m3 = fmaxf(fmaxf(t[12], t[13]), fmaxf(t[14], t[15]));
-            bmax = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+            const int j0 = 8 * g;
+            const float a = max3_raw(t[j0], t[j0 + 1], t[j0 + 2]);
+            const float b = max3_raw(t[j0 + 3], t[j0 + 4], t[j0 + 5]);
+            const float m = max3_raw(a, b, max3_raw(t[j0 + 6], t[j0 + 7], t[j0 + 7]));
+            bmax = g == 0 ? m : max3_raw(bmax, m, m);
         } else if (g == 3) {
-            const float bm = fmaxf(bmax, __shfl_xor(bmax, 32));
+            const float bm = sl2 * max3_raw(bmax, __shfl_xor(bmax, 32), bmax);
             if (first) ref = bm;
             over = over || bm > ref + kHeadroom;
             mtrue = fmaxf(mtrue, bm);
@@ -326,7 +333,7 @@ void k_flash(FlashArgs p)
             float w[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                w[e] = __builtin_amdgcn_exp2f(t[j0 + e] - ref);
+                w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j0 + e], sl2, -ref));
                 pk[g - 4][e] = (_Float16)w[e];
             }
             lsum += ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
