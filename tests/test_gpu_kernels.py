@@ -75,7 +75,7 @@ def test_rmsnorm_config1():
 @pytest.mark.parametrize("c,cp,with_bias,silu", [(288, 320, True, True), (144, 192, False, True),
                                                  (128, 128, True, False), (64, 64, True, True),
                                                  (512, 512, False, True), (576, 576, True, True),
-                                                 (1000, 1024, True, False)])
+                                                 (700, 768, True, True), (1000, 1024, True, False)])
 def test_rmsnorm_widths_bias_padding(c, cp, with_bias, silu):
     H, W = 7, 9  # M = 63, not a multiple of the 16-pixel block
     x = synth.normal(11, c, (H, W, c), 4.0)
@@ -421,10 +421,12 @@ def test_conv1x1_isolated(H, W, cin, cout):
 
 
 @pytest.mark.parametrize("H,W,cin,cout", [(17, 45, 128, 3), (8, 32, 64, 1), (40, 70, 192, 16), (33, 31, 128, 5),
-                                          (1, 1, 64, 3), (64, 64, 128, 3)])
+                                          (1, 1, 64, 3), (64, 64, 128, 3), (9, 33, 256, 2), (24, 40, 128, 4)])
 def test_output_conv_nchw(H, W, cin, cout):
     """The decoder's output conv: few output channels, NCHW frame + bias,
-    against the oracle's convolution on the same f16 input."""
+    against the oracle's convolution on the same f16 input (up to 3
+    channels the nine taps' products side by side, 4 and more one tap per
+    MFMA)."""
     seed = 300 + H + cout
     x16 = synth.normal(16, seed, (H, W, cin), 1.0, np.float16)
     w = synth.normal(16, seed + 1, (cout, cin, 3, 3), 1.0 / (9 * cin), np.float16)
