@@ -784,8 +784,8 @@ def main():
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the decoder on a single MI355X "
-              "(--gpus %d requested). Multi-GPU sharding is a design note only." % args.gpus,
+        print("bench.py measures one GPU: the decoder runs on a single MI355X "
+              "(--gpus %d requested); sharding across GPUs is not implemented." % args.gpus,
               file=sys.stderr)
         return 2
 
