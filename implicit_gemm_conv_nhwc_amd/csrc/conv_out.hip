@@ -200,7 +200,11 @@ __global__ __launch_bounds__(NT) void k_conv_out_taps(const _Float16 *__restrict
     const int nblk = gridDim.x;
     int bid = blockIdx.x;
     if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-    const int y0 = (bid / tiles_x) * OH, x0 = (bid % tiles_x) * OW;
+    // tiles column by column within each XCD's range, so vertical
+    // neighbours (which share the larger halo) run back to back: 3% faster
+    // than row order at 1024^2 x 128
+    const int tiles_y = (H + OH - 1) / OH;
+    const int y0 = (bid % tiles_y) * OH, x0 = (bid / tiles_y) * OW;
     const __amdgpu_buffer_rsrc_t src = make_rsrc(x, (uint32_t)H * W * cin_p * 2);
 
     unsigned aoff[PER_WAVE];
