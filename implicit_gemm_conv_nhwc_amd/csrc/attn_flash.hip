@@ -462,14 +462,27 @@ __global__ __launch_bounds__(128) void k_flash_merge(FlashArgs p)
     *reinterpret_cast<half4v *>(p.out + (int64_t)q * C + 4 * t) = y;
 }
 
-// key ranges: enough workgroups to cover the chip, each range >= 8 blocks
+// key ranges (at most 8, each >= 8 blocks): workgroups run one per CU in
+// waves of 256, so the count is the fewest ranges whose workgroups fill
+// those waves to 90% or more, else the count that fills them best (each
+// range adds a partial result for the merge to read)
 void flash_split(int m, int &nsplit, int &bps)
 {
     const int nqb = (m + BQ - 1) / BQ;
     const int nblocks = (m + BK - 1) / BK;
-    int ns = (256 + nqb - 1) / nqb;
-    const int cap = nblocks / 8 > 1 ? nblocks / 8 : 1;
-    if (ns > cap) ns = cap;
+    int cap = nblocks / 8 > 1 ? nblocks / 8 : 1;
+    if (cap > 8) cap = 8;
+    int ns = 1;
+    double best = 0.0;
+    for (int k = 1; k <= cap; ++k) {
+        const int64_t w = (int64_t)nqb * k;
+        const double fill = (double)w / (double)(((w + 255) / 256) * 256);
+        if (fill > best + 1e-9) {
+            best = fill;
+            ns = k;
+        }
+        if (fill >= 0.9) break;
+    }
     bps = (nblocks + ns - 1) / ns;
     nsplit = (nblocks + bps - 1) / bps;
 }

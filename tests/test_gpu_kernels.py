@@ -984,10 +984,11 @@ def test_attention_single_pass(m, kind):
     _check_attn(got[rows], q[rows], k, vt, bv, "attention m=%d %s" % (m, kind))
 
 
-@pytest.mark.parametrize("m", [16384, 40000])
+@pytest.mark.parametrize("m", [16384, 32768, 40000])
 def test_attention_single_pass_large(m):
-    """16384 = the 1024^2 decode's tokens (two key ranges merged); 40000
-    runs as one key range per workgroup (no merge)."""
+    """16384 = the 1024^2 decode's tokens (two key ranges merged); 32768
+    runs as one key range per workgroup (no merge); 40000 as three ranges
+    (its 313 query blocks fill waves of 256 workgroups best that way)."""
     q, k, vt, bv = _attn_inputs(m, "flat", seed=3)
     got = _run_flash(q, k, vt, bv)
     rows = np.unique(np.r_[0:32, m - 32:m, np.linspace(0, m - 1, 64).astype(int)])
